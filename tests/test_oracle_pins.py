@@ -1,0 +1,295 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+* Philox4x32-10: published known-answer vectors (tests/golden).
+* Projection: exact rational dot products of bf16 values; one-hot weights.
+* Top-k: O(V^2) rank counting.  Top-p: the membership characterisation
+  "v is kept iff the mass of strictly larger logits in the top-k set is below
+  p times that set's mass", evaluated by a double loop.
+* Worked examples derived by hand (tests/golden/sampler_worked_examples.json).
+* Log-softmax: closed forms and scipy's logsumexp.
+* Gumbel-max: chi-square of sampled frequencies against the filtered softmax.
+* RNG uniformity: Kolmogorov-Smirnov.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# -------------------------------------------------------------------- Philox
+def test_philox_known_answers():
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.txt")) as f:
+        lines = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    assert len(lines) == 3
+    for ln in lines:
+        v = [int(x, 16) for x in ln]
+        out = oracle.philox4x32_10(*[np.array([x]) for x in v[:4]], v[4], v[5])
+        assert [int(o[0]) for o in out] == v[6:10]
+
+
+def test_uniform_range_and_ks():
+    ids = np.arange(200_000)
+    w = oracle.random_words(0x123456789ABCDEF, 7, ids)
+    u = oracle.uniform_from_words(w)
+    assert u.min() > 0.0 and u.max() < 1.0
+    # 23-bit grid: u * 2^23 - 1/2 is an integer.
+    g = u * 2.0**23 - 0.5
+    assert np.all(g == np.round(g))
+    assert scipy.stats.kstest(u, "uniform").pvalue > 1e-3
+
+
+def test_rng_rows_and_seeds_independent():
+    ids = np.arange(4096)
+    a = oracle.random_words(1, 0, ids)
+    b = oracle.random_words(1, 1, ids)
+    c = oracle.random_words(2, 0, ids)
+    d = oracle.random_words(1 << 32, 0, ids)   # high seed word matters
+    e = oracle.random_words(1, 1 << 32, ids)   # high row word matters
+    for x, y in [(a, b), (a, c), (a, d), (a, e)]:
+        assert np.mean(x == y) < 0.01
+    # Words of one counter block are distinct outputs of one Philox call.
+    assert len(set(a[:4].tolist())) == 4
+
+
+# ----------------------------------------------------------------- projection
+def _bf16_fraction(bits: int) -> Fraction:
+    """Exact value of a bf16 bit pattern, from the IEEE binary32 layout."""
+    sign = -1 if bits & 0x8000 else 1
+    exp = (bits >> 7) & 0xFF
+    man = bits & 0x7F
+    assert exp != 0xFF
+    if exp == 0:
+        return sign * Fraction(man, 1 << 7) * Fraction(1, 1 << 126)
+    return sign * (1 + Fraction(man, 1 << 7)) * (Fraction(2) ** (exp - 127))
+
+
+@pytest.mark.parametrize("rows,vocab,hidden", [(3, 5, 7), (2, 9, 16), (5, 4, 33)])
+def test_projection_exact_rational(rows, vocab, hidden):
+    rng = np.random.default_rng(rows * 100 + vocab)
+    xb = workloads.bf16_bits_from_f32(rng.standard_normal((rows, hidden)).astype(np.float32))
+    wb = workloads.bf16_bits_from_f32(
+        (rng.standard_normal((vocab, hidden)) * 0.1).astype(np.float32))
+    got = oracle.lmhead_logits(xb, wb, vocab_chunk=3)
+    assert got.shape == (rows, vocab)
+    for r in range(rows):
+        for v in range(vocab):
+            exact = sum(_bf16_fraction(int(xb[r, h])) * _bf16_fraction(int(wb[v, h]))
+                        for h in range(hidden))
+            bound = sum(abs(_bf16_fraction(int(xb[r, h])) * _bf16_fraction(int(wb[v, h])))
+                        for h in range(hidden))
+            assert abs(Fraction(got[r, v]) - exact) <= float(bound) * hidden * 2.0**-52 + 1e-300
+
+
+def test_projection_one_hot_rows_reproduce_hidden_columns():
+    rng = np.random.default_rng(5)
+    hidden = 24
+    xb = workloads.bf16_bits_from_f32(rng.standard_normal((6, hidden)).astype(np.float32))
+    w = np.zeros((hidden, hidden), dtype=np.float32)
+    perm = rng.permutation(hidden)
+    w[np.arange(hidden), perm] = 1.0
+    wb = workloads.bf16_bits_from_f32(w)
+    got = oracle.lmhead_logits(xb, wb)
+    np.testing.assert_array_equal(got, oracle.decode_bf16(xb)[:, perm])
+
+
+def test_decode_bf16_known_values():
+    bits = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x3E80, 0x7F7F, 0x0001], dtype=np.uint16)
+    got = oracle.decode_bf16(bits)
+    assert got[:5].tolist() == [1.0, -2.0, 0.0, -0.0, 0.25]
+    assert got[5] == float(np.float32(3.3895313892515355e38))
+    assert got[6] == 2.0**-133
+
+
+def test_assemble_round_trip():
+    rng = np.random.default_rng(1)
+    a = rng.standard_normal((7, 23)).astype(np.float32)
+    parts = [a[:, :5], a[:, 5:6], a[:, 6:20], a[:, 20:]]
+    np.testing.assert_array_equal(oracle.assemble_vocab_slices(parts), a)
+    b = oracle.assemble_vocab_slices([np.full((2, 2), 1.0), np.full((2, 1), 2.0)])
+    assert b.tolist() == [[1.0, 1.0, 2.0], [1.0, 1.0, 2.0]]
+
+
+# --------------------------------------------------------- kept-set brute force
+def _brute_top_k(l, k):
+    """v kept iff fewer than k tokens have a strictly larger logit."""
+    V = len(l)
+    if k <= 0 or k >= V:
+        return set(range(V))
+    return {v for v in range(V) if sum(1 for u in range(V) if l[u] > l[v]) < k}
+
+
+def _brute_top_p(l, t, k, p):
+    """v kept iff v is in the top-k set and the temperature-scaled mass of the
+    top-k tokens with a strictly larger logit is below p times the set's mass."""
+    K = _brute_top_k(l, k)
+    if p >= 1.0:
+        return K
+    m = max(l)
+    w = {u: math.exp((l[u] - m) / t) for u in K}
+    z = math.fsum(w.values())
+    out = set()
+    for v in K:
+        above = math.fsum(w[u] for u in K if l[u] > l[v])
+        if above < p * z:
+            out.add(v)
+    return out
+
+
+def test_worked_examples_kept_sets():
+    with open(os.path.join(GOLDEN, "sampler_worked_examples.json")) as f:
+        cases = json.load(f)["kept"]
+    for c in cases:
+        l = np.array(c["logits"], dtype=np.float64)
+        kept, _ = oracle.kept_set(l, c["T"], c["k"], c["p"])
+        assert kept.tolist() == c["kept"], c
+        assert sorted(_brute_top_p(list(l), c["T"], c["k"], c["p"])) == c["kept"], c
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_kept_set_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    V = int(rng.integers(2, 40))
+    # Coarse values force ties at the top-k and top-p boundaries.
+    if seed % 2:
+        l = rng.integers(-3, 4, size=V).astype(np.float64) * 0.5
+    else:
+        l = rng.standard_normal(V) * 2.0
+    t = float(rng.uniform(0.2, 2.0))
+    k = int(rng.choice([0, 1, 2, 3, V - 1, V, V + 3]))
+    p = float(rng.choice([1.0, float(rng.uniform(0.05, 0.999))]))
+    kept, _ = oracle.kept_set(l, t, k, p)
+    assert set(kept.tolist()) == _brute_top_p(list(l), t, k, p)
+
+
+def test_top_p_one_and_k_v_keep_everything():
+    rng = np.random.default_rng(3)
+    l = rng.standard_normal(100)
+    for k in (0, 100, 1000):
+        kept, flag = oracle.kept_set(l, 0.9, k, 1.0)
+        assert kept.tolist() == list(range(100)) and not flag
+
+
+# ---------------------------------------------------------------- logprobs
+def test_logprob_closed_forms():
+    with open(os.path.join(GOLDEN, "sampler_worked_examples.json")) as f:
+        cases = json.load(f)["logprobs"]
+    for c in cases:
+        l = np.array(c["logits"], dtype=np.float64)
+        V = len(l)
+        r = oracle.sample_row(l, 0.0, 0, 1.0, V, 0, 0, V)
+        got = np.empty(V)
+        got[r.topn_ids] = r.topn_logprobs
+        np.testing.assert_allclose(got, c["logprobs"], rtol=1e-12, atol=1e-12)
+
+
+def test_logprobs_match_scipy_and_topn_order():
+    rng = np.random.default_rng(11)
+    l = rng.standard_normal(3000).astype(np.float32)
+    l[17] = l[18] = l.max() + 1          # tie at the top: lower id first
+    r = oracle.sample_row(l, 0.8, 0, 1.0, 20, 9, 3, 20)
+    ref = l.astype(np.float64) - scipy.special.logsumexp(l.astype(np.float64))
+    assert r.topn_ids[0] == 17 and r.topn_ids[1] == 18
+    np.testing.assert_allclose(r.topn_logprobs, ref[r.topn_ids], atol=1e-12)
+    # Top-N are the 20 largest values in non-increasing order.
+    vals = l[r.topn_ids]
+    assert np.all(np.diff(vals) <= 0)
+    assert vals[-1] >= np.sort(l)[-20]
+    assert r.token_logprob == pytest.approx(ref[r.token], abs=1e-12)
+
+
+def test_unused_slots_and_zero_logprobs():
+    l = np.linspace(-1, 1, 50).astype(np.float32)
+    r = oracle.sample_row(l, 1.0, 0, 1.0, 0, 1, 0, 6)
+    assert r.topn_ids.tolist() == [-1] * 6
+    assert np.all(np.isneginf(r.topn_logprobs))
+
+
+# ------------------------------------------------------------------ greedy
+def test_greedy_cases():
+    rng = np.random.default_rng(2)
+    l = rng.standard_normal(500).astype(np.float32)
+    l[[40, 300]] = l.max() + 2.0   # tie for the maximum
+    for t, k in [(0.0, 0), (0.0, 50), (5e-7, 0), (1.3, 1), (0.0, 1)]:
+        r = oracle.sample_row(l, t, k, 0.5, 3, 77, 5, 3)
+        assert r.token == 40
+    # A small temperature with a wide gap is argmax for every seed.
+    l2 = l.copy()
+    l2[300] -= 1.0
+    for s in range(50):
+        assert oracle.sample_row(l2, 0.01, 0, 1.0, 0, s, 0, 0).token == 40
+
+
+# ----------------------------------------------------------------- statuses
+def test_row_status():
+    l = np.zeros(8, dtype=np.float32)
+    bad = [(-0.1, 0, 1.0, 1), (math.nan, 0, 1.0, 1), (math.inf, 0, 1.0, 1), (1.0, -1, 1.0, 1),
+           (1.0, 0, 0.0, 1), (1.0, 0, 1.01, 1), (1.0, 0, math.nan, 1), (1.0, 0, 1.0, -1),
+           (1.0, 0, 1.0, 5)]
+    for t, k, p, n in bad:
+        r = oracle.sample_row(l, t, k, p, n, 0, 0, 4)
+        assert r.status == oracle.STATUS_BAD_PARAMS and r.token == -1
+        assert math.isnan(r.token_logprob) and np.all(r.topn_ids == -1)
+    for bad_val in (math.nan, math.inf):
+        l2 = l.copy()
+        l2[3] = bad_val
+        assert oracle.sample_row(l2, 1.0, 0, 1.0, 1, 0, 0, 4).status == oracle.STATUS_BAD_LOGITS
+    l3 = np.full(8, -np.inf, dtype=np.float32)
+    assert oracle.sample_row(l3, 1.0, 0, 1.0, 1, 0, 0, 4).status == oracle.STATUS_BAD_LOGITS
+    # -inf entries are allowed and never sampled.
+    l4 = np.full(8, -np.inf, dtype=np.float32)
+    l4[5] = 0.0
+    l4[2] = -1.0
+    r = oracle.sample_row(l4, 1.0, 0, 1.0, 4, 0, 0, 4)
+    assert r.status == 0 and r.token in (2, 5)
+    assert r.topn_ids.tolist() == [5, 2, 0, 1]
+
+
+# ------------------------------------------------------------- Gumbel-max
+@pytest.mark.parametrize("t,k,p", [(1.0, 0, 1.0), (0.6, 0, 0.8), (1.4, 4, 1.0), (0.9, 5, 0.7)])
+def test_gumbel_max_frequencies_chi_square(t, k, p):
+    l = np.array([1.2, 0.3, -0.4, 0.9, 0.0, -1.0, 0.5], dtype=np.float32)
+    kept = sorted(_brute_top_p([float(x) for x in l], t, k, p))
+    probs = scipy.special.softmax(l[kept].astype(np.float64) / t)
+    draws = 12_000
+    counts = {v: 0 for v in range(len(l))}
+    for row in range(draws):
+        counts[oracle.sample_row(l, t, k, p, 0, 1234, row, 0).token] += 1
+    assert all(counts[v] == 0 for v in range(len(l)) if v not in kept)
+    obs = np.array([counts[v] for v in kept])
+    if len(kept) > 1:
+        assert scipy.stats.chisquare(obs, probs * draws).pvalue > 1e-3
+    else:
+        assert obs[0] == draws
+
+
+def test_rows_share_seed_but_differ():
+    """Spec-decode rows of one request share a seed; the global row index
+    separates their draws, and row_offset shifts it."""
+    l = np.zeros((6, 64), dtype=np.float32)
+    params = np.zeros(6, dtype=workloads.PARAMS_DTYPE)
+    params["temperature"] = 1.0
+    params["top_p"] = 1.0
+    params["seed"] = 99
+    a = oracle.sample(l, params, 0, 0)
+    assert len(set(a.token_ids.tolist())) > 1
+    b = oracle.sample(l[3:], params[3:], 3, 0)
+    np.testing.assert_array_equal(a.token_ids[3:], b.token_ids)
+
+
+def test_workload_params_in_domain():
+    for w in workloads.WORKLOADS.values():
+        p = workloads.make_params(w)
+        assert p.shape == (w.rows,)
+        for r in p:
+            assert oracle.params_valid(float(r["temperature"]), int(r["top_k"]),
+                                       float(r["top_p"]), int(r["n_logprobs"]), w.max_logprobs)
