@@ -1,0 +1,176 @@
+/*
+ * top_sampling.h -- C ABI of the MI355X (gfx950) batch-sharded sampling path.
+ *
+ * One tensor-parallel rank's share of batch-sharded sampling, as described on
+ * the page "Qwen4Exp batch-sharded sampling: inside vLLM PR #61018"
+ * (orcarouter.ai blog, ja/nl/fr editions):
+ *
+ *   1. lmhead_logits_local       -- the rank's own vocabulary slice of the
+ *      projection, with no gather (sections "What batch-sharded sampling is,
+ *      in one paragraph" and "Why three lines were the whole job": the
+ *      model's local-logits hook hands back only the rank's vocabulary shard);
+ *   2. sampler_assemble_vocab_slices -- the receive side of the all-to-all:
+ *      vocabulary slices from every rank stitched into full-vocabulary rows
+ *      for the rank's slice of requests (section "What batch-sharded sampling
+ *      is, in one paragraph");
+ *   3. sampler_sample            -- the per-row sampler over
+ *      batch x (speculative tokens + 1) rows: temperature, top-k, top-p,
+ *      log-probabilities and seeded sampling (same section; the page names
+ *      top-k, top-p and a non-negative max_logprobs, not their arithmetic).
+ *
+ * Conventions shared by every call
+ *   - All pointers to bulk data are DEVICE pointers unless stated otherwise.
+ *     The caller owns every buffer; the library never allocates device
+ *     memory, never synchronises the host and never prints.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously on it.
+ *   - A nonzero return value means argument validation failed and NOTHING was
+ *     enqueued (invalid configurations are rejected up front rather than
+ *     degraded silently).  ts_last_error() then describes the failure for
+ *     the calling thread.  TS_EHIP reports a failed kernel launch.
+ *   - Sizes of zero are valid no-ops.
+ *   - Matrices are row-major with an explicit leading dimension (elements).
+ */
+#ifndef TOP_SAMPLING_H_
+#define TOP_SAMPLING_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+enum {
+  TS_OK = 0,
+  TS_EINVAL = -1,        /* bad sizes, leading dimensions or NULL pointers     */
+  TS_EUNSUPPORTED = -2,  /* valid but outside what the kernels take (alignment,
+                            limits such as TS_MAX_LOGPROBS)                    */
+  TS_EWORKSPACE = -3,    /* workspace NULL or smaller than required            */
+  TS_EHIP = -4           /* the HIP runtime rejected a launch                  */
+};
+
+/* Per-row status written by sampler_sample. */
+enum {
+  TS_ROW_OK = 0,
+  TS_ROW_BAD_PARAMS = 1,  /* temperature < 0 or not finite; top_k < 0;
+                             top_p not in (0, 1]; n_logprobs not in
+                             [0, max_logprobs]                               */
+  TS_ROW_BAD_LOGITS = 2   /* a NaN or +inf logit, or no finite logit          */
+};
+
+#define TS_MAX_LOGPROBS 1024   /* largest accepted max_logprobs              */
+#define TS_MAX_SLICES 64       /* largest accepted n_slices                  */
+#define TS_GREEDY_EPS 1e-6f    /* temperatures below this sample greedily    */
+
+/*
+ * Sampling parameters of one row (24 bytes, 8-byte aligned; an array of
+ * `rows` of them lives in device memory).
+ *   temperature  0 (or < TS_GREEDY_EPS): greedy argmax of the raw logits.
+ *   top_k        0 or >= vocab: no top-k filter; 1: greedy.  Every token
+ *                tied with the k-th largest logit is kept.
+ *   top_p        1: no top-p filter.  Otherwise the smallest set of most
+ *                likely tokens (of the temperature-scaled distribution
+ *                renormalised over the top-k set) whose mass reaches top_p;
+ *                the crossing token and its ties are kept.
+ *   n_logprobs   how many of the row's largest logits to report (<= the
+ *                call's max_logprobs).
+ *   seed         RNG key of the row.  Sampling is Gumbel-max:
+ *                token = argmax over kept v of (l_v - max l) / T + g_v,
+ *                g_v = -ln(-ln u_v), u_v = ((x >> 9) + 1/2) * 2^-23 where x
+ *                is word (v & 3) of Philox4x32-10 with key (seed lo32,
+ *                seed hi32) and counter (v >> 2, row lo32, row hi32, 0),
+ *                row = row_offset + local row (Salmon et al., "Parallel
+ *                Random Numbers: As Easy as 1, 2, 3", SC'11).  Lowest id
+ *                wins exact ties.
+ */
+typedef struct ts_row_params {
+  float temperature;
+  int32_t top_k;
+  float top_p;
+  int32_t n_logprobs;
+  uint64_t seed;
+} ts_row_params;
+
+/*
+ * lmhead_logits_local: logits[r, v] = sum_h hidden[r, h] * lm_head[v, h].
+ *
+ * The rank's local vocabulary projection: only the slice of the vocabulary
+ * this rank holds (vocab_local rows of lm_head), never gathered.
+ *   hidden     bf16 [rows, hidden_dim], leading dimension ld_hidden
+ *   lm_head    bf16 [vocab_local, hidden_dim], leading dimension ld_lm_head
+ *              (both K-contiguous)
+ *   logits     fp32 [rows, vocab_local] written with leading dimension
+ *              ld_logits >= vocab_local, so a slice can be written straight
+ *              into a wider buffer.
+ * Products of bf16 are exact in fp32; accumulation is fp32 (MFMA).
+ * Requirements (else TS_EUNSUPPORTED): hidden_dim % 8 == 0, ld_hidden and
+ * ld_lm_head multiples of 8, hidden and lm_head 16-byte aligned, logits
+ * 4-byte aligned.  rows, vocab_local < 2^31.
+ */
+int lmhead_logits_local(const void* hidden, int64_t rows, int64_t hidden_dim,
+                        int64_t ld_hidden, const void* lm_head, int64_t vocab_local,
+                        int64_t ld_lm_head, float* logits, int64_t ld_logits,
+                        void* stream);
+
+/*
+ * sampler_workspace_bytes: device workspace sampler_sample needs for these
+ * sizes (host-only computation; callable without a GPU).
+ */
+size_t sampler_workspace_bytes(int64_t rows, int64_t vocab, int32_t max_logprobs);
+
+/*
+ * sampler_sample: sample one token per row and report log-probabilities.
+ *   logits          fp32 [rows, vocab], leading dimension ld_logits; read only.
+ *   params          device array of `rows` ts_row_params.
+ *   row_offset      global index of local row 0 (keys the RNG, so a rank's
+ *                   share of rows draws exactly what the unsharded call would).
+ *   max_logprobs    0..TS_MAX_LOGPROBS: width of the top-N outputs.
+ *   token_ids       int32 [rows]: sampled token, -1 for a row whose status != 0.
+ *   token_logprobs  fp32 [rows] or NULL: raw log_softmax of the sampled token
+ *                   (NaN for a bad row).
+ *   topn_ids        int32 [rows, max_logprobs] (may be NULL iff max_logprobs
+ *                   == 0): the row's n_logprobs largest logits, largest first,
+ *                   lower id first on ties; unused slots -1.
+ *   topn_logprobs   fp32 [rows, max_logprobs]: their raw log-probabilities;
+ *                   unused slots -inf; NaN for a bad row.
+ *   row_status      int32 [rows] or NULL: TS_ROW_* per row.
+ *   workspace       device scratch of at least sampler_workspace_bytes(...)
+ *                   bytes, 256-byte aligned; contents need no initialisation
+ *                   and are clobbered.
+ * Log-probabilities describe the raw distribution log_softmax(logits)
+ * (unscaled, unfiltered).  Calls that share a workspace must be ordered on
+ * one stream.  vocab < 2^31.
+ */
+int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_logits,
+                   const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                   int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                   float* topn_logprobs, int32_t* row_status, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
+ * sampler_assemble_vocab_slices: out[r, off_s + c] = slice_s[r, c] with
+ * off_s = slice_cols[0] + ... + slice_cols[s-1].
+ *   slices      HOST array of n_slices DEVICE pointers, slice s fp32
+ *               [rows, slice_cols[s]] with leading dimension slice_ld[s]
+ *   slice_cols, slice_ld   HOST arrays of n_slices entries
+ *   out         fp32 [rows, sum slice_cols], leading dimension ld_out
+ * A bit-exact copy.  1 <= n_slices <= TS_MAX_SLICES.  Slices must not
+ * overlap `out`.
+ */
+int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* slice_cols,
+                                  const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                                  float* out, int64_t ld_out, void* stream);
+
+/* Name of a TS_* return code (static string). */
+const char* ts_status_string(int status);
+
+/* Detail of the calling thread's last nonzero return (static per thread). */
+const char* ts_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOP_SAMPLING_H_ */

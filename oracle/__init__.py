@@ -57,7 +57,7 @@ import os
 import numpy as np
 
 GREEDY_EPS = 1e-6          # R2: temperatures below this sample greedily
-TOP_P_FLAG_WINDOW = 1e-5   # rows whose top-p boundary mass lies this close to p are flagged
+TOP_P_FLAG_WINDOW = 1e-5   # top-p boundaries whose mass lies this close to p are ambiguous
 KEY_TIE_WINDOW = 1e-4      # rows whose two best Gumbel keys lie this close are flagged
 
 STATUS_OK = 0
@@ -176,7 +176,7 @@ class RowResult:
     token_logprob: float
     topn_ids: np.ndarray
     topn_logprobs: np.ndarray
-    flag_top_p: bool = False   # top-p boundary mass within TOP_P_FLAG_WINDOW of p
+    flag_top_p: bool = False   # token depends on a top-p boundary within TOP_P_FLAG_WINDOW
     flag_tie: bool = False     # two best Gumbel keys within KEY_TIE_WINDOW
     kept: int = 0              # size of the kept set (diagnostic)
 
@@ -195,11 +195,14 @@ def params_valid(t: float, k: int, p: float, n: int, max_logprobs: int) -> bool:
 
 
 def kept_set(l: np.ndarray, t: float, k: int, p: float,
-             order: np.ndarray | None = None) -> tuple[np.ndarray, bool]:
+             order: np.ndarray | None = None) -> tuple[np.ndarray, np.ndarray]:
     """Token ids (ascending) that survive top-k then top-p at temperature t > 0,
-    and whether the row's top-p boundary lies within TOP_P_FLAG_WINDOW of p.
+    and the ids whose membership is within rounding of the top-p boundary.
 
     ``l`` is the float64 row; ``order`` its sort by (logit desc, id asc).
+    The second array lists the top-k tokens that some boundary drawn where
+    the cumulative mass lies within TOP_P_FLAG_WINDOW of p would add to or
+    drop from the smallest such kept set (empty without a top-p filter).
     """
     vocab = l.shape[0]
     if order is None:
@@ -218,25 +221,31 @@ def kept_set(l: np.ndarray, t: float, k: int, p: float,
     cum = np.cumsum(w)
     z_k = cum[-1]
     if p >= 1.0:
-        return np.sort(sorted_ids), False
+        return np.sort(sorted_ids), np.zeros(0, dtype=np.int64)
     # Smallest prefix whose mass reaches p; the crossing token is kept, and so
     # is every token tied with it.
     frac = cum / z_k
     j_star = int(np.argmax(frac >= p))
     t_p = l[sorted_ids[j_star]]
-    keep_sorted = l[sorted_ids] >= t_p
-    # Boundary masses at the threshold value: tokens >= t_p and tokens > t_p.
-    c_plus = w[keep_sorted].sum() / z_k
-    c_minus = w[l[sorted_ids] > t_p].sum() / z_k
-    flag = abs(c_plus - p) < TOP_P_FLAG_WINDOW or abs(c_minus - p) < TOP_P_FLAG_WINDOW
-    return np.sort(sorted_ids[keep_sorted]), bool(flag)
+    kept = np.sort(sorted_ids[l[sorted_ids] >= t_p])
+    # Boundaries drawn where the cumulative mass is within the window of p.
+    last = frac.shape[0] - 1
+    j_lo = int(np.argmax(frac >= p - TOP_P_FLAG_WINDOW))
+    j_hi = int(np.argmax(frac >= p + TOP_P_FLAG_WINDOW)) if frac[-1] >= p + TOP_P_FLAG_WINDOW \
+        else last
+    t_lo, t_hi = l[sorted_ids[j_lo]], l[sorted_ids[j_hi]]
+    vals = l[sorted_ids]
+    ambiguous = np.sort(sorted_ids[(vals >= t_hi) & (vals < t_lo)])
+    return kept, ambiguous
 
 
 def sample_row(logits: np.ndarray, temperature: float, top_k: int, top_p: float,
                n_logprobs: int, seed: int, row_global: int, max_logprobs: int) -> RowResult:
-    """Sample one row; ``logits`` is the fp32 row, used as exact values."""
-    t = float(np.float32(temperature))
-    p = float(np.float32(top_p))
+    """Sample one row; ``logits`` is the fp32 row, used as exact values.
+    Parameters are taken as given (the callers pass the fp32 values the GPU
+    receives)."""
+    t = float(temperature)
+    p = float(top_p)
     k = int(top_k)
     n = int(n_logprobs)
     vocab = logits.shape[0]
@@ -266,7 +275,7 @@ def sample_row(logits: np.ndarray, temperature: float, top_k: int, top_p: float,
         tok = int(order[0])
         return RowResult(STATUS_OK, tok, float(logprob[tok]), topn_ids, topn_lp, kept=1)
 
-    kept_ids, flag_top_p = kept_set(l, t, k, p, order)
+    kept_ids, ambiguous = kept_set(l, t, k, p, order)
 
     # R6: Gumbel-max over the kept set.
     keys = (l[kept_ids] - m) / t + gumbel_noise(seed, row_global, kept_ids)
@@ -276,6 +285,20 @@ def sample_row(logits: np.ndarray, temperature: float, top_k: int, top_p: float,
     if keys.shape[0] > 1:
         top2 = np.partition(keys, -2)[-2:]
         flag_tie = bool(abs(top2[1] - top2[0]) < KEY_TIE_WINDOW)
+    # Flag the row when moving the top-p boundary within the window changes
+    # the winner: the winners over the smallest and the largest plausible
+    # kept sets differ.
+    flag_top_p = False
+    if ambiguous.shape[0]:
+        amb = np.isin(kept_ids, ambiguous)
+        small = kept_ids[~amb]
+        k_small = keys[~amb]
+        w_small = int(small[int(np.argmax(k_small))])
+        extra = ambiguous[~np.isin(ambiguous, kept_ids)]
+        big = np.concatenate([kept_ids, extra])
+        k_big = np.concatenate([keys, (l[extra] - m) / t + gumbel_noise(seed, row_global, extra)])
+        ob = np.lexsort((big, -k_big))
+        flag_top_p = int(big[ob[0]]) != w_small
     return RowResult(STATUS_OK, tok, float(logprob[tok]), topn_ids, topn_lp,
                      flag_top_p=flag_top_p, flag_tie=flag_tie, kept=int(kept_ids.shape[0]))
 

@@ -1,0 +1,174 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and its host-side validation rejects bad calls before any HIP call (so these
+run without a GPU).  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import top_sampling_amd as ts
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "top_sampling.h")
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M))
+
+
+def test_header_symbols_exported():
+    names = _declared_functions()
+    assert names == set(ts.SYMBOLS), names
+    lib = ctypes.CDLL(ts.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name, val in [("TS_MAX_LOGPROBS", ts.TS_MAX_LOGPROBS), ("TS_MAX_SLICES", ts.TS_MAX_SLICES)]:
+        assert re.search(rf"#define {name} {val}\b", text)
+    assert workloads.PARAMS_DTYPE.itemsize == ts.PARAMS_BYTES
+
+
+def test_status_strings():
+    assert ts.lib.ts_status_string(0) == b"TS_OK"
+    assert ts.lib.ts_status_string(-1) == b"TS_EINVAL"
+    assert ts.lib.ts_status_string(-3) == b"TS_EWORKSPACE"
+    assert ts.lib.ts_status_string(99) == b"TS_UNKNOWN"
+
+
+def test_workspace_query_is_host_only():
+    assert ts.sampler_workspace_bytes(640, 151936, 20) > 0
+    assert ts.sampler_workspace_bytes(-1, 10, 0) == 0
+
+
+def _gemm(**kw):
+    a = dict(hidden=FAKE, rows=4, hidden_dim=256, ld_hidden=256, lm_head=FAKE, vocab=64,
+             ld_lm_head=256, logits=FAKE, ld_logits=64)
+    a.update(kw)
+    return ts.lib.lmhead_logits_local(a["hidden"], a["rows"], a["hidden_dim"], a["ld_hidden"],
+                                      a["lm_head"], a["vocab"], a["ld_lm_head"], a["logits"],
+                                      a["ld_logits"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), ts.TS_EINVAL),
+    (dict(vocab=-5), ts.TS_EINVAL),
+    (dict(hidden=None), ts.TS_EINVAL),
+    (dict(ld_hidden=128), ts.TS_EINVAL),
+    (dict(ld_logits=63), ts.TS_EINVAL),
+    (dict(hidden_dim=0), ts.TS_EINVAL),
+    (dict(hidden_dim=250, ld_hidden=256, ld_lm_head=256), ts.TS_EUNSUPPORTED),
+    (dict(ld_hidden=260), ts.TS_EUNSUPPORTED),
+    (dict(hidden=FAKE + 8), ts.TS_EUNSUPPORTED),
+    (dict(rows=1 << 31), ts.TS_EUNSUPPORTED),
+])
+def test_gemm_validation(kw, code):
+    assert _gemm(**kw) == code
+    assert ts.lib.ts_last_error()
+
+
+def test_gemm_empty_is_noop():
+    assert _gemm(rows=0, hidden=None, lm_head=None, logits=None) == ts.TS_OK
+    assert _gemm(vocab=0) == ts.TS_OK
+
+
+def _sample(**kw):
+    a = dict(logits=FAKE, rows=8, vocab=100, ld=100, params=FAKE, row_offset=0, max_logprobs=5,
+             tok=FAKE, tlp=FAKE, tid=FAKE, tnlp=FAKE, status=FAKE, ws=None, ws_bytes=0)
+    a.update(kw)
+    return ts.lib.sampler_sample(a["logits"], a["rows"], a["vocab"], a["ld"], a["params"],
+                                 a["row_offset"], a["max_logprobs"], a["tok"], a["tlp"],
+                                 a["tid"], a["tnlp"], a["status"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), ts.TS_EINVAL),
+    (dict(max_logprobs=-1), ts.TS_EINVAL),
+    (dict(max_logprobs=ts.TS_MAX_LOGPROBS + 1), ts.TS_EUNSUPPORTED),
+    (dict(row_offset=-3), ts.TS_EINVAL),
+    (dict(vocab=0), ts.TS_EINVAL),
+    (dict(ld=99), ts.TS_EINVAL),
+    (dict(logits=None), ts.TS_EINVAL),
+    (dict(params=None), ts.TS_EINVAL),
+    (dict(tok=None), ts.TS_EINVAL),
+    (dict(tid=None), ts.TS_EINVAL),
+    (dict(params=FAKE + 4), ts.TS_EUNSUPPORTED),
+    (dict(), ts.TS_EWORKSPACE),                       # no workspace
+    (dict(ws=FAKE, ws_bytes=1), ts.TS_EWORKSPACE),    # too small
+])
+def test_sampler_validation(kw, code):
+    assert _sample(**kw) == code
+
+
+def test_sampler_empty_is_noop():
+    assert _sample(rows=0, logits=None, params=None, tok=None) == ts.TS_OK
+
+
+def test_sampler_null_topn_allowed_only_without_logprobs():
+    # max_logprobs == 0: NULL top-N is fine, so validation reaches the workspace check.
+    assert _sample(max_logprobs=0, tid=None, tnlp=None) == ts.TS_EWORKSPACE
+
+
+def _assemble(ptrs, cols, lds, rows=4, out=FAKE * 16, ld_out=None):
+    n = len(ptrs)
+    ld_out = sum(cols) if ld_out is None else ld_out
+    P = (ctypes.c_void_p * max(n, 1))(*ptrs)
+    C = (ctypes.c_int64 * max(n, 1))(*cols)
+    L = (ctypes.c_int64 * max(n, 1))(*lds)
+    return ts.lib.sampler_assemble_vocab_slices(P, C, L, n, rows, out, ld_out, None)
+
+
+def test_assemble_validation():
+    assert _assemble([], [], []) == ts.TS_EINVAL
+    assert _assemble([FAKE] * 65, [4] * 65, [4] * 65) == ts.TS_EUNSUPPORTED
+    assert _assemble([FAKE, FAKE * 2], [4, -1], [4, 4]) == ts.TS_EINVAL
+    assert _assemble([FAKE, FAKE * 2], [4, 8], [4, 4]) == ts.TS_EINVAL       # ld < width
+    assert _assemble([FAKE, None], [4, 8], [4, 8]) == ts.TS_EINVAL           # NULL slice
+    assert _assemble([FAKE, FAKE * 2], [4, 8], [4, 8], ld_out=11) == ts.TS_EINVAL
+    assert _assemble([FAKE, FAKE * 2], [4, 8], [4, 8], out=None) == ts.TS_EINVAL
+    # a slice inside the output rows is rejected
+    assert _assemble([FAKE * 16 + 8, FAKE * 2], [4, 8], [12, 8]) == ts.TS_EINVAL
+    assert _assemble([FAKE, FAKE * 2], [4, 8], [4, 8], rows=0) == ts.TS_OK
+
+
+def test_compute_logits_local_wiring(monkeypatch):
+    """Mirror of the wiring test the page describes (a recording fake in place
+    of the kernel): the local-logits hook asks for the rank's own slice,
+    [rows, V_local], and hands back exactly that, with no gather."""
+    import torch
+
+    calls = []
+
+    class FakeLib:
+        def lmhead_logits_local(self, *args):
+            calls.append(args)
+            return 0
+
+    monkeypatch.setattr(ts, "lib", FakeLib())
+    hidden = torch.zeros(6, 16, dtype=torch.bfloat16)
+    lm_head_local = torch.zeros(40, 16, dtype=torch.bfloat16)   # this rank's vocabulary slice
+    out = ts.compute_logits_local(hidden, lm_head_local, stream=0)
+    assert tuple(out.shape) == (6, 40)
+    (_, rows, h, ldh, _, vocab, ldw, _, ldl, _), = calls
+    assert (rows, h, ldh, vocab, ldw, ldl) == (6, 16, 16, 40, 16, 40)
+    # Writing the slice into a wider buffer uses the wider row stride.
+    wide = torch.empty(6, 160)
+    ts.compute_logits_local(hidden, lm_head_local, out=wide[:, 40:80], stream=0)
+    assert calls[-1][8] == 160 and calls[-1][5] == 40
+
+
+def test_params_layout_roundtrip():
+    p = workloads.make_params(workloads.get("spec_decode"))
+    raw = np.ascontiguousarray(p).view(np.uint8)
+    assert raw.shape[0] == 24 * p.shape[0]
+    back = raw.view(workloads.PARAMS_DTYPE)
+    assert np.array_equal(back["seed"], p["seed"])

@@ -1,0 +1,359 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: logits within 2e-3 absolute (fp32 MFMA accumulation vs float64);
+log-probabilities within 1e-4; token ids, top-N ids and row status bit-exact,
+except token ids on rows the oracle flags (top-p boundary mass within 1e-5 of
+p, or two best Gumbel keys within 1e-4), which must stay below 0.1% of rows;
+slice assembly bit-exact.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+LOGIT_TOL = 2e-3
+LOGPROB_TOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ts():
+    import top_sampling_amd
+
+    return top_sampling_amd
+
+
+def _bf16_to_device(bits, dev):
+    import torch
+
+    return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+
+
+def _bits(t):
+    import torch
+
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ GEMM
+def test_gemm_tiny_workload(dev, ts):
+    w = workloads.get("tiny")
+    xb, wb = workloads.make_projection_host(w)
+    say("gemm tiny", xb.shape, wb.shape)
+    out = ts.lmhead_logits_local(_bf16_to_device(xb, dev), _bf16_to_device(wb, dev))
+    ref = oracle.lmhead_logits(xb, wb)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref).max()
+    assert err <= LOGIT_TOL, err
+
+
+@pytest.mark.parametrize("rows,vocab,hidden", [
+    (1, 300, 64), (4, 4096, 256), (63, 1000, 520), (65, 513, 136), (129, 777, 264),
+    (257, 1031, 1032), (300, 2000, 8), (640, 700, 4096)])
+def test_gemm_ragged(dev, ts, rows, vocab, hidden):
+    rng = np.random.default_rng(rows * 7 + vocab)
+    xb = workloads.bf16_bits_from_f32(rng.standard_normal((rows, hidden)).astype(np.float32))
+    wb = workloads.bf16_bits_from_f32(
+        (rng.standard_normal((vocab, hidden)) / np.sqrt(hidden)).astype(np.float32))
+    say("gemm", rows, vocab, hidden)
+    out = ts.lmhead_logits_local(_bf16_to_device(xb, dev), _bf16_to_device(wb, dev))
+    ref = oracle.lmhead_logits(xb, wb)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref).max()
+    assert err <= LOGIT_TOL, err
+
+
+def test_gemm_slices_into_wide_buffer(dev, ts):
+    """Vocabulary slices written through ld_logits into one buffer equal one
+    full projection bit for bit, and columns outside the slices are untouched."""
+    import torch
+
+    rng = np.random.default_rng(3)
+    rows, vocab, hidden = 200, 1500, 512
+    x = _bf16_to_device(workloads.bf16_bits_from_f32(
+        rng.standard_normal((rows, hidden)).astype(np.float32)), dev)
+    wt = _bf16_to_device(workloads.bf16_bits_from_f32(
+        (rng.standard_normal((vocab, hidden)) * 0.05).astype(np.float32)), dev)
+    say("gemm slices")
+    full = ts.lmhead_logits_local(x, wt)
+    wide = torch.full((rows, vocab + 37), 7.0, device=dev)
+    cuts = [0, 333, 334, 1024, vocab]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        ts.lmhead_logits_local(x, wt[a:b], out=wide[:, a:b])
+    torch.cuda.synchronize()
+    assert torch.equal(wide[:, :vocab], full)
+    assert torch.all(wide[:, vocab:] == 7.0)
+
+
+@pytest.mark.parametrize("name", ["decode", "spec_decode", "large"])
+def test_gemm_full_size_sampled(dev, ts, name):
+    """Full-size projection in the launch configuration the bench times,
+    checked on sampled rows and columns (including the ragged tails)."""
+    import torch
+
+    w = workloads.get(name)
+    say("gemm full", name)
+    x, wt = workloads.make_projection_device(w, dev)
+    out = ts.lmhead_logits_local(x, wt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.index)
+    rows = np.unique(np.concatenate([rng.choice(w.rows, 6, replace=False), [0, w.rows - 1]]))
+    cols = np.unique(np.concatenate([rng.choice(w.vocab, 3000, replace=False),
+                                     np.arange(w.vocab - 300, w.vocab)]))
+    xb = _bits(x)
+    # whole rows for two rows (one pass over the lm_head)
+    full_rows = rows[:2]
+    ref = oracle.lmhead_logits(xb[full_rows], _bits(wt))
+    got = out[torch.from_numpy(full_rows).to(dev)].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref).max()
+    assert err <= LOGIT_TOL, err
+    # every row at the sampled columns
+    wsel = _bits(wt[torch.from_numpy(cols).to(dev)])
+    ref = oracle.lmhead_logits(xb, wsel)
+    got = out[:, torch.from_numpy(cols).to(dev)].cpu().numpy().astype(np.float64)
+    err = np.abs(got - ref).max()
+    assert err <= LOGIT_TOL, err
+
+
+# --------------------------------------------------------------- assembly
+def test_assemble_rank_share(dev, ts):
+    import torch
+
+    w = workloads.get("rank_share")
+    logits = torch.from_numpy(workloads.make_logits(w)).to(dev)
+    cuts = np.concatenate([[0], np.cumsum(w.slice_cols)])
+    slices = [logits[:, a:b].contiguous() for a, b in zip(cuts[:-1], cuts[1:])]
+    say("assemble rank_share", [s.shape for s in slices])
+    out = ts.sampler_assemble_vocab_slices(slices)
+    torch.cuda.synchronize()
+    assert torch.equal(out, logits)
+
+
+@pytest.mark.parametrize("widths,ld_extra,rows", [
+    ([5, 1, 4097, 3], 0, 7), ([4, 8, 12], 0, 3), ([4, 8, 12], 5, 9), ([9000], 3, 2),
+    ([1] * 64, 0, 5), ([0, 17, 0, 4], 2, 4)])
+def test_assemble_ragged(dev, ts, widths, ld_extra, rows):
+    import torch
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(sum(widths) + rows)
+    slices = []
+    for c in widths:
+        base = torch.randn(rows, c + ld_extra, generator=g, device=dev)
+        slices.append(base[:, :c])
+    say("assemble", widths, ld_extra, rows)
+    out = torch.full((rows, sum(widths) + 3), 5.0, device=dev)
+    ts.sampler_assemble_vocab_slices(slices, out=out[:, :sum(widths)])
+    ref = oracle.assemble_vocab_slices([s.cpu().numpy() for s in slices])
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got[:, :sum(widths)].view(np.uint32), ref.view(np.uint32))
+    assert np.all(got[:, sum(widths):] == 5.0)
+
+
+# ---------------------------------------------------------------- sampler
+def _run_sampler(ts, dev, logits_np, params, row_offset, max_logprobs, ld_extra=0):
+    import torch
+
+    rows, vocab = logits_np.shape
+    if ld_extra:
+        buf = torch.full((rows, vocab + ld_extra), float("nan"), device=dev)
+        buf[:, :vocab] = torch.from_numpy(logits_np).to(dev)
+        logits = buf[:, :vocab]
+    else:
+        logits = torch.from_numpy(np.ascontiguousarray(logits_np)).to(dev)
+    p = ts.params_to_device(params, dev)
+    out = ts.sampler_sample(logits, p, row_offset=row_offset, max_logprobs=max_logprobs)
+    torch.cuda.synchronize()
+    return {k: getattr(out, k).cpu().numpy() for k in
+            ("token_ids", "token_logprobs", "topn_ids", "topn_logprobs", "row_status")}
+
+
+def _compare(got, ref_tokens, ref_tlp, ref_topn_ids, ref_topn_lp, ref_status, flagged, lse,
+             logits_np, max_frac=1e-3, label=""):
+    rows = ref_tokens.shape[0]
+    np.testing.assert_array_equal(got["row_status"], ref_status)
+    ok = ref_status == 0
+    bad = ~ok
+    assert np.all(got["token_ids"][bad] == -1)
+    assert np.all(np.isnan(got["token_logprobs"][bad]))
+    mism = (got["token_ids"] != ref_tokens) & ok
+    assert not np.any(mism & ~flagged), (label, np.nonzero(mism & ~flagged)[0][:10])
+    assert flagged.sum() <= max_frac * rows, (label, flagged.sum())
+    np.testing.assert_array_equal(got["topn_ids"][ok], ref_topn_ids[ok])
+    fin = np.isfinite(ref_topn_lp[ok])
+    assert np.array_equal(np.isfinite(got["topn_logprobs"][ok]), fin)
+    assert np.abs(got["topn_logprobs"][ok][fin] - ref_topn_lp[ok][fin]).max(initial=0) <= LOGPROB_TOL
+    # the sampled token's raw log-probability, for whichever token was drawn
+    r_ok = np.nonzero(ok)[0]
+    tok = got["token_ids"][r_ok]
+    want = logits_np[r_ok, tok].astype(np.float64) - lse[r_ok]
+    assert np.abs(got["token_logprobs"][r_ok] - want).max(initial=0) <= LOGPROB_TOL
+    return int(mism.sum())
+
+
+def _load_expected(name):
+    return dict(np.load(os.path.join(GOLDEN, f"sampler_expected_{name}.npz")))
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode", "spec_decode", "rank_share", "large"])
+def test_sampler_workloads(dev, ts, name):
+    import torch
+
+    w = workloads.get(name)
+    exp = _load_expected(name)
+    params = workloads.make_params(w)
+    assert str(exp["params_digest"]) == __import__("hashlib").sha256(
+        np.ascontiguousarray(params).tobytes()).hexdigest()
+    if name == "tiny":
+        logits = exp["logits"]
+    else:
+        logits = workloads.make_logits(w)
+        for (r0, r1), dg in zip(exp["digest_rows"], exp["logits_digests"]):
+            assert __import__("hashlib").sha256(
+                np.ascontiguousarray(logits[r0:r1]).tobytes()).hexdigest() == dg
+    say("sampler", name, logits.shape)
+    if name == "rank_share":
+        # receive side: four vocabulary slices assembled on the device, then sampled
+        cuts = np.concatenate([[0], np.cumsum(w.slice_cols)])
+        full = torch.from_numpy(logits).to(dev)
+        slices = [full[:, a:b].contiguous() for a, b in zip(cuts[:-1], cuts[1:])]
+        del full
+        assembled = ts.sampler_assemble_vocab_slices(slices)
+        p = ts.params_to_device(params, dev)
+        out = ts.sampler_sample(assembled, p, 0, w.max_logprobs)
+        torch.cuda.synchronize()
+        got = {k: getattr(out, k).cpu().numpy() for k in
+               ("token_ids", "token_logprobs", "topn_ids", "topn_logprobs", "row_status")}
+    else:
+        got = _run_sampler(ts, dev, logits, params, 0, w.max_logprobs)
+    flagged = exp["flag_top_p"] | exp["flag_tie"]
+    mism = _compare(got, exp["token_ids"], exp["token_logprobs"], exp["topn_ids"],
+                    exp["topn_logprobs"], exp["row_status"], flagged, exp["lse"], logits,
+                    label=name)
+    say(f"{name}: rows={w.rows} flagged={int(flagged.sum())} mismatched_flagged={mism}")
+
+
+def _oracle_ref(logits, params, row_offset, max_logprobs):
+    res = oracle.sample(logits, params, row_offset, max_logprobs)
+    l64 = logits.astype(np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        m = np.where(np.isfinite(l64), l64, -np.inf).max(axis=1)
+        lse = m + np.log(np.exp(l64 - m[:, None]).sum(axis=1))
+    return res, lse
+
+
+def _edge_case(rng, V, rows, kind):
+    if kind == "ints":
+        l = rng.integers(-4, 5, size=(rows, V)).astype(np.float32)
+    elif kind == "const":
+        l = np.full((rows, V), 0.25, dtype=np.float32)
+    elif kind == "neginf":
+        l = rng.standard_normal((rows, V)).astype(np.float32)
+        l[rng.random((rows, V)) < 0.7] = -np.inf
+        l[:, 0] = np.where(np.all(np.isneginf(l), axis=1), 1.0, l[:, 0])
+    elif kind == "wide":
+        l = (rng.standard_normal((rows, V)) * 30).astype(np.float32)
+    else:
+        l = rng.standard_normal((rows, V)).astype(np.float32)
+    return l
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 64, 1000, 4097, 20000])
+@pytest.mark.parametrize("kind", ["normal", "ints", "const", "neginf", "wide"])
+def test_sampler_edge_cases(dev, ts, V, kind):
+    rng = np.random.default_rng(V * 10 + len(kind))
+    rows = 24
+    logits = _edge_case(rng, V, rows, kind)
+    max_lp = 7
+    params = workloads.random_params(rng, rows, V, max_lp)
+    say("sampler edge", V, kind)
+    got = _run_sampler(ts, dev, logits, params, 5, max_lp, ld_extra=3)
+    res, lse = _oracle_ref(logits, params, 5, max_lp)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=f"{V}/{kind}")
+
+
+def test_sampler_bad_rows(dev, ts):
+    rng = np.random.default_rng(0)
+    rows, V = 12, 500
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    logits[1, 7] = np.nan
+    logits[2, 9] = np.inf
+    logits[3, :] = -np.inf
+    params = workloads.random_params(rng, rows, V, 4)
+    params["temperature"][4] = -1.0
+    params["top_k"][5] = -2
+    params["top_p"][6] = 0.0
+    params["top_p"][7] = 1.5
+    params["n_logprobs"][8] = 5
+    params["temperature"][9] = np.inf
+    params["top_p"][10] = np.nan
+    params["temperature"][11] = np.nan
+    say("sampler bad rows")
+    got = _run_sampler(ts, dev, logits, params, 0, 4)
+    res, lse = _oracle_ref(logits, params, 0, 4)
+    assert got["row_status"].tolist() == [0, 2, 2, 2, 1, 1, 1, 1, 1, 1, 1, 1]
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0)
+    assert np.all(np.isnan(got["topn_logprobs"][1:]))
+
+
+@pytest.mark.parametrize("max_lp,n", [(0, 0), (300, 300), (1024, 700)])
+def test_sampler_logprob_widths(dev, ts, max_lp, n):
+    rng = np.random.default_rng(max_lp)
+    rows, V = 6, 3000
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    logits[0, 100:400] = 2.0   # a long tie run inside the top-N
+    params = workloads.random_params(rng, rows, V, max_lp)
+    params["n_logprobs"] = n
+    say("sampler widths", max_lp, n)
+    got = _run_sampler(ts, dev, logits, params, 0, max_lp)
+    res, lse = _oracle_ref(logits, params, 0, max_lp)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0)
+
+
+def test_sampler_row_offset_split_matches_single_call(dev, ts):
+    """A rank's share of rows (row_offset) draws exactly what one call over all
+    rows draws: the RNG is keyed on the global row."""
+    w = workloads.get("spec_decode")
+    rng = np.random.default_rng(8)
+    rows, V = 40, 5000
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    params = workloads.random_params(rng, rows, V, 5, greedy_frac=0.0)
+    say("sampler split", w.name)
+    whole = _run_sampler(ts, dev, logits, params, 100, 5)
+    a = _run_sampler(ts, dev, logits[:17], params[:17], 100, 5)
+    b = _run_sampler(ts, dev, logits[17:], params[17:], 117, 5)
+    for k in whole:
+        np.testing.assert_array_equal(np.concatenate([a[k], b[k]]), whole[k])
+
+
+def test_sampler_deterministic(dev, ts):
+    rng = np.random.default_rng(4)
+    rows, V = 32, 30000
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    params = workloads.random_params(rng, rows, V, 8)
+    say("sampler determinism")
+    a = _run_sampler(ts, dev, logits, params, 0, 8)
+    b = _run_sampler(ts, dev, logits, params, 0, 8)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k

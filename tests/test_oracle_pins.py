@@ -175,8 +175,45 @@ def test_top_p_one_and_k_v_keep_everything():
     rng = np.random.default_rng(3)
     l = rng.standard_normal(100)
     for k in (0, 100, 1000):
-        kept, flag = oracle.kept_set(l, 0.9, k, 1.0)
-        assert kept.tolist() == list(range(100)) and not flag
+        kept, amb = oracle.kept_set(l, 0.9, k, 1.0)
+        assert kept.tolist() == list(range(100)) and amb.size == 0
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_ambiguous_set_is_the_shifted_boundaries(seed):
+    """The ids near the top-p boundary are exactly those kept at p + window
+    but not at p - window."""
+    rng = np.random.default_rng(100 + seed)
+    V = 5000
+    l = rng.standard_normal(V) * 1.3
+    t = float(rng.uniform(0.3, 1.5))
+    k = int(rng.choice([0, 50, 1000]))
+    p = float(rng.uniform(0.3, 0.99999))
+    w = oracle.TOP_P_FLAG_WINDOW
+    kept, amb = oracle.kept_set(l, t, k, p)
+    small, _ = oracle.kept_set(l, t, k, p - w)
+    big, _ = oracle.kept_set(l, t, k, min(1.0, p + w))
+    assert set(amb.tolist()) == set(big.tolist()) - set(small.tolist())
+    assert set(small.tolist()) <= set(kept.tolist()) <= set(big.tolist())
+
+
+def test_top_p_flag_means_token_depends_on_boundary():
+    """A row is flagged exactly when sampling with the boundary moved to
+    p - window and to p + window draws different tokens."""
+    rng = np.random.default_rng(7)
+    V = 20000
+    l = (rng.standard_normal(V) * 1.3).astype(np.float32)
+    w = oracle.TOP_P_FLAG_WINDOW
+    flagged = 0
+    for row in range(150):
+        p = float(rng.uniform(0.5, 0.95))
+        r = oracle.sample_row(l, 1.0, 0, p, 0, 5, row, 0)
+        lo = oracle.sample_row(l, 1.0, 0, p - w, 0, 5, row, 0).token
+        hi = oracle.sample_row(l, 1.0, 0, p + w, 0, 5, row, 0).token
+        assert r.flag_top_p == (lo != hi)
+        assert r.token in (lo, hi) or r.flag_top_p
+        flagged += r.flag_top_p
+    assert flagged < 10   # a token rarely depends on a boundary this narrow
 
 
 # ---------------------------------------------------------------- logprobs

@@ -1,0 +1,215 @@
+"""Python binding of ``libtopsampling.so`` (MI355X / gfx950).
+
+Argument marshalling only: every step of the sampling path runs in the HIP
+kernels behind the C ABI (``include/top_sampling.h``).  PyTorch supplies device
+memory and the current stream.  Importing this package fails if the library is
+not built (``python -m top_sampling_amd.build``); there is no fallback.
+
+Calls mirror the C entry points:
+  lmhead_logits_local            local vocabulary projection, bf16 -> fp32
+  sampler_assemble_vocab_slices  stitch received vocabulary slices
+  sampler_sample                 per-row temperature / top-k / top-p /
+                                 logprobs / Gumbel-max sampling
+  sampler_workspace_bytes        workspace size query
+and ``compute_logits_local`` returns the rank's own ``[rows, V_local]`` slice,
+the local-logits hook of batch-sharded sampling (page "Qwen4Exp batch-sharded
+sampling: inside vLLM PR #61018", section "Why three lines were the whole
+job").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtopsampling.so")
+
+TS_OK, TS_EINVAL, TS_EUNSUPPORTED, TS_EWORKSPACE, TS_EHIP = 0, -1, -2, -3, -4
+TS_ROW_OK, TS_ROW_BAD_PARAMS, TS_ROW_BAD_LOGITS = 0, 1, 2
+TS_MAX_LOGPROBS = 1024
+TS_MAX_SLICES = 64
+PARAMS_BYTES = 24
+
+# (name, restype, argtypes) of every symbol the header declares.
+_VP, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+SYMBOLS = {
+    "lmhead_logits_local": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _VP]),
+    "sampler_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
+    "sampler_sample": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _I32, _VP, _VP, _VP, _VP,
+                                      _VP, _VP, _SZ, _VP]),
+    "sampler_assemble_vocab_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _VP]),
+    "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "ts_last_error": (ctypes.c_char_p, []),
+}
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m top_sampling_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SYMBOLS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class TopSamplingError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{lib.ts_status_string(code).decode()}: {msg}")
+        self.code = code
+
+
+class TopSamplingValueError(TopSamplingError, ValueError):
+    pass
+
+
+def _check(code: int) -> None:
+    if code == TS_OK:
+        return
+    msg = lib.ts_last_error().decode()
+    if code in (TS_EINVAL, TS_EUNSUPPORTED, TS_EWORKSPACE):
+        raise TopSamplingValueError(code, msg)
+    raise TopSamplingError(code, msg)
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+# ---------------------------------------------------------------- projection
+def lmhead_logits_local(hidden, lm_head, out=None, stream=None):
+    """fp32 ``[rows, V_local]`` logits of bf16 ``hidden [rows, H]`` against the
+    bf16 vocabulary slice ``lm_head [V_local, H]``.  ``out`` may be a column
+    slice of a wider fp32 buffer (its row stride is the leading dimension)."""
+    torch = _torch()
+    rows, h = hidden.shape
+    vocab, h2 = lm_head.shape
+    if h != h2:
+        raise ValueError(f"hidden size mismatch: {h} vs {h2}")
+    if hidden.dtype != torch.bfloat16 or lm_head.dtype != torch.bfloat16:
+        raise TypeError("hidden and lm_head must be bfloat16")
+    if hidden.stride(1) != 1 or lm_head.stride(1) != 1:
+        raise ValueError("hidden and lm_head must be K-contiguous")
+    if out is None:
+        out = torch.empty(rows, vocab, dtype=torch.float32, device=hidden.device)
+    if out.shape != (rows, vocab) or out.dtype != torch.float32 or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [rows, V_local] with unit column stride")
+    _check(lib.lmhead_logits_local(_ptr(hidden), rows, h, hidden.stride(0), _ptr(lm_head), vocab,
+                                   lm_head.stride(0), _ptr(out), out.stride(0),
+                                   _stream_ptr(stream)))
+    return out
+
+
+def compute_logits_local(hidden, lm_head, out=None, stream=None):
+    """The rank's own vocabulary shard ``[rows, V_local]``: no gather, no
+    full-vocabulary buffer anywhere."""
+    return lmhead_logits_local(hidden, lm_head, out=out, stream=stream)
+
+
+# ------------------------------------------------------------------ assembly
+def sampler_assemble_vocab_slices(slices, out=None, stream=None):
+    """``out[:, off_s:off_s+cols_s] = slices[s]`` (bit-exact)."""
+    torch = _torch()
+    n = len(slices)
+    if n < 1:
+        raise ValueError("need at least one slice")
+    rows = slices[0].shape[0]
+    for s in slices:
+        if s.dtype != torch.float32 or s.dim() != 2 or s.shape[0] != rows or s.stride(1) != 1:
+            raise ValueError("slices must be fp32 [rows, cols_s] with unit column stride")
+    total = sum(int(s.shape[1]) for s in slices)
+    if out is None:
+        out = torch.empty(rows, total, dtype=torch.float32, device=slices[0].device)
+    if out.shape != (rows, total) or out.stride(1) != 1 or out.dtype != torch.float32:
+        raise ValueError("out must be fp32 [rows, sum cols] with unit column stride")
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(s) for s in slices])
+    cols = (ctypes.c_int64 * n)(*[int(s.shape[1]) for s in slices])
+    lds = (ctypes.c_int64 * n)(*[int(s.stride(0)) for s in slices])
+    _check(lib.sampler_assemble_vocab_slices(ptrs, cols, lds, n, rows, _ptr(out), out.stride(0),
+                                             _stream_ptr(stream)))
+    return out
+
+
+# ------------------------------------------------------------------- sampler
+def sampler_workspace_bytes(rows: int, vocab: int, max_logprobs: int) -> int:
+    return int(lib.sampler_workspace_bytes(rows, vocab, max_logprobs))
+
+
+def params_to_device(params: np.ndarray, device):
+    """Copy a record array of row parameters (24-byte records) to the device."""
+    torch = _torch()
+    raw = np.ascontiguousarray(params).view(np.uint8).reshape(-1)
+    if raw.shape[0] != PARAMS_BYTES * params.shape[0]:
+        raise ValueError("parameter records must be 24 bytes")
+    return torch.from_numpy(raw.copy()).to(device)
+
+
+@dataclass
+class SampleOutput:
+    token_ids: object       # int32 [rows]
+    token_logprobs: object  # fp32 [rows]
+    topn_ids: object        # int32 [rows, max_logprobs]
+    topn_logprobs: object   # fp32 [rows, max_logprobs]
+    row_status: object      # int32 [rows]
+
+
+def allocate_sample_output(rows: int, max_logprobs: int, device) -> SampleOutput:
+    torch = _torch()
+    return SampleOutput(
+        torch.empty(rows, dtype=torch.int32, device=device),
+        torch.empty(rows, dtype=torch.float32, device=device),
+        torch.empty(rows, max_logprobs, dtype=torch.int32, device=device),
+        torch.empty(rows, max_logprobs, dtype=torch.float32, device=device),
+        torch.empty(rows, dtype=torch.int32, device=device),
+    )
+
+
+def allocate_workspace(rows: int, vocab: int, max_logprobs: int, device):
+    torch = _torch()
+    n = max(256, sampler_workspace_bytes(rows, vocab, max_logprobs))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sampler_sample(logits, params, row_offset: int = 0, max_logprobs: int = 0, out=None,
+                   workspace=None, stream=None) -> SampleOutput:
+    """Sample one token per row of fp32 ``logits [rows, V]`` (row stride = its
+    leading dimension).  ``params`` is a device uint8 tensor of 24-byte
+    ``ts_row_params`` records (see ``params_to_device``)."""
+    torch = _torch()
+    rows, vocab = logits.shape
+    if logits.dtype != torch.float32 or logits.stride(1) != 1:
+        raise ValueError("logits must be fp32 with unit column stride")
+    if params.dtype != torch.uint8 or params.numel() != PARAMS_BYTES * rows:
+        raise ValueError("params must be rows x 24 bytes (uint8)")
+    if out is None:
+        out = allocate_sample_output(rows, max_logprobs, logits.device)
+    if workspace is None:
+        workspace = allocate_workspace(rows, vocab, max_logprobs, logits.device)
+    _check(lib.sampler_sample(
+        _ptr(logits), rows, vocab, logits.stride(0), _ptr(params), row_offset, max_logprobs,
+        _ptr(out.token_ids), _ptr(out.token_logprobs),
+        _ptr(out.topn_ids) if max_logprobs > 0 else None,
+        _ptr(out.topn_logprobs) if max_logprobs > 0 else None,
+        _ptr(out.row_status), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+    return out

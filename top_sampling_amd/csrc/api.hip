@@ -1,0 +1,174 @@
+// C ABI of the batch-sharded sampling path (declared in include/top_sampling.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime: invalid configurations are rejected up front with a status
+// code and a per-thread message, and nothing is enqueued.  Valid calls only
+// enqueue kernels on the caller's stream (no allocation, no synchronisation).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "ts_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TS_OK;
+  return fail(TS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxDim = 0x7fffffff;
+
+}  // namespace
+
+extern "C" {
+
+const char* ts_status_string(int status) {
+  switch (status) {
+    case TS_OK: return "TS_OK";
+    case TS_EINVAL: return "TS_EINVAL";
+    case TS_EUNSUPPORTED: return "TS_EUNSUPPORTED";
+    case TS_EWORKSPACE: return "TS_EWORKSPACE";
+    case TS_EHIP: return "TS_EHIP";
+    default: return "TS_UNKNOWN";
+  }
+}
+
+const char* ts_last_error(void) { return g_last_error; }
+
+int lmhead_logits_local(const void* hidden, int64_t rows, int64_t hidden_dim, int64_t ld_hidden,
+                        const void* lm_head, int64_t vocab_local, int64_t ld_lm_head,
+                        float* logits, int64_t ld_logits, void* stream) {
+  if (rows < 0 || vocab_local < 0 || hidden_dim < 0)
+    return fail(TS_EINVAL, "negative size (rows=%lld vocab_local=%lld hidden_dim=%lld)",
+                (long long)rows, (long long)vocab_local, (long long)hidden_dim);
+  if (rows > kMaxDim || vocab_local > kMaxDim || hidden_dim > kMaxDim)
+    return fail(TS_EUNSUPPORTED, "size above 2^31-1");
+  if (rows == 0 || vocab_local == 0) return TS_OK;
+  if (hidden_dim == 0) return fail(TS_EINVAL, "hidden_dim == 0 with a non-empty output");
+  if (!hidden || !lm_head || !logits) return fail(TS_EINVAL, "NULL pointer");
+  if (ld_hidden < hidden_dim || ld_lm_head < hidden_dim || ld_logits < vocab_local)
+    return fail(TS_EINVAL, "leading dimension below the row width (ld_hidden=%lld ld_lm_head=%lld "
+                "ld_logits=%lld)", (long long)ld_hidden, (long long)ld_lm_head,
+                (long long)ld_logits);
+  if (hidden_dim % 8 || ld_hidden % 8 || ld_lm_head % 8)
+    return fail(TS_EUNSUPPORTED, "hidden_dim, ld_hidden and ld_lm_head must be multiples of 8");
+  if (!aligned(hidden, 16) || !aligned(lm_head, 16) || !aligned(logits, 4))
+    return fail(TS_EUNSUPPORTED, "hidden/lm_head must be 16-byte aligned, logits 4-byte aligned");
+  const hipError_t e = ts::launch_lmhead_gemm(
+      static_cast<const uint16_t*>(hidden), ld_hidden, static_cast<const uint16_t*>(lm_head),
+      ld_lm_head, logits, ld_logits, static_cast<int>(rows), static_cast<int>(vocab_local),
+      static_cast<int>(hidden_dim), static_cast<hipStream_t>(stream));
+  return hip_status(e, "lmhead_logits_local launch");
+}
+
+size_t sampler_workspace_bytes(int64_t rows, int64_t vocab, int32_t max_logprobs) {
+  if (rows < 0 || vocab < 0 || max_logprobs < 0) return 0;
+  return ts::sampler_workspace_size(rows, vocab, max_logprobs);
+}
+
+int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_logits,
+                   const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                   int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                   float* topn_logprobs, int32_t* row_status, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (rows < 0 || vocab < 0)
+    return fail(TS_EINVAL, "negative size (rows=%lld vocab=%lld)", (long long)rows,
+                (long long)vocab);
+  if (max_logprobs < 0) return fail(TS_EINVAL, "max_logprobs < 0");
+  if (max_logprobs > TS_MAX_LOGPROBS)
+    return fail(TS_EUNSUPPORTED, "max_logprobs %d above %d", max_logprobs, TS_MAX_LOGPROBS);
+  if (row_offset < 0) return fail(TS_EINVAL, "row_offset < 0");
+  if (rows > kMaxDim || vocab > kMaxDim) return fail(TS_EUNSUPPORTED, "size above 2^31-1");
+  if (rows == 0) return TS_OK;
+  if (vocab == 0) return fail(TS_EINVAL, "vocab == 0 with rows > 0");
+  if (ld_logits < vocab) return fail(TS_EINVAL, "ld_logits %lld < vocab %lld",
+                                     (long long)ld_logits, (long long)vocab);
+  if (!logits || !params || !token_ids) return fail(TS_EINVAL, "NULL logits/params/token_ids");
+  if (max_logprobs > 0 && (!topn_ids || !topn_logprobs))
+    return fail(TS_EINVAL, "NULL top-N outputs with max_logprobs > 0");
+  if (!aligned(logits, 4) || !aligned(params, 8) || !aligned(token_ids, 4))
+    return fail(TS_EUNSUPPORTED, "misaligned pointer");
+  const size_t need = ts::sampler_workspace_size(rows, vocab, max_logprobs);
+  if (!workspace || workspace_bytes < need)
+    return fail(TS_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(TS_EUNSUPPORTED, "workspace not 256-byte aligned");
+  ts::SamplerArgs a;
+  a.logits = logits;
+  a.ld = ld_logits;
+  a.rows = static_cast<int>(rows);
+  a.vocab = static_cast<int>(vocab);
+  a.params = params;
+  a.row_offset = row_offset;
+  a.max_logprobs = max_logprobs;
+  a.token_ids = token_ids;
+  a.token_logprobs = token_logprobs;
+  a.topn_ids = topn_ids;
+  a.topn_logprobs = topn_logprobs;
+  a.row_status = row_status;
+  const hipError_t e =
+      ts::launch_sampler(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+  return hip_status(e, "sampler_sample launch");
+}
+
+int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* slice_cols,
+                                  const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                                  float* out, int64_t ld_out, void* stream) {
+  if (n_slices < 1 || n_slices > TS_MAX_SLICES)
+    return fail(n_slices < 1 ? TS_EINVAL : TS_EUNSUPPORTED, "n_slices %d not in [1, %d]",
+                n_slices, TS_MAX_SLICES);
+  if (rows < 0) return fail(TS_EINVAL, "rows < 0");
+  if (!slices || !slice_cols || !slice_ld) return fail(TS_EINVAL, "NULL slice arrays");
+  ts::AssembleSlices s;
+  s.n = n_slices;
+  int64_t total = 0;
+  bool vec4 = aligned(out, 16) && (ld_out % 4 == 0);
+  s.chunk_start[0] = 0;
+  for (int i = 0; i < n_slices; ++i) {
+    const int64_t c = slice_cols[i];
+    if (c < 0) return fail(TS_EINVAL, "slice %d has negative width", i);
+    if (slice_ld[i] < c) return fail(TS_EINVAL, "slice %d leading dimension below its width", i);
+    if (rows > 0 && c > 0 && !slices[i]) return fail(TS_EINVAL, "slice %d is NULL", i);
+    if (slices[i] && !aligned(slices[i], 4)) return fail(TS_EUNSUPPORTED, "slice %d misaligned", i);
+    s.ptr[i] = slices[i];
+    s.cols[i] = c;
+    s.ld[i] = slice_ld[i];
+    s.col_off[i] = total;
+    vec4 = vec4 && aligned(slices[i], 16) && (slice_ld[i] % 4 == 0) && (c % 4 == 0) &&
+           (total % 4 == 0);
+    s.chunk_start[i + 1] = s.chunk_start[i] + (c + 4095) / 4096;
+    total += c;
+  }
+  if (ld_out < total) return fail(TS_EINVAL, "ld_out %lld below total width %lld",
+                                  (long long)ld_out, (long long)total);
+  if (rows == 0 || total == 0) return TS_OK;
+  if (!out) return fail(TS_EINVAL, "NULL out");
+  if (!aligned(out, 4)) return fail(TS_EUNSUPPORTED, "out misaligned");
+  if (s.chunk_start[n_slices] > kMaxDim) return fail(TS_EUNSUPPORTED, "too many column chunks");
+  // Slices must not overlap the output rows they are copied into.
+  const char* ob = reinterpret_cast<const char*>(out);
+  const char* oe = reinterpret_cast<const char*>(out + (rows - 1) * ld_out + total);
+  for (int i = 0; i < n_slices; ++i) {
+    if (s.cols[i] == 0) continue;
+    const char* sb = reinterpret_cast<const char*>(slices[i]);
+    const char* se = reinterpret_cast<const char*>(slices[i] + (rows - 1) * slice_ld[i] + s.cols[i]);
+    if (sb < oe && ob < se) return fail(TS_EINVAL, "slice %d overlaps out", i);
+  }
+  s.vec4 = vec4 ? 1 : 0;
+  const hipError_t e = ts::launch_assemble(s, rows, out, ld_out, static_cast<hipStream_t>(stream));
+  return hip_status(e, "sampler_assemble_vocab_slices launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+// Device helpers shared by the gfx950 kernels: order-preserving float keys,
+// Philox4x32-10, Gumbel noise and deterministic wave/block reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ts {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// ------------------------------------------------------------ float order keys
+// Monotone map fp32 -> uint32: a < b (as reals, -0 == +0) iff key(a) < key(b).
+// Negative floats have all bits flipped, non-negative ones get the sign bit
+// set.  -0 is folded onto +0 first so equal values share one key.  NaNs are
+// screened out by the callers before keys are compared.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  b = (b == 0x80000000u) ? 0u : b;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(b);
+}
+
+// ------------------------------------------------------------- Philox4x32-10
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11): a 10-round counter-based generator.  Each round takes the 32x32->64
+// products of counter words 0 and 2 with two odd multipliers; the new counter
+// is (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0).  The key advances by two Weyl
+// increments before every round after the first.
+struct U32x4 {
+  uint32_t v[4];
+};
+
+__device__ __forceinline__ U32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c0;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c2;
+    const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c3 ^ k1;
+    c1 = static_cast<uint32_t>(p1);
+    c3 = static_cast<uint32_t>(p0);
+    c0 = n0;
+    c2 = n2;
+  }
+  U32x4 out;
+  out.v[0] = c0;
+  out.v[1] = c1;
+  out.v[2] = c2;
+  out.v[3] = c3;
+  return out;
+}
+
+// The four words for tokens 4q .. 4q+3 of global row `row`: one Philox call
+// with counter (q, row lo, row hi, 0) and key (seed lo, seed hi).
+__device__ __forceinline__ U32x4 token_words(uint64_t seed, uint64_t row, uint32_t q) {
+  return philox4x32_10(q, static_cast<uint32_t>(row), static_cast<uint32_t>(row >> 32), 0u,
+                       static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+}
+
+// Standard Gumbel noise from one 32-bit word: u = ((x >> 9) + 1/2) * 2^-23 is
+// exact in fp32 and lies in [2^-24, 1 - 2^-24]; g = -ln(-ln u).
+__device__ __forceinline__ float gumbel_from_word(uint32_t x) {
+  const float u = (static_cast<float>(x >> 9) + 0.5f) * 1.1920928955078125e-7f;
+  return -logf(-logf(u));
+}
+
+// ------------------------------------------------------------ reductions
+// Ordering of (key, id) candidates: larger key first, lower id on ties.
+__device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+__device__ __forceinline__ bool better_u(uint32_t ka, int ia, uint32_t kb, int ib) {
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ void wave_best(float& k, int& i) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float k2 = __shfl_xor(k, o, kWave);
+    const int i2 = __shfl_xor(i, o, kWave);
+    if (better(k2, i2, k, i)) {
+      k = k2;
+      i = i2;
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_best_u(uint32_t& k, int& i) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const uint32_t k2 = __shfl_xor(k, o, kWave);
+    const int i2 = __shfl_xor(i, o, kWave);
+    if (better_u(k2, i2, k, i)) {
+      k = k2;
+      i = i2;
+    }
+  }
+}
+
+// Inclusive prefix sum within a wave (lane order).
+template <typename T>
+__device__ __forceinline__ T wave_inclusive_scan(T v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const T u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Block-wide helpers for a block of NT threads.  `scratch` must hold NT/64
+// entries of the value type; every thread of the block must call them.
+template <int NT, typename T>
+__device__ __forceinline__ T block_sum(T v, T* scratch) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  T t = 0;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) t += scratch[j];  // same order in every thread
+  return t;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  v = wave_max(v);
+  __syncthreads();
+  if (lane == 0) scratch[w] = v;
+  __syncthreads();
+  float t = scratch[0];
+#pragma unroll
+  for (int j = 1; j < NW; ++j) t = fmaxf(t, scratch[j]);
+  return t;
+}
+
+template <int NT>
+__device__ __forceinline__ void block_best(float& k, int& i, float* sk, int* si) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  wave_best(k, i);
+  __syncthreads();
+  if (lane == 0) {
+    sk[w] = k;
+    si[w] = i;
+  }
+  __syncthreads();
+  k = sk[0];
+  i = si[0];
+#pragma unroll
+  for (int j = 1; j < NW; ++j)
+    if (better(sk[j], si[j], k, i)) {
+      k = sk[j];
+      i = si[j];
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void block_best_u(uint32_t& k, int& i, uint32_t* sk, int* si) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  wave_best_u(k, i);
+  __syncthreads();
+  if (lane == 0) {
+    sk[w] = k;
+    si[w] = i;
+  }
+  __syncthreads();
+  k = sk[0];
+  i = si[0];
+#pragma unroll
+  for (int j = 1; j < NW; ++j)
+    if (better_u(sk[j], si[j], k, i)) {
+      k = sk[j];
+      i = si[j];
+    }
+}
+
+// Exclusive prefix sum over the block in thread order; returns the block total
+// through `total`.
+template <int NT, typename T>
+__device__ __forceinline__ T block_exclusive_scan(T v, T* scratch, T& total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const T inc = wave_inclusive_scan(v);
+  __syncthreads();
+  if (lane == kWave - 1) scratch[w] = inc;
+  __syncthreads();
+  T before = 0, all = 0;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    before += (j < w) ? scratch[j] : T(0);
+    all += scratch[j];
+  }
+  total = all;
+  return before + inc - v;
+}
+
+}  // namespace ts

@@ -1,0 +1,52 @@
+// Host-side interfaces between the C ABI layer (api.hip) and the kernel files.
+// Every launcher assumes its arguments were validated by the ABI layer and
+// returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/top_sampling.h"
+
+namespace ts {
+
+// ---------------------------------------------------------------- projection
+hipError_t launch_lmhead_gemm(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* lm_head,
+                              int64_t ld_lm_head, float* logits, int64_t ld_logits, int rows,
+                              int vocab, int hidden_dim, hipStream_t stream);
+
+// ------------------------------------------------------------------- sampler
+struct SamplerArgs {
+  const float* logits;
+  int64_t ld;
+  int rows;
+  int vocab;
+  const ts_row_params* params;
+  int64_t row_offset;
+  int max_logprobs;
+  int32_t* token_ids;
+  float* token_logprobs;  // may be null
+  int32_t* topn_ids;      // may be null iff max_logprobs == 0
+  float* topn_logprobs;
+  int32_t* row_status;    // may be null
+};
+
+size_t sampler_workspace_size(int64_t rows, int64_t vocab, int max_logprobs);
+hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+// ------------------------------------------------------------------ assembly
+struct AssembleSlices {
+  const float* ptr[TS_MAX_SLICES];
+  int64_t cols[TS_MAX_SLICES];
+  int64_t ld[TS_MAX_SLICES];
+  int64_t col_off[TS_MAX_SLICES];
+  int64_t chunk_start[TS_MAX_SLICES + 1];  // prefix of per-slice column chunks
+  int n;
+  int vec4;  // every pointer, leading dimension and offset allows float4 copies
+};
+
+hipError_t launch_assemble(const AssembleSlices& s, int64_t rows, float* out, int64_t ld_out,
+                           hipStream_t stream);
+
+}  // namespace ts
