@@ -267,8 +267,9 @@ def sample_row(logits: np.ndarray, temperature: float, top_k: int, top_p: float,
     order = np.lexsort((ids, -l))
     topn_ids = np.full(max_logprobs, -1, dtype=np.int64)
     topn_lp = np.full(max_logprobs, -np.inf)
-    topn_ids[:n] = order[:n]
-    topn_lp[:n] = logprob[order[:n]]
+    n_listed = min(n, vocab)               # a row has only V tokens to list
+    topn_ids[:n_listed] = order[:n_listed]
+    topn_lp[:n_listed] = logprob[order[:n_listed]]
 
     # R2: greedy.
     if t < GREEDY_EPS or k == 1:

@@ -9,3 +9,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
     config.addinivalue_line("markers", "slow: long CPU test")
+
+
+def pytest_runtest_logreport(report):
+    """Print a failure's details as soon as it happens, so a crash later in
+    the session cannot swallow them."""
+    if report.failed:
+        print(f"\n--- {report.nodeid} ({report.when}) ---\n{str(report.longrepr)[-4000:]}",
+              flush=True)

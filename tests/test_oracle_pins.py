@@ -244,6 +244,19 @@ def test_logprobs_match_scipy_and_topn_order():
     assert r.token_logprob == pytest.approx(ref[r.token], abs=1e-12)
 
 
+def test_top_n_wider_than_vocabulary():
+    """Asking for more log-probabilities than the row has tokens lists each
+    token once (a 3-token row: ids by descending logit) and leaves the other
+    slots unused."""
+    l = np.array([0.5, 2.0, -1.0], dtype=np.float32)
+    r = oracle.sample_row(l, 1.0, 0, 1.0, 6, 3, 0, 8)
+    assert r.topn_ids.tolist() == [1, 0, 2, -1, -1, -1, -1, -1]
+    assert np.all(np.isneginf(r.topn_logprobs[3:]))
+    r1 = oracle.sample_row(np.array([4.0], dtype=np.float32), 0.7, 0, 1.0, 5, 3, 0, 5)
+    assert r1.topn_ids.tolist() == [0, -1, -1, -1, -1] and r1.token == 0
+    assert r1.topn_logprobs[0] == 0.0
+
+
 def test_unused_slots_and_zero_logprobs():
     l = np.linspace(-1, 1, 50).astype(np.float32)
     r = oracle.sample_row(l, 1.0, 0, 1.0, 0, 1, 0, 6)

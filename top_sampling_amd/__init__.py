@@ -47,6 +47,11 @@ SYMBOLS = {
 
 
 def _load() -> ctypes.CDLL:
+    # PyTorch ships its own HIP runtime.  Load it first so the library binds to
+    # that same runtime: a second copy of the HIP/HSA runtime in the process
+    # (the one under /opt/rocm) would own the device independently.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is not built; run `python -m top_sampling_amd.build` (hipcc, gfx950)")
