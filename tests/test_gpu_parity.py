@@ -213,8 +213,23 @@ def _load_expected(name):
     return dict(np.load(os.path.join(GOLDEN, f"sampler_expected_{name}.npz")))
 
 
+ROUTES = {"fast": {}, "exact": {"TS_SAMPLER_EXACT": "1"}, "probe": {"TS_SAMPLER_FORCE_PROBE": "1"}}
+
+
+@pytest.fixture(params=list(ROUTES))
+def route(request, monkeypatch):
+    """The sampler's routes: the single-read fast path, the exact per-row
+    kernel for every row, and the probe pass for every top-p-only row.  All
+    must match the oracle."""
+    for k in ("TS_SAMPLER_EXACT", "TS_SAMPLER_FORCE_PROBE"):
+        monkeypatch.delenv(k, raising=False)
+    for k, v in ROUTES[request.param].items():
+        monkeypatch.setenv(k, v)
+    return request.param
+
+
 @pytest.mark.parametrize("name", ["tiny", "decode", "spec_decode", "rank_share", "large"])
-def test_sampler_workloads(dev, ts, name):
+def test_sampler_workloads(dev, ts, name, route):
     import torch
 
     w = workloads.get(name)
@@ -229,7 +244,7 @@ def test_sampler_workloads(dev, ts, name):
         for (r0, r1), dg in zip(exp["digest_rows"], exp["logits_digests"]):
             assert __import__("hashlib").sha256(
                 np.ascontiguousarray(logits[r0:r1]).tobytes()).hexdigest() == dg
-    say("sampler", name, logits.shape)
+    say("sampler", name, route, logits.shape)
     if name == "rank_share":
         # receive side: four vocabulary slices assembled on the device, then sampled
         cuts = np.concatenate([[0], np.cumsum(w.slice_cols)])
@@ -248,7 +263,7 @@ def test_sampler_workloads(dev, ts, name):
     mism = _compare(got, exp["token_ids"], exp["token_logprobs"], exp["topn_ids"],
                     exp["topn_logprobs"], exp["row_status"], flagged, exp["lse"], logits,
                     label=name)
-    say(f"{name}: rows={w.rows} flagged={int(flagged.sum())} mismatched_flagged={mism}")
+    say(f"{name}/{route}: rows={w.rows} flagged={int(flagged.sum())} mismatched_flagged={mism}")
 
 
 def _oracle_ref(logits, params, row_offset, max_logprobs):
@@ -276,22 +291,22 @@ def _edge_case(rng, V, rows, kind):
     return l
 
 
-@pytest.mark.parametrize("V", [1, 2, 3, 7, 64, 1000, 4097, 20000])
+@pytest.mark.parametrize("V", [1, 2, 3, 7, 64, 1000, 4097, 20000, 70001])
 @pytest.mark.parametrize("kind", ["normal", "ints", "const", "neginf", "wide"])
-def test_sampler_edge_cases(dev, ts, V, kind):
+def test_sampler_edge_cases(dev, ts, V, kind, route):
     rng = np.random.default_rng(V * 10 + len(kind))
     rows = 24
     logits = _edge_case(rng, V, rows, kind)
     max_lp = 7
     params = workloads.random_params(rng, rows, V, max_lp)
-    say("sampler edge", V, kind)
+    say("sampler edge", V, kind, route)
     got = _run_sampler(ts, dev, logits, params, 5, max_lp, ld_extra=3)
     res, lse = _oracle_ref(logits, params, 5, max_lp)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
              res.row_status, res.flagged, lse, logits, max_frac=1.0, label=f"{V}/{kind}")
 
 
-def test_sampler_bad_rows(dev, ts):
+def test_sampler_bad_rows(dev, ts, route):
     rng = np.random.default_rng(0)
     rows, V = 12, 500
     logits = rng.standard_normal((rows, V)).astype(np.float32)
@@ -317,7 +332,7 @@ def test_sampler_bad_rows(dev, ts):
 
 
 @pytest.mark.parametrize("max_lp,n", [(0, 0), (300, 300), (1024, 700)])
-def test_sampler_logprob_widths(dev, ts, max_lp, n):
+def test_sampler_logprob_widths(dev, ts, max_lp, n, route):
     rng = np.random.default_rng(max_lp)
     rows, V = 6, 3000
     logits = rng.standard_normal((rows, V)).astype(np.float32)
@@ -357,3 +372,22 @@ def test_sampler_deterministic(dev, ts):
     b = _run_sampler(ts, dev, logits, params, 0, 8)
     for k in a:
         assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+
+def test_gumbel_noise_on_flat_rows(dev, ts, route):
+    """With every logit equal, the sampled token is the argmax of the Gumbel
+    noise alone, so these rows check the noise itself (Philox words, the
+    uniform map and both logarithms) against the oracle's float64 values."""
+    rows, V = 48, 50000
+    logits = np.full((rows, V), 0.5, dtype=np.float32)
+    params = np.zeros(rows, dtype=workloads.PARAMS_DTYPE)
+    params["temperature"] = np.linspace(0.3, 1.7, rows).astype(np.float32)
+    params["top_p"] = np.where(np.arange(rows) % 2 == 0, 1.0, 0.999).astype(np.float32)
+    params["n_logprobs"] = 3
+    params["seed"] = np.arange(rows, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15)
+    say("flat rows", route)
+    got = _run_sampler(ts, dev, logits, params, 1 << 33, 3)
+    res, lse = _oracle_ref(logits, params, 1 << 33, 3)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label="flat")
+    assert res.flagged.sum() <= 1

@@ -68,10 +68,23 @@ __device__ __forceinline__ U32x4 token_words(uint64_t seed, uint64_t row, uint32
 }
 
 // Standard Gumbel noise from one 32-bit word: u = ((x >> 9) + 1/2) * 2^-23 is
-// exact in fp32 and lies in [2^-24, 1 - 2^-24]; g = -ln(-ln u).
+// exact in fp32 and lies in [2^-24, 1 - 2^-24]; g = -ln(-ln u).  Both
+// logarithms use the hardware base-2 logarithm (v_log_f32) scaled by ln 2:
+// u and -ln u are normal numbers here, and the result's error (a few ulp of
+// -ln u, i.e. ~1e-7 relative, so ~1e-6 absolute on g) is far below the
+// 1e-4 key gap at which two Gumbel keys count as tied.
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+
 __device__ __forceinline__ float gumbel_from_word(uint32_t x) {
   const float u = (static_cast<float>(x >> 9) + 0.5f) * 1.1920928955078125e-7f;
-  return -logf(-logf(u));
+  const float a = __builtin_amdgcn_logf(u) * -kLn2;  // -ln u > 0
+  return __builtin_amdgcn_logf(a) * -kLn2;
+}
+
+// exp(x) for x <= 0 through the hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * kLog2e);
 }
 
 // ------------------------------------------------------------ reductions
@@ -203,6 +216,56 @@ __device__ __forceinline__ void block_best_u(uint32_t& k, int& i, uint32_t* sk, 
       k = sk[j];
       i = si[j];
     }
+}
+
+// Bitonic sort of one value per lane across the wave, largest at lane 0
+// (compare-exchange through lane shuffles; no LDS, no barrier).
+__device__ __forceinline__ float wave_sort_desc(float x) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float y = __shfl_xor(x, j, kWave);
+      const bool desc = (lane & k) == 0;
+      const bool lower = (lane & j) == 0;
+      x = (desc == lower) ? fmaxf(x, y) : fminf(x, y);
+    }
+  }
+  return x;
+}
+
+// Same over four values per lane (256 per wave, element index lane * 4 + i);
+// afterwards v[i] of lane l holds rank 4 * l + i.
+__device__ __forceinline__ void wave_sort4_desc(float (&v)[4]) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int k = 2; k <= 4 * kWave; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 4) {
+        const int lj = j >> 2;
+        const bool lower = (lane & lj) == 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int idx = lane * 4 + i;
+          const bool desc = (idx & k) == 0;
+          const float y = __shfl_xor(v[i], lj, kWave);
+          v[i] = (desc == lower) ? fmaxf(v[i], y) : fminf(v[i], y);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i & j) continue;
+          const int idx = lane * 4 + i;
+          const bool desc = (idx & k) == 0;
+          const float a = v[i], b = v[i + j];
+          v[i] = desc ? fmaxf(a, b) : fminf(a, b);
+          v[i + j] = desc ? fminf(a, b) : fmaxf(a, b);
+        }
+      }
+    }
+  }
 }
 
 // Exclusive prefix sum over the block in thread order; returns the block total

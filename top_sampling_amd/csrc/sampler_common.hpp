@@ -1,0 +1,239 @@
+// Definitions shared by the sampler kernels (fast path and exact path).
+//
+// Semantics (the page "Qwen4Exp batch-sharded sampling: inside vLLM PR
+// #61018", section "What batch-sharded sampling is, in one paragraph", names
+// top-k, top-p and log-probabilities but not their arithmetic; the readings
+// below are the ones the C ABI documents):
+//   * log-probabilities: raw log_softmax of the row;
+//   * greedy (temperature < TS_GREEDY_EPS or top_k == 1): argmax, lowest id;
+//   * otherwise temperature, then top-k (ties with the k-th largest kept),
+//     then top-p over the temperature-scaled distribution renormalised on the
+//     top-k set (the crossing token and its ties kept), then Gumbel-max with
+//     key (l - max) / T + g, g from Philox4x32-10 keyed on (seed, global row,
+//     token id), lowest id on exact ties.
+#pragma once
+
+#include <math.h>
+
+#include "device_common.hpp"
+#include "ts_internal.hpp"
+
+namespace ts {
+
+// ------------------------------------------------------------------ row kinds
+enum RowKind : int {
+  KIND_BAD = 0,     // invalid parameters
+  KIND_GREEDY = 1,  // argmax
+  KIND_TOPK = 2,    // 0 < top_k < V (top_k <= kFastTopKMax), any top_p
+  KIND_FULL = 3,    // no filter: Gumbel-max over every token
+  KIND_TOPP = 4,    // top-p only
+  KIND_EXACT = 5    // handled by the exact per-row kernel (large top_k)
+};
+
+constexpr int kFastTopKMax = 1024;
+
+__device__ __forceinline__ bool params_ok(const ts_row_params& p, int max_logprobs) {
+  if (!(p.temperature >= 0.0f) || isinf(p.temperature)) return false;
+  if (p.top_k < 0) return false;
+  if (!(p.top_p > 0.0f && p.top_p <= 1.0f)) return false;
+  if (p.n_logprobs < 0 || p.n_logprobs > max_logprobs) return false;
+  return true;
+}
+
+// How many of a chunk's largest logits its candidate list must hold.
+__device__ __forceinline__ int cand_target(int kind, const ts_row_params& p, int V) {
+  const int n_eff = p.n_logprobs < V ? p.n_logprobs : V;
+  int M = n_eff > 1 ? n_eff : 1;
+  if (kind == 2 && p.top_k > M) M = p.top_k;         // KIND_TOPK
+  if (kind == 4 && 64 > M) M = 64;                   // KIND_TOPP
+  return M < V ? M : V;
+}
+
+__device__ __forceinline__ int row_kind(const ts_row_params& p, int V, int max_logprobs) {
+  if (!params_ok(p, max_logprobs)) return KIND_BAD;
+  if (p.temperature < TS_GREEDY_EPS || p.top_k == 1) return KIND_GREEDY;
+  if (p.top_k > 0 && p.top_k < V) return p.top_k <= kFastTopKMax ? KIND_TOPK : KIND_EXACT;
+  return p.top_p < 1.0f ? KIND_TOPP : KIND_FULL;
+}
+
+// ------------------------------------------------------------------- numerics
+constexpr float kMassScale = 1099511627776.0f;  // 2^40: fixed-point unit of a weight in [0, 1]
+constexpr double kMassUnit = 1.0 / 1099511627776.0;
+constexpr float kGumbelMax = 16.7f;  // above every Gumbel value a 23-bit uniform can give
+constexpr float kMinGumbel = -2.9f;  // below every such Gumbel value (-ln(-ln 2^-24) = -2.81)
+
+__device__ __forceinline__ unsigned long long fixed_mass(float w) {
+  return static_cast<unsigned long long>(w * kMassScale);
+}
+
+// A candidate packed so that a larger value means "earlier in the order
+// (logit descending, token id ascending)": key in the high word, inverted id
+// in the low word.  Zero means "no candidate" (every real key is > 0).
+__device__ __forceinline__ unsigned long long pack_cand(uint32_t key, int id) {
+  return (static_cast<unsigned long long>(key) << 32) | static_cast<uint32_t>(~id);
+}
+__device__ __forceinline__ uint32_t cand_key(unsigned long long c) {
+  return static_cast<uint32_t>(c >> 32);
+}
+__device__ __forceinline__ int cand_id(unsigned long long c) {
+  return static_cast<int>(~static_cast<uint32_t>(c));
+}
+
+// Gumbel key of token `id` (logit l) of a row with maximum m.
+__device__ __forceinline__ float gumbel_key(float l, float m, float inv_t, uint64_t seed,
+                                            uint64_t grow, int id) {
+  const U32x4 w = token_words(seed, grow, static_cast<uint32_t>(id) >> 2);
+  return (l - m) * inv_t + gumbel_from_word(w.v[id & 3]);
+}
+
+// ------------------------------------------------------------ workspace layout
+constexpr int kCandCap = 1536;    // logit candidates per chunk
+constexpr int kKeyCap = 32;       // Gumbel-key candidates per chunk (top-p-only rows)
+constexpr int kKeyTarget = 8;     // chunk keys above which the key list is complete
+constexpr int kProbes = 8;        // probe points per top-p-only row
+constexpr int kMaxChunks = 128;   // chunks per row
+constexpr int kChunkThreads = 256;
+constexpr int kChunkVec = 16;     // float4 per thread
+constexpr int kChunkMax = kChunkThreads * kChunkVec * 4;  // 16384 logits
+constexpr int kListMax = 4096;    // merged candidates a row may keep in LDS
+constexpr float kKeyMargin = 1e-4f;  // rounding margin between chunk-local and row keys
+
+struct ChunkRec {  // one per (row, chunk); 64 bytes
+  float cmax;      // chunk maximum
+  float sumexp;    // sum exp(l - cmax)
+  float tmass;     // sum exp((l - cmax) / T)                (top-p-only rows)
+  uint32_t kt;     // logit candidate threshold: every logit with key >= kt is listed
+  int ncand;       // listed logit candidates
+  int status;      // 0 ok, 1 NaN/+inf seen, 2 candidate overflow
+  int nkey;        // listed Gumbel-key candidates (full and top-p-only rows)
+  float kfloor;    // every token whose key (l - cmax)/T + g >= kfloor is listed
+  int pad[8];
+};
+
+struct ProbeRec {  // a top-p-only row whose boundary lies below the listed logits
+  double z;        // total temperature-scaled mass, relative to the row maximum
+  float m, lse, inv_t;
+  int npts;        // probe tokens, best Gumbel key first
+  int id[kProbes];
+  float pt[kProbes];  // their logits
+};
+
+struct FastLayout {
+  int S;  // chunks per row
+  int L;  // logits per chunk (multiple of 4; the last chunk may be shorter)
+  size_t off_ctr, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part, total;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Chunks per row: at most kChunkMax logits each, enough workgroups to fill
+// the chip (about 1024), chunks of at least 1024 logits, at most kMaxChunks.
+inline FastLayout make_layout(int64_t rows, int64_t vocab) {
+  FastLayout l{};
+  int64_t S = (vocab + kChunkMax - 1) / kChunkMax;
+  int64_t want = rows > 0 ? (1024 + rows - 1) / rows : 1;
+  int64_t most = vocab / 1024 > 0 ? vocab / 1024 : 1;
+  if (want > most) want = most;
+  if (want > kMaxChunks) want = kMaxChunks;
+  if (S < want) S = want;
+  if (S < 1) S = 1;
+  int64_t L = (vocab + S - 1) / S;
+  L = (L + 3) / 4 * 4;
+  if (L < 4) L = 4;
+  S = (vocab + L - 1) / L;
+  if (S < 1) S = 1;
+  l.S = static_cast<int>(S);
+  l.L = static_cast<int>(L);
+  const size_t R = static_cast<size_t>(rows);
+  const size_t RS = R * static_cast<size_t>(S);
+  size_t off = 0;
+  l.off_ctr = off;  // [0] exact rows, [1] probe rows
+  off = align_up(off + 256, 256);
+  l.off_exact = off;
+  off = align_up(off + R * sizeof(int), 256);
+  l.off_probe = off;
+  off = align_up(off + R * sizeof(int), 256);
+  l.off_chunk = off;
+  off = align_up(off + RS * sizeof(ChunkRec), 256);
+  l.off_cand = off;
+  off = align_up(off + RS * kCandCap * sizeof(unsigned long long), 256);
+  l.off_key = off;
+  off = align_up(off + RS * kKeyCap * sizeof(int), 256);
+  l.off_prec = off;
+  off = align_up(off + R * sizeof(ProbeRec), 256);
+  l.off_part = off;
+  off = align_up(off + RS * kProbes * sizeof(double), 256);
+  l.total = off;
+  return l;
+}
+
+inline bool fast_path_supported(int64_t rows, int64_t vocab) {
+  if (vocab > static_cast<int64_t>(kChunkMax) * kMaxChunks) return false;
+  return rows * static_cast<int64_t>(make_layout(rows, vocab).S) <= 0x7fffffff;
+}
+
+// ---------------------------------------------------------- block utilities
+typedef double double4v __attribute__((ext_vector_type(4)));
+typedef double double2v __attribute__((ext_vector_type(2)));
+
+// Sort n (a power of two) packed candidates in LDS, largest first.
+template <int NT>
+__device__ void bitonic_sort_desc(unsigned long long* s, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += NT) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const unsigned long long a = s[i], b = s[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            s[i] = b;
+            s[ixj] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Radix digit search from the top bin down over `nb` LDS counts (NT threads,
+// nb <= NT * BPT): finds d with above(d) < rem <= above(d) + cnt[d], where
+// above(d) counts bins > d.  Writes d and above(d) to *sel_d / *sel_above.
+template <int NT, int BPT>
+__device__ void select_digit_top(const uint32_t* cnt, int nb, uint32_t rem, uint32_t* scratch,
+                                 uint32_t* sel_d, uint32_t* sel_above) {
+  uint32_t h[BPT];
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int b = nb - 1 - (static_cast<int>(threadIdx.x) * BPT + j);
+    h[j] = b >= 0 ? cnt[b] : 0u;
+    s += h[j];
+  }
+  uint32_t total;
+  uint32_t ex = block_exclusive_scan<NT, uint32_t>(s, scratch, total);
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int b = nb - 1 - (static_cast<int>(threadIdx.x) * BPT + j);
+    if (b >= 0 && ex < rem && rem <= ex + h[j]) {
+      *sel_d = static_cast<uint32_t>(b);
+      *sel_above = ex;
+    }
+    ex += h[j];
+  }
+  __syncthreads();
+}
+
+// ----------------------------------------------------------------- launchers
+// Finishes probe rows and computes exact rows (all rows when lay == nullptr).
+hipError_t launch_sampler_finish(const SamplerArgs& a, const FastLayout* lay, uint8_t* ws,
+                                 hipStream_t stream);
+
+}  // namespace ts

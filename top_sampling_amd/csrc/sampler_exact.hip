@@ -1,48 +1,42 @@
-// Per-row sampler for batch-sharded sampling on gfx950.
+// Finishing kernel of the sampler and the exact per-row sampler (gfx950).
 //
-// The sampler runs on the rank's slice of requests, batch x (speculative
-// tokens + 1) rows of full-vocabulary fp32 logits, and does temperature,
-// top-k, top-p, log-probabilities and seeded sampling (page "Qwen4Exp
-// batch-sharded sampling: inside vLLM PR #61018", orcarouter.ai blog, section
-// "What batch-sharded sampling is, in one paragraph"; the page names the
-// filters and a non-negative max_logprobs, not their arithmetic).  Semantics
-// implemented here:
-//   * log-probabilities are the raw log_softmax of the row;
-//   * greedy (temperature < TS_GREEDY_EPS or top_k == 1): argmax, lowest id;
-//   * otherwise temperature, then top-k (every token tied with the k-th
-//     largest logit kept), then top-p on the temperature-scaled distribution
-//     renormalised over the top-k set (the token whose cumulative mass first
-//     reaches p is kept, with its ties), then Gumbel-max over the kept set
-//     with Philox4x32-10 noise keyed on (seed, global row, token id).
-//
-// Exact kernel: one 1024-thread workgroup per row, radix selection on
-// order-preserving 32-bit keys with LDS histograms (11/11/10-bit digits), and
-// a top-p threshold search over the same digits with fixed-point (2^-40)
-// masses, so every sum is exact integer arithmetic and independent of the
-// order of atomics.  The row is re-read per pass from cache.
+// One 1024-thread workgroup per row that the single-read fast path leaves
+// open:
+//   probe rows: top-p-only rows whose boundary lies below the listed logits.
+//     The probe pass has summed, per probe token v (the row's best Gumbel
+//     keys, best first), the temperature-scaled mass of the logits strictly
+//     above l_v.  v is kept by top-p iff that mass is below p times the
+//     total, so the first kept probe is the Gumbel-max winner over the kept
+//     set.  If no probe is kept, the row is computed exactly.
+//   exact rows (candidate overflow, top_k > 1024, heavy ties): the whole row
+//     from scratch with radix selection on order-preserving keys (11/11/10-bit
+//     digits in LDS) and a top-p threshold search over the same digits with
+//     fixed-point (2^-40) masses, so every sum is exact integer arithmetic.
+//     With TS_SAMPLER_EXACT=1 every row takes this route.
 #include <float.h>
-#include <math.h>
 
-#include "device_common.hpp"
-#include "ts_internal.hpp"
+#include "sampler_common.hpp"
 
 namespace ts {
 namespace {
 
-constexpr int XT = 1024;          // threads per row
-constexpr int XW = XT / kWave;    // waves per row
-constexpr int RBINS = 2048;       // radix bins (11-bit digit)
-constexpr float kMassScale = 1099511627776.0f;  // 2^40: fixed-point unit of a weight
+constexpr int XT = 1024;        // threads per row
+constexpr int XW = XT / kWave;  // waves per row
+constexpr int RBINS = 2048;     // radix bins (11-bit digit)
 
 struct ExactSmem {
   uint32_t cnt[RBINS];
   unsigned long long mass[RBINS];
-  float rf[XW];
+  uint32_t list_key[TS_MAX_LOGPROBS];
+  int list_id[TS_MAX_LOGPROBS];
+};
+
+struct FallbackSmem {
+  ExactSmem ex;
+  float rf_[XW];
   int ri[XW];
   uint32_t ru[XW];
   unsigned long long rq[XW];
-  uint32_t list_key[TS_MAX_LOGPROBS];
-  int list_id[TS_MAX_LOGPROBS];
   uint32_t sel_digit;
   uint32_t sel_above;
   unsigned long long sel_above_q;
@@ -52,36 +46,13 @@ struct ExactSmem {
 __device__ __forceinline__ int digit_shift(int rd) { return rd == 0 ? 21 : (rd == 1 ? 10 : 0); }
 __device__ __forceinline__ int digit_width(int rd) { return rd == 2 ? 10 : 11; }
 
-__device__ __forceinline__ unsigned long long fixed_mass(float w) {
-  return static_cast<unsigned long long>(w * kMassScale);  // w in [0, 1]
-}
-
-// Pick the digit whose bin holds the `rem`-th largest element, counting from
-// the top bin down; sets sel_digit and sel_above (count strictly above it).
-__device__ void select_digit_count(ExactSmem& sh, int nb, uint32_t rem) {
-  const int t = threadIdx.x;
-  const int b0 = nb - 1 - 2 * t, b1 = nb - 2 - 2 * t;
-  const uint32_t h0 = b0 >= 0 ? sh.cnt[b0] : 0u;
-  const uint32_t h1 = b1 >= 0 ? sh.cnt[b1] : 0u;
-  uint32_t total;
-  const uint32_t ex = block_exclusive_scan<XT, uint32_t>(h0 + h1, sh.ru, total);
-  if (b0 >= 0 && ex < rem && rem <= ex + h0) {
-    sh.sel_digit = static_cast<uint32_t>(b0);
-    sh.sel_above = ex;
-  } else if (b1 >= 0 && ex + h0 < rem && rem <= ex + h0 + h1) {
-    sh.sel_digit = static_cast<uint32_t>(b1);
-    sh.sel_above = ex + h0;
-  }
-  __syncthreads();
-}
-
 // Same search over fixed-point masses: the bin where the mass counted from the
 // top first reaches `rem`.
-__device__ void select_digit_mass(ExactSmem& sh, int nb, unsigned long long rem) {
+__device__ void select_digit_mass(FallbackSmem& sh, int nb, unsigned long long rem) {
   const int t = threadIdx.x;
   const int b0 = nb - 1 - 2 * t, b1 = nb - 2 - 2 * t;
-  const unsigned long long h0 = b0 >= 0 ? sh.mass[b0] : 0ull;
-  const unsigned long long h1 = b1 >= 0 ? sh.mass[b1] : 0ull;
+  const unsigned long long h0 = b0 >= 0 ? sh.ex.mass[b0] : 0ull;
+  const unsigned long long h1 = b1 >= 0 ? sh.ex.mass[b1] : 0ull;
   unsigned long long total;
   const unsigned long long ex = block_exclusive_scan<XT, unsigned long long>(h0 + h1, sh.rq, total);
   if (b0 >= 0 && ex < rem && rem <= ex + h0) {
@@ -96,22 +67,22 @@ __device__ void select_digit_mass(ExactSmem& sh, int nb, unsigned long long rem)
 
 // The k-th largest key of the row (1 <= k <= V): K with
 // #(key > K) < k <= #(key >= K).  Returns K, gt = #(key > K), eq = #(key == K).
-__device__ void radix_kth(const float* __restrict__ row, int V, uint32_t k, ExactSmem& sh,
+__device__ void radix_kth(const float* __restrict__ row, int V, uint32_t k, FallbackSmem& sh,
                           uint32_t& K, uint32_t& gt, uint32_t& eq) {
   uint32_t prefix = 0, pmask = 0, rem = k, above = 0, last = 0;
   for (int rd = 0; rd < 3; ++rd) {
     const int shift = digit_shift(rd), width = digit_width(rd);
     const uint32_t dmask = (1u << width) - 1u;
-    for (int b = threadIdx.x; b < RBINS; b += XT) sh.cnt[b] = 0u;
+    for (int b = threadIdx.x; b < RBINS; b += XT) sh.ex.cnt[b] = 0u;
     __syncthreads();
     for (int i = threadIdx.x; i < V; i += XT) {
       const uint32_t key = order_key(row[i]);
-      if ((key & pmask) == prefix) atomicAdd(&sh.cnt[(key >> shift) & dmask], 1u);
+      if ((key & pmask) == prefix) atomicAdd(&sh.ex.cnt[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
-    select_digit_count(sh, 1 << width, rem);
+    select_digit_top<XT, 2>(sh.ex.cnt, 1 << width, rem, sh.ru, &sh.sel_digit, &sh.sel_above);
     const uint32_t d = sh.sel_digit, a = sh.sel_above;
-    last = sh.cnt[d];
+    last = sh.ex.cnt[d];
     __syncthreads();
     rem -= a;
     above += a;
@@ -126,19 +97,19 @@ __device__ void radix_kth(const float* __restrict__ row, int V, uint32_t k, Exac
 // The largest key K such that the fixed-point mass of {key >= max(K, floor)}
 // reaches `target` (1 <= target <= mass of {key >= floor}).
 __device__ uint32_t radix_mass(const float* __restrict__ row, int V, uint32_t floor_key, float m,
-                               float inv_t, unsigned long long target, ExactSmem& sh) {
+                               float inv_t, unsigned long long target, FallbackSmem& sh) {
   uint32_t prefix = 0, pmask = 0;
   unsigned long long rem = target;
   for (int rd = 0; rd < 3; ++rd) {
     const int shift = digit_shift(rd), width = digit_width(rd);
     const uint32_t dmask = (1u << width) - 1u;
-    for (int b = threadIdx.x; b < RBINS; b += XT) sh.mass[b] = 0ull;
+    for (int b = threadIdx.x; b < RBINS; b += XT) sh.ex.mass[b] = 0ull;
     __syncthreads();
     for (int i = threadIdx.x; i < V; i += XT) {
       const float l = row[i];
       const uint32_t key = order_key(l);
       if (key >= floor_key && (key & pmask) == prefix)
-        atomicAdd(&sh.mass[(key >> shift) & dmask], fixed_mass(expf((l - m) * inv_t)));
+        atomicAdd(&sh.ex.mass[(key >> shift) & dmask], fixed_mass(expf((l - m) * inv_t)));
     }
     __syncthreads();
     select_digit_mass(sh, 1 << width, rem);
@@ -165,22 +136,8 @@ __device__ void write_bad_row(const SamplerArgs& a, int r, int status) {
   }
 }
 
-__device__ bool params_ok(const ts_row_params& p, int max_logprobs) {
-  if (!(p.temperature >= 0.0f) || isinf(p.temperature)) return false;
-  if (p.top_k < 0) return false;
-  if (!(p.top_p > 0.0f && p.top_p <= 1.0f)) return false;
-  if (p.n_logprobs < 0 || p.n_logprobs > max_logprobs) return false;
-  return true;
-}
-
-// One workgroup samples one row.  `row_list` (optional) maps blockIdx.x to a
-// local row; `row_count` (optional, device) bounds the list.
-__global__ __launch_bounds__(XT) void sampler_exact_kernel(SamplerArgs a, const int* row_list,
-                                                           const int* row_count) {
-  __shared__ ExactSmem sh;
-  int r = blockIdx.x;
-  if (row_count != nullptr && r >= *row_count) return;
-  if (row_list != nullptr) r = row_list[r];
+// The whole row from scratch.
+__device__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
   const int tid = threadIdx.x;
   const int V = a.vocab;
   const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
@@ -216,7 +173,7 @@ __global__ __launch_bounds__(XT) void sampler_exact_kernel(SamplerArgs a, const 
   // Pass 2: log-sum-exp of the raw logits (fixed per-thread order, fixed tree).
   float s = 0.0f;
   for (int i = tid; i < V; i += XT) s += expf(row[i] - m);
-  s = block_sum<XT, float>(s, sh.rf);
+  s = block_sum<XT, float>(s, sh.rf_);
   const float lse = m + logf(s);
 
   // Top-N log-probabilities.
@@ -236,8 +193,8 @@ __global__ __launch_bounds__(XT) void sampler_exact_kernel(SamplerArgs a, const 
       const uint32_t key = order_key(row[i]);
       if (key > kn || (eq == need && key == kn)) {
         const int slot = atomicAdd(&sh.list_n, 1);
-        sh.list_key[slot] = key;
-        sh.list_id[slot] = i;
+        sh.ex.list_key[slot] = key;
+        sh.ex.list_id[slot] = i;
       }
     }
     if (eq != need) {
@@ -249,18 +206,19 @@ __global__ __launch_bounds__(XT) void sampler_exact_kernel(SamplerArgs a, const 
         const uint32_t ex = block_exclusive_scan<XT, uint32_t>(f ? 1u : 0u, sh.ru, tot);
         if (f && taken + ex < need) {
           const int slot = atomicAdd(&sh.list_n, 1);
-          sh.list_key[slot] = kn;
-          sh.list_id[slot] = i;
+          sh.ex.list_key[slot] = kn;
+          sh.ex.list_id[slot] = i;
         }
         taken += tot;
       }
     }
     __syncthreads();
     for (int t = tid; t < n; t += XT) {
-      const uint32_t kt = sh.list_key[t];
-      const int it = sh.list_id[t];
+      const uint32_t kt = sh.ex.list_key[t];
+      const int it = sh.ex.list_id[t];
       int rank = 0;
-      for (int j = 0; j < n; ++j) rank += better_u(sh.list_key[j], sh.list_id[j], kt, it) ? 1 : 0;
+      for (int j = 0; j < n; ++j)
+        rank += better_u(sh.ex.list_key[j], sh.ex.list_id[j], kt, it) ? 1 : 0;
       a.topn_ids[obase + rank] = it;
       a.topn_logprobs[obase + rank] = key_to_float(kt) - lse;
     }
@@ -286,7 +244,7 @@ __global__ __launch_bounds__(XT) void sampler_exact_kernel(SamplerArgs a, const 
         if (order_key(l) >= kk) z += fixed_mass(expf((l - m) * inv_t));
       }
       z = block_sum<XT, unsigned long long>(z, sh.rq);
-      double tgt = ceil(static_cast<double>(p.top_p) * static_cast<double>(z));
+      const double tgt = ceil(static_cast<double>(p.top_p) * static_cast<double>(z));
       unsigned long long target = static_cast<unsigned long long>(tgt);
       if (target < 1ull) target = 1ull;
       if (target > z) target = z;
@@ -321,7 +279,7 @@ __global__ __launch_bounds__(XT) void sampler_exact_kernel(SamplerArgs a, const 
         }
       }
     }
-    block_best<XT>(gk, gi, sh.rf, sh.ri);
+    block_best<XT>(gk, gi, sh.rf_, sh.ri);
     token = gi;
   }
   if (tid == 0) {
@@ -331,22 +289,65 @@ __global__ __launch_bounds__(XT) void sampler_exact_kernel(SamplerArgs a, const 
   }
 }
 
-}  // namespace
-
-size_t sampler_workspace_size(int64_t rows, int64_t vocab, int max_logprobs) {
-  (void)rows;
-  (void)vocab;
-  (void)max_logprobs;
-  return 256;
+// Probe row: the first probe (best Gumbel key first) whose mass-above is below
+// p times the total is the winner.
+__device__ void finish_probe_row(const SamplerArgs& a, const FastLayout& lay, const uint8_t* ws,
+                                 int li, int r, FallbackSmem& sh) {
+  const ProbeRec pr = reinterpret_cast<const ProbeRec*>(ws + lay.off_prec)[r];
+  const ts_row_params p = a.params[r];
+  const double* part = reinterpret_cast<const double*>(ws + lay.off_part) +
+                       static_cast<size_t>(li) * lay.S * kProbes;
+  if (threadIdx.x == 0) {
+    const double target = static_cast<double>(p.top_p) * pr.z;
+    int win = -1;
+    for (int i = 0; i < pr.npts && win < 0; ++i) {
+      double above = 0.0;
+      for (int c = 0; c < lay.S; ++c) above += part[static_cast<size_t>(c) * kProbes + i];
+      if (above < target) win = pr.id[i];
+    }
+    sh.list_n = win;
+  }
+  __syncthreads();
+  const int win = sh.list_n;
+  __syncthreads();
+  if (win < 0) {
+    exact_row(a, r, sh);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
+    a.token_ids[r] = win;
+    if (a.token_logprobs) a.token_logprobs[r] = row[win] - pr.lse;
+    if (a.row_status) a.row_status[r] = TS_ROW_OK;
+  }
 }
 
-hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  if (a.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(sampler_exact_kernel, dim3(a.rows), dim3(XT), 0, stream, a,
-                     static_cast<const int*>(nullptr), static_cast<const int*>(nullptr));
+// Workgroup b finishes probe row b, then exact row b - (probe rows); with
+// all_rows every row is computed exactly.
+__global__ __launch_bounds__(XT) void sampler_finish_kernel(SamplerArgs a, FastLayout lay,
+                                                            uint8_t* ws, int all_rows) {
+  __shared__ FallbackSmem sh;
+  const int b = blockIdx.x;
+  if (all_rows) {
+    exact_row(a, b, sh);
+    return;
+  }
+  const int* ctr = reinterpret_cast<const int*>(ws + lay.off_ctr);
+  const int n_exact = ctr[0], n_probe = ctr[1];
+  if (b < n_probe) {
+    finish_probe_row(a, lay, ws, b, reinterpret_cast<const int*>(ws + lay.off_probe)[b], sh);
+  } else if (b - n_probe < n_exact) {
+    exact_row(a, reinterpret_cast<const int*>(ws + lay.off_exact)[b - n_probe], sh);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sampler_finish(const SamplerArgs& a, const FastLayout* lay, uint8_t* ws,
+                                 hipStream_t stream) {
+  const FastLayout l = lay ? *lay : FastLayout{};
+  hipLaunchKernelGGL(sampler_finish_kernel, dim3(a.rows), dim3(XT), 0, stream, a, l, ws,
+                     lay ? 0 : 1);
   return hipGetLastError();
 }
 

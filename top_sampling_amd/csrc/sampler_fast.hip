@@ -1,0 +1,871 @@
+// Single-read sampler for batch-sharded sampling on gfx950.
+//
+// The sampler runs on the rank's slice of requests: batch x (speculative
+// tokens + 1) rows of full-vocabulary fp32 logits (page "Qwen4Exp
+// batch-sharded sampling: inside vLLM PR #61018", section "What
+// batch-sharded sampling is, in one paragraph").  It is HBM-bound: every
+// logit is read from HBM once, except the rows of the probe pass below.
+//
+// A  chunk pass   one 256-thread workgroup per (row, chunk of <= 16384
+//                 logits), the chunk held in registers (16 float4 per thread,
+//                 two workgroups per CU).  Per chunk:
+//                   - max and sum exp(l - max) (hardware exp2); a NaN or +inf
+//                     shows up as a NaN sum;
+//                   - a logit candidate list holding at least the chunk's M
+//                     largest, M = max(n_logprobs, top_k) (64 for top-p-only
+//                     rows): the threshold is the M-th largest per-thread
+//                     maximum (or of the per-thread top two), found by LDS
+//                     radix selection over 256 or 512 values; M of the
+//                     chunk's logits are at or above it by construction;
+//                   - full-vocabulary rows: the chunk's best Gumbel key;
+//                   - top-p-only rows: every token whose Gumbel key is at or
+//                     above the 8th largest per-thread best key (a complete
+//                     list above that floor), and the temperature-scaled mass.
+// B  merge        one 256-thread workgroup per row: log-sum-exp; the union of
+//                 logit candidates above the highest chunk threshold (radix
+//                 selection trims it to the row's M largest when needed) is
+//                 exactly the row's logits above it, sorted in LDS (bitonic).
+//                 Top-N, greedy, top-k, top-p and Gumbel-max are exact on that
+//                 prefix.  A top-p-only row whose boundary lies below it takes
+//                 the row's best Gumbel keys as probes.
+// P  probe        chunk-parallel re-read of probe rows only: the mass of the
+//                 logits strictly above each probe's logit.  Token v is kept
+//                 by top-p iff that mass is below p times the total, so the
+//                 first probe (by key) that is kept is the Gumbel-max winner.
+// X  finish       (sampler_exact.hip) settles probe rows; rows that no fast
+//                 route settles (candidate overflow, top_k > 1024, no kept
+//                 probe) run the exact per-row kernel.
+#include <stdlib.h>
+
+#include "sampler_common.hpp"
+
+namespace ts {
+namespace {
+
+constexpr int AT = kChunkThreads;
+constexpr int AW = AT / kWave;
+constexpr int AV = kChunkVec;
+constexpr int RB = 2048;
+constexpr int BT = 1024;
+constexpr int BW = BT / kWave;
+constexpr int PT = 256;
+constexpr int PW = PT / kWave;
+constexpr int PER = kListMax / BT;  // list entries per merge thread
+
+__device__ __forceinline__ float lane(const float4& f, int q) {
+  return q == 0 ? f.x : (q == 1 ? f.y : (q == 2 ? f.z : f.w));
+}
+
+// Threshold below which every logit qualifies: keys at or below the key of
+// -inf map to -inf (all lower keys are NaN patterns).
+__device__ __forceinline__ float key_floor_value(uint32_t kt) {
+  return kt <= 0x007fffffu ? -INFINITY : key_to_float(kt);
+}
+
+template <int NT>
+__device__ void write_bad(const SamplerArgs& a, int r, int status) {
+  const float qnan = __builtin_nanf("");
+  for (int j = threadIdx.x; j < a.max_logprobs; j += NT) {
+    a.topn_ids[static_cast<int64_t>(r) * a.max_logprobs + j] = -1;
+    a.topn_logprobs[static_cast<int64_t>(r) * a.max_logprobs + j] = qnan;
+  }
+  if (threadIdx.x == 0) {
+    a.token_ids[r] = -1;
+    if (a.token_logprobs) a.token_logprobs[r] = qnan;
+    if (a.row_status) a.row_status[r] = status;
+  }
+}
+
+// The M-th largest of nk keys in LDS (1 <= M <= nk), by radix selection
+// (11/11/10-bit digits).
+template <int NT>
+__device__ uint32_t lds_kth_largest(const uint32_t* keys, int nk, uint32_t M, uint32_t* hist,
+                                    uint32_t* scratch, uint32_t* sel_d, uint32_t* sel_above) {
+  uint32_t prefix = 0u, pmask = 0u, rem = M;
+  for (int rd = 0; rd < 3; ++rd) {
+    const int shift = rd == 0 ? 21 : (rd == 1 ? 10 : 0);
+    const int width = rd == 2 ? 10 : 11;
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int b = threadIdx.x; b < RB; b += NT) hist[b] = 0u;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nk; i += NT) {
+      const uint32_t k = keys[i];
+      if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    select_digit_top<NT, RB / NT>(hist, 1 << width, rem, scratch, sel_d, sel_above);
+    const uint32_t d = *sel_d, ab = *sel_above;
+    __syncthreads();
+    rem -= ab;
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+  }
+  return prefix;
+}
+
+// Visit the valid logits (l, id) of this thread's 16 float4.
+#define FOR_VALID(BODY)                                       \
+  _Pragma("unroll") for (int j = 0; j < AV; ++j) {            \
+    const int e = 4 * (j * AT + tid);                         \
+    if (e + 3 < n) {                                          \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {         \
+        const float l = lane(v[j], q);                        \
+        const int id = c0 + e + q;                            \
+        (void)id;                                             \
+        BODY                                                  \
+      }                                                       \
+    } else if (e < n) {                                       \
+      _Pragma("unroll") for (int q = 0; q < 4; ++q) {         \
+        if (e + q < n) {                                      \
+          const float l = lane(v[j], q);                      \
+          const int id = c0 + e + q;                          \
+          (void)id;                                           \
+          BODY                                                \
+        }                                                     \
+      }                                                       \
+    }                                                         \
+  }
+
+// ------------------------------------------------------------------ A: chunks
+struct ChunkSmem {
+  uint32_t hist[RB];
+  int klist[kKeyCap];
+  float wthr[AW];
+  float rm[AW], rs[AW], rt[AW];
+  int rb[AW];
+  float rf[AW];
+  int ri[AW];
+  uint32_t ru[AW];
+  uint32_t sel_d, sel_above;
+  int ncand, nkey;
+};
+
+// (m, s, t): a maximum with sum exp(l - m) and sum exp((l - m) / T); merging
+// two rescales both sums to the larger maximum.
+__device__ __forceinline__ void merge_stats(float& m, float& s, float& t, float m2, float s2,
+                                            float t2, float inv_t) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;  // both empty
+  s = s * fast_exp(m - mm) + s2 * fast_exp(m2 - mm);
+  t = t * fast_exp((m - mm) * inv_t) + t2 * fast_exp((m2 - mm) * inv_t);
+  m = mm;
+}
+
+// The q-th largest (1-based, q <= 64) per-thread value of this wave.
+__device__ __forceinline__ float wave_qth(float x, int q) {
+  return __shfl(wave_sort_desc(x), q - 1, kWave);
+}
+
+// The q-th largest (q <= 256) of the wave's per-thread top-4 values.
+__device__ __forceinline__ float wave_qth4(const float (&t)[4], int q) {
+  float v[4] = {t[0], t[1], t[2], t[3]};
+  wave_sort4_desc(v);
+  const int idx = q - 1, i = idx & 3;
+  const float mine = i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
+  return __shfl(mine, idx >> 2, kWave);
+}
+
+__global__ __launch_bounds__(AT) void chunk_pass_kernel(SamplerArgs a, FastLayout lay,
+                                                        uint8_t* __restrict__ ws, int vec) {
+  __shared__ ChunkSmem sh;
+  const int S = lay.S;
+  const int bid = blockIdx.x;
+  const int r = bid / S, c = bid - r * S;
+  const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
+  if (bid == 0 && tid < 2) reinterpret_cast<int*>(ws + lay.off_ctr)[tid] = 0;
+  const ts_row_params p = a.params[r];
+  const int V = a.vocab;
+  const int kind = row_kind(p, V, a.max_logprobs);
+  if (kind == KIND_BAD || kind == KIND_EXACT) return;
+  ChunkRec* rec = reinterpret_cast<ChunkRec*>(ws + lay.off_chunk) + bid;
+  const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
+  const int c0 = c * lay.L;
+  const int n = min(lay.L, V - c0);
+  const bool topp = kind == KIND_TOPP;
+  const float inv_t = kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature;
+
+  // The chunk: 16 float4 per thread, logit e = 4 * (j * AT + tid) + q.
+  float4 v[AV];
+#pragma unroll
+  for (int j = 0; j < AV; ++j) {
+    const int e = 4 * (j * AT + tid);
+    if (vec && e + 3 < n) {
+      v[j] = *reinterpret_cast<const float4*>(row + c0 + e);
+    } else {
+      v[j].x = e + 0 < n ? row[c0 + e + 0] : -INFINITY;
+      v[j].y = e + 1 < n ? row[c0 + e + 1] : -INFINITY;
+      v[j].z = e + 2 < n ? row[c0 + e + 2] : -INFINITY;
+      v[j].w = e + 3 < n ? row[c0 + e + 3] : -INFINITY;
+    }
+  }
+
+  // Per-thread largest value (or largest four when M > 256).  Out-of-chunk
+  // slots hold -inf, which changes no maximum and adds no mass.
+  const int M = cand_target(kind, p, V);
+  const bool four = M > 256;
+  float t[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  if (four) {
+#pragma unroll
+    for (int j = 0; j < AV; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float x = lane(v[j], q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float hi = fmaxf(t[i], x);
+          x = fminf(t[i], x);
+          t[i] = hi;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < AV; ++j)
+      t[0] = fmaxf(fmaxf(t[0], fmaxf(v[j].x, v[j].y)), fmaxf(v[j].z, v[j].w));
+  }
+
+  // Thread statistics relative to the thread maximum, then one block
+  // reduction of (max, sum exp, sum exp/T).  A NaN logit makes the sum NaN;
+  // +inf makes the maximum infinite; a thread holding only -inf and NaN
+  // scans for NaN.
+  float lm = t[0], ls = 0.0f, lt = 0.0f;
+  int flag = lm == INFINITY ? 1 : 0;
+  if (lm > -INFINITY && lm < INFINITY) {
+    const float sc = inv_t * kLog2e;
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float d = lane(v[j], q) - lm;
+        ls += fast_exp(d);
+        if (topp) lt += __builtin_amdgcn_exp2f(d * sc);
+      }
+    }
+  } else if (lm == -INFINITY) {
+#pragma unroll
+    for (int j = 0; j < AV; ++j)
+      flag |= (isnan(v[j].x) || isnan(v[j].y) || isnan(v[j].z) || isnan(v[j].w)) ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(lm, o, kWave), s2 = __shfl_xor(ls, o, kWave),
+                t2 = __shfl_xor(lt, o, kWave);
+    merge_stats(lm, ls, lt, m2, s2, t2, inv_t);
+  }
+  flag = __any(flag) ? 1 : 0;
+  if (lane_id == 0) {
+    sh.rm[wave] = lm;
+    sh.rs[wave] = ls;
+    sh.rt[wave] = lt;
+    sh.rb[wave] = flag;
+  }
+  __syncthreads();
+  float cmax = sh.rm[0], s = sh.rs[0], tmass = sh.rt[0];
+  int bad = sh.rb[0];
+#pragma unroll
+  for (int w = 1; w < AW; ++w) {
+    merge_stats(cmax, s, tmass, sh.rm[w], sh.rs[w], sh.rt[w], inv_t);
+    bad |= sh.rb[w];
+  }
+  if (bad || isnan(s) || cmax == INFINITY) {
+    if (tid == 0) rec->status = 1;
+    return;
+  }
+  if (!topp) tmass = 0.0f;
+
+  // Logit candidate threshold tf: every wave holds ceil(M/4) per-thread
+  // values >= its own q-th largest, so at least M logits are >= the smallest
+  // of the four.  The list takes every logit >= tf.
+  float tf = -INFINITY;
+  if (M < n) {
+    const int q = (M + AW - 1) / AW;
+    const float tw = four ? wave_qth4(t, q) : wave_qth(t[0], q);
+    if (lane_id == 0) sh.wthr[wave] = tw;
+  }
+  if (tid == 0) {
+    sh.ncand = 0;
+    sh.nkey = 0;
+  }
+  __syncthreads();
+  if (M < n) {
+    tf = sh.wthr[0];
+#pragma unroll
+    for (int w = 1; w < AW; ++w) tf = fminf(tf, sh.wthr[w]);
+  }
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws + lay.off_cand) +
+                             static_cast<size_t>(bid) * kCandCap;
+  FOR_VALID(if (l >= tf) {
+    const int slot = atomicAdd(&sh.ncand, 1);
+    if (slot < kCandCap) cand[slot] = pack_cand(order_key(l), id);
+  })
+  __syncthreads();
+  uint32_t kt = order_key(tf);
+  bool ovf = sh.ncand > kCandCap;
+  if (ovf) {
+    // Too many ties or a flat chunk: radix selection over every logit.
+    uint32_t prefix = 0u, pmask = 0u, rem = static_cast<uint32_t>(M), above = 0u, cnt = 0u;
+    for (int rd = 0; rd < 3; ++rd) {
+      const int shift = rd == 0 ? 21 : (rd == 1 ? 10 : 0);
+      const int width = rd == 2 ? 10 : 11;
+      const uint32_t dmask = (1u << width) - 1u;
+      for (int b = tid; b < RB; b += AT) sh.hist[b] = 0u;
+      __syncthreads();
+      FOR_VALID({
+        const uint32_t key = order_key(l);
+        if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+      })
+      __syncthreads();
+      select_digit_top<AT, RB / AT>(sh.hist, 1 << width, rem, sh.ru, &sh.sel_d, &sh.sel_above);
+      const uint32_t d = sh.sel_d, ab = sh.sel_above, hd = sh.hist[d];
+      __syncthreads();
+      above += ab;
+      rem -= ab;
+      prefix |= d << shift;
+      pmask |= dmask << shift;
+      cnt = above + hd;
+      if (cnt <= static_cast<uint32_t>(kCandCap)) break;
+    }
+    kt = prefix;
+    ovf = cnt > static_cast<uint32_t>(kCandCap);
+    if (tid == 0) sh.ncand = 0;
+    __syncthreads();
+    if (!ovf) {
+      FOR_VALID(if (order_key(l) >= kt) {
+        const int slot = atomicAdd(&sh.ncand, 1);
+        cand[slot] = pack_cand(order_key(l), id);
+      })
+    }
+    __syncthreads();
+  }
+
+  // Gumbel keys relative to the chunk maximum: x = (l - cmax) / T, key = x + g.
+  float kfloor = INFINITY;
+  bool key_ovf = false;
+  if (kind == KIND_FULL || topp) {
+    const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
+    // Full rows: the chunk maximum's key is at least the smallest Gumbel
+    // value, so no token whose key cannot reach it needs its noise.
+    const float bar0 = topp ? -INFINITY : kMinGumbel;
+    float k1 = -INFINITY, k2 = -INFINITY;
+    int i1 = 0x7fffffff, i2 = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const int e = 4 * (j * AT + tid);
+      if (e >= n) continue;
+      float x[4];
+      float xm = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[q] = e + q < n ? (lane(v[j], q) - cmax) * inv_t : -INFINITY;
+        xm = fmaxf(xm, x[q]);
+      }
+      // A key is x + g with g below kGumbelMax: skip the noise when no token
+      // of the four can enter this thread's best one (or two).
+      if (xm + kGumbelMax < fmaxf(bar0, topp ? k2 : k1)) continue;
+      const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (x[q] == -INFINITY) continue;
+        const float key = x[q] + gumbel_from_word(w.v[q]);
+        const int id = c0 + e + q;
+        if (better(key, id, k1, i1)) {
+          k2 = k1;
+          i2 = i1;
+          k1 = key;
+          i1 = id;
+        } else if (topp && better(key, id, k2, i2)) {
+          k2 = key;
+          i2 = id;
+        }
+      }
+    }
+    int* klist_out = reinterpret_cast<int*>(ws + lay.off_key) + static_cast<size_t>(bid) * kKeyCap;
+    if (!topp) {
+      block_best<AT>(k1, i1, sh.rf, sh.ri);
+      if (tid == 0 && i1 != 0x7fffffff) {
+        klist_out[0] = i1;
+        sh.nkey = 1;
+      }
+      kfloor = k1;
+      __syncthreads();
+    } else {
+      // Floor: each wave's second-best per-thread key, the smallest of the
+      // four; at least kKeyTarget threads have a best key at or above it.
+      // Every token at or above the floor is listed: a thread's best if it
+      // qualifies, and all of a thread's qualifying tokens when its second
+      // best qualifies too (the thread recomputes its keys).
+      const float tw = wave_qth(k1, kKeyTarget / AW);
+      if (lane_id == 0) sh.wthr[wave] = tw;
+      __syncthreads();
+      kfloor = sh.wthr[0];
+#pragma unroll
+      for (int w = 1; w < AW; ++w) kfloor = fminf(kfloor, sh.wthr[w]);
+      if (k2 > -INFINITY && k2 >= kfloor) {
+#pragma unroll
+        for (int j = 0; j < AV; ++j) {
+          const int e = 4 * (j * AT + tid);
+          if (e >= n) continue;
+          const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (e + q >= n) continue;
+            const float x = (lane(v[j], q) - cmax) * inv_t;
+            if (x == -INFINITY) continue;
+            const float key = x + gumbel_from_word(w.v[q]);
+            if (key >= kfloor) {
+              const int slot = atomicAdd(&sh.nkey, 1);
+              if (slot < kKeyCap) sh.klist[slot] = c0 + e + q;
+            }
+          }
+        }
+      } else if (k1 > -INFINITY && k1 >= kfloor) {
+        const int slot = atomicAdd(&sh.nkey, 1);
+        if (slot < kKeyCap) sh.klist[slot] = i1;
+      }
+      __syncthreads();
+      key_ovf = sh.nkey > kKeyCap;
+      if (!key_ovf && tid < sh.nkey) klist_out[tid] = sh.klist[tid];
+    }
+  }
+  if (tid == 0) {
+    ChunkRec o;
+    o.cmax = cmax;
+    o.sumexp = s;
+    o.tmass = tmass;
+    o.kt = kt;
+    o.ncand = ovf ? 0 : sh.ncand;
+    o.status = (ovf || key_ovf) ? 2 : 0;
+    o.nkey = key_ovf ? 0 : sh.nkey;
+    o.kfloor = kfloor;
+    *rec = o;
+  }
+}
+
+// ------------------------------------------------------------------- B: merge
+constexpr int kUnionMax = 1 << 20;  // candidates a merge workgroup walks
+
+struct MergeSmem {
+  unsigned long long list[kListMax];
+  uint32_t hist[RB];
+  ChunkRec recs[kMaxChunks];
+  int pos[kMaxChunks + 1];
+  double dscan[BW];
+  float rf[BW];
+  int ri[BW];
+  uint32_t ru[BW];
+  uint32_t sel_d, sel_above, rmax;
+  int nlist, jstar, status, total;
+  float m, lse, kmin;
+  uint32_t floor_key;
+  double z;
+};
+
+__device__ __forceinline__ void push_row(int* ctr, int* list, int r) { list[atomicAdd(ctr, 1)] = r; }
+
+// force: bit 0 sends every top-p-only row through the probe pass (a
+// diagnostic route; the result is the same).
+__global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay,
+                                                   uint8_t* __restrict__ ws, int force) {
+  __shared__ MergeSmem sh;
+  const int r = blockIdx.x, tid = threadIdx.x, S = lay.S, V = a.vocab;
+  const ts_row_params p = a.params[r];
+  const int kind = row_kind(p, V, a.max_logprobs);
+  int* ctr = reinterpret_cast<int*>(ws + lay.off_ctr);
+  int* exact_list = reinterpret_cast<int*>(ws + lay.off_exact);
+  int* probe_list = reinterpret_cast<int*>(ws + lay.off_probe);
+  const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
+  if (kind == KIND_BAD) {
+    write_bad<BT>(a, r, TS_ROW_BAD_PARAMS);
+    return;
+  }
+  if (kind == KIND_EXACT) {
+    if (tid == 0) push_row(&ctr[0], exact_list, r);
+    return;
+  }
+  const ChunkRec* recs = reinterpret_cast<const ChunkRec*>(ws + lay.off_chunk) +
+                         static_cast<size_t>(r) * S;
+  for (int c = tid; c < S; c += BT) sh.recs[c] = recs[c];
+  __syncthreads();
+  const float inv_t = kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature;
+  if (tid == 0) {
+    int st = 0;
+    for (int c = 0; c < S; ++c)
+      if (sh.recs[c].status == 1) st = 1;
+    if (st == 0)
+      for (int c = 0; c < S; ++c)
+        if (sh.recs[c].status == 2) st = 2;
+    float m = -INFINITY;
+    uint32_t fl = 0u;
+    int tot = 0;
+    if (st != 1) {
+      for (int c = 0; c < S; ++c) {
+        m = fmaxf(m, sh.recs[c].cmax);
+        if (sh.recs[c].kt > fl) fl = sh.recs[c].kt;
+        sh.pos[c] = tot;
+        tot += sh.recs[c].ncand;
+      }
+    }
+    sh.pos[S] = tot;
+    float se = 0.0f;
+    double z = 0.0;
+    float kmin = -INFINITY;
+    if (m > -INFINITY) {
+      for (int c = 0; c < S; ++c) {
+        if (!(sh.recs[c].cmax > -INFINITY)) continue;
+        se += sh.recs[c].sumexp * fast_exp(sh.recs[c].cmax - m);
+        if (kind == KIND_TOPP) {
+          const float shift = (sh.recs[c].cmax - m) * inv_t;
+          z += static_cast<double>(sh.recs[c].tmass) *
+               static_cast<double>(__builtin_amdgcn_exp2f(shift * kLog2e));
+          kmin = fmaxf(kmin, sh.recs[c].kfloor + shift);
+        }
+      }
+    }
+    sh.status = st;
+    sh.m = m;
+    sh.floor_key = fl;
+    sh.total = tot;
+    sh.lse = m + logf(se);
+    sh.z = z;
+    sh.kmin = kmin + kKeyMargin;
+    sh.nlist = 0;
+    sh.rmax = 0u;
+  }
+  __syncthreads();
+  if (sh.status == 1 || !(sh.m > -INFINITY)) {
+    write_bad<BT>(a, r, TS_ROW_BAD_LOGITS);
+    return;
+  }
+  if (sh.status == 2 || sh.total > kUnionMax) {
+    if (tid == 0) push_row(&ctr[0], exact_list, r);
+    return;
+  }
+  const float m = sh.m, lse = sh.lse;
+  uint32_t floor_key = sh.floor_key;
+  const int total = sh.total;
+
+  // The union of the chunks' candidates above the floor holds the row's M
+  // largest logits (each chunk listed at least its own M largest).  Passes
+  // over it read global memory (L2-resident), four entries in flight per
+  // thread.
+  const unsigned long long* cand = reinterpret_cast<const unsigned long long*>(ws + lay.off_cand) +
+                                   static_cast<size_t>(r) * S * kCandCap;
+  auto cand_at = [&](int g) -> unsigned long long {
+    int lo = 0, hi = S - 1;  // chunk c with pos[c] <= g < pos[c + 1]
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sh.pos[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    return cand[static_cast<size_t>(lo) * kCandCap + (g - sh.pos[lo])];
+  };
+  if (total > kListMax) {
+    // Raise the floor to the row's M-th largest candidate: radix selection
+    // on the key offset above the floor, digits from its highest set bit.
+    uint32_t rmax = 0u;
+    int mine = 0;
+#pragma unroll 4
+    for (int g = tid; g < total; g += BT) {
+      const uint32_t key = cand_key(cand_at(g));
+      if (key >= floor_key) {
+        rmax = max(rmax, key - floor_key);
+        ++mine;
+      }
+    }
+    atomicMax(&sh.rmax, rmax);
+    const int U0 = block_sum<BT, int>(mine, sh.ri);
+    rmax = sh.rmax;
+    if (U0 > kListMax) {
+      const int M = cand_target(kind, p, V);
+      const int hb = rmax == 0u ? -1 : 31 - __builtin_clz(rmax);
+      uint32_t prefix = 0u, rem = static_cast<uint32_t>(M), above = 0u;
+      int lowbit = hb + 1;  // offset bits >= lowbit are resolved
+      while (lowbit > 0) {
+        const int width = lowbit < 11 ? lowbit : 11;
+        const int shift = lowbit - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        const uint32_t hi_pref = lowbit >= 32 ? 0u : (prefix >> lowbit);
+        for (int b = tid; b < RB; b += BT) sh.hist[b] = 0u;
+        __syncthreads();
+#pragma unroll 4
+        for (int g = tid; g < total; g += BT) {
+          const uint32_t key = cand_key(cand_at(g));
+          if (key < floor_key) continue;
+          const uint32_t off = key - floor_key;
+          if ((lowbit >= 32 ? 0u : (off >> lowbit)) == hi_pref)
+            atomicAdd(&sh.hist[(off >> shift) & dmask], 1u);
+        }
+        __syncthreads();
+        select_digit_top<BT, RB / BT>(sh.hist, 1 << width, rem, sh.ru, &sh.sel_d,
+                                      &sh.sel_above);
+        const uint32_t d = sh.sel_d, ab = sh.sel_above, hd = sh.hist[d];
+        __syncthreads();
+        above += ab;
+        rem -= ab;
+        prefix |= d << shift;
+        lowbit = shift;
+        if (above + hd <= static_cast<uint32_t>(kListMax)) break;
+      }
+      floor_key += prefix;
+    }
+  }
+#pragma unroll 4
+  for (int g = tid; g < total; g += BT) {
+    const unsigned long long x = cand_at(g);
+    if (cand_key(x) >= floor_key) {
+      const int slot = atomicAdd(&sh.nlist, 1);
+      if (slot < kListMax) sh.list[slot] = x;
+    }
+  }
+  __syncthreads();
+  const int U = sh.nlist;
+  if (U > kListMax) {
+    if (tid == 0) push_row(&ctr[0], exact_list, r);
+    return;
+  }
+  const int np2 = next_pow2(U > 0 ? U : 1);
+  for (int i = U + tid; i < np2; i += BT) sh.list[i] = 0ull;
+  __syncthreads();
+  bitonic_sort_desc<BT>(sh.list, np2);
+  // Top-N log-probabilities.
+  const int n_eff = p.n_logprobs < V ? p.n_logprobs : V;
+  const int64_t obase = static_cast<int64_t>(r) * a.max_logprobs;
+  for (int j = tid; j < a.max_logprobs; j += BT) {
+    if (j < n_eff) {
+      const unsigned long long e = sh.list[j];
+      a.topn_ids[obase + j] = cand_id(e);
+      a.topn_logprobs[obase + j] = key_to_float(cand_key(e)) - lse;
+    } else {
+      a.topn_ids[obase + j] = -1;
+      a.topn_logprobs[obase + j] = -INFINITY;
+    }
+  }
+
+  const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
+  int token = cand_id(sh.list[0]);  // greedy: the largest logit, lowest id
+  if (kind == KIND_FULL) {
+    const int* keys = reinterpret_cast<const int*>(ws + lay.off_key) +
+                      static_cast<size_t>(r) * S * kKeyCap;
+    float gk = -INFINITY;
+    int gi = 0x7fffffff;
+    for (int c = tid; c < S; c += BT) {
+      if (sh.recs[c].nkey < 1) continue;
+      const int id = keys[static_cast<size_t>(c) * kKeyCap];
+      const float key = gumbel_key(row[id], m, inv_t, p.seed, grow, id);
+      if (better(key, id, gk, gi)) {
+        gk = key;
+        gi = id;
+      }
+    }
+    block_best<BT>(gk, gi, sh.rf, sh.ri);
+    token = gi;
+  } else if (kind == KIND_TOPK || kind == KIND_TOPP) {
+    // Top-k set: the sorted prefix down to the k-th largest (ties kept).
+    int nK = U;
+    if (kind == KIND_TOPK) {
+      const uint32_t tk = cand_key(sh.list[p.top_k - 1]);
+      int cK = 0;
+      for (int i = tid; i < U; i += BT) cK += cand_key(sh.list[i]) >= tk ? 1 : 0;
+      nK = block_sum<BT, int>(cK, sh.ri);
+    }
+    int nP = nK;
+    bool probe = false;
+    if (p.top_p < 1.0f) {
+      // Mass prefix over the sorted set, PER consecutive entries per thread.
+      double local = 0.0;
+      double wv[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = tid * PER + j;
+        wv[j] = i < nK ? static_cast<double>(
+                             fast_exp((key_to_float(cand_key(sh.list[i])) - m) * inv_t))
+                       : 0.0;
+        local += wv[j];
+      }
+      double total;
+      const double ex = block_exclusive_scan<BT, double>(local, sh.dscan, total);
+      if (tid == 0) {
+        if (kind == KIND_TOPK) sh.z = total;
+        sh.jstar = 0x7fffffff;
+      }
+      __syncthreads();
+      const double target = static_cast<double>(p.top_p) * sh.z;
+      double cum = ex;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const int i = tid * PER + j;
+        cum += wv[j];
+        if (i < nK && cum >= target) atomicMin(&sh.jstar, i);
+      }
+      __syncthreads();
+      if (sh.jstar == 0x7fffffff || (kind == KIND_TOPP && (force & 1))) {
+        probe = true;
+      } else {
+        const uint32_t tp = cand_key(sh.list[sh.jstar]);
+        int cP = 0;
+        for (int i = tid; i < nK; i += BT) cP += cand_key(sh.list[i]) >= tp ? 1 : 0;
+        nP = block_sum<BT, int>(cP, sh.ri);
+      }
+    }
+    if (!probe) {
+      float gk = -INFINITY;
+      int gi = 0x7fffffff;
+      for (int i = tid; i < nP; i += BT) {
+        const unsigned long long e = sh.list[i];
+        const int id = cand_id(e);
+        const float key = gumbel_key(key_to_float(cand_key(e)), m, inv_t, p.seed, grow, id);
+        if (better(key, id, gk, gi)) {
+          gk = key;
+          gi = id;
+        }
+      }
+      block_best<BT>(gk, gi, sh.rf, sh.ri);
+      token = gi;
+    } else {
+      // Top-p-only row whose boundary lies below the listed logits: the
+      // chunks' key candidates, complete above the highest chunk floor,
+      // sorted by row key; the best few become probes.
+      const int* keys = reinterpret_cast<const int*>(ws + lay.off_key) +
+                        static_cast<size_t>(r) * S * kKeyCap;
+      const float kmin = sh.kmin;
+      __syncthreads();
+      if (tid == 0) sh.nlist = 0;
+      __syncthreads();
+      const int kspan = S * kKeyCap;
+      for (int g = tid; g < kspan; g += BT) {
+        const int c = g / kKeyCap, i = g - c * kKeyCap;
+        if (i >= sh.recs[c].nkey) continue;
+        const int id = keys[g];
+        const float key = gumbel_key(row[id], m, inv_t, p.seed, grow, id);
+        if (key >= kmin) {
+          const int slot = atomicAdd(&sh.nlist, 1);
+          if (slot < kListMax) sh.list[slot] = pack_cand(order_key(key), id);
+        }
+      }
+      __syncthreads();
+      const int nk = sh.nlist;
+      if (nk == 0 || nk > kListMax) {
+        if (tid == 0) push_row(&ctr[0], exact_list, r);
+        return;
+      }
+      const int kp2 = next_pow2(nk);
+      for (int i = nk + tid; i < kp2; i += BT) sh.list[i] = 0ull;
+      __syncthreads();
+      bitonic_sort_desc<BT>(sh.list, kp2);
+      if (tid == 0) {
+        ProbeRec pr;
+        pr.z = sh.z;
+        pr.m = m;
+        pr.lse = lse;
+        pr.inv_t = inv_t;
+        pr.npts = nk < kProbes ? nk : kProbes;
+        for (int i = 0; i < kProbes; ++i) {
+          const int id = i < pr.npts ? cand_id(sh.list[i]) : 0;
+          pr.id[i] = id;
+          pr.pt[i] = i < pr.npts ? row[id] : INFINITY;
+        }
+        reinterpret_cast<ProbeRec*>(ws + lay.off_prec)[r] = pr;
+        push_row(&ctr[1], probe_list, r);
+      }
+      return;
+    }
+  }
+  if (tid == 0) {
+    a.token_ids[r] = token;
+    if (a.token_logprobs) a.token_logprobs[r] = row[token] - lse;
+    if (a.row_status) a.row_status[r] = TS_ROW_OK;
+  }
+}
+
+// ------------------------------------------------------------------- P: probe
+// Mass strictly above each probe logit, per (probe row, chunk).
+__global__ __launch_bounds__(PT) void probe_kernel(SamplerArgs a, FastLayout lay,
+                                                   uint8_t* __restrict__ ws, int vec) {
+  __shared__ double part[kProbes][PW];
+  const int S = lay.S;
+  const int count = reinterpret_cast<const int*>(ws + lay.off_ctr)[1];
+  const int* probe_list = reinterpret_cast<const int*>(ws + lay.off_probe);
+  const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
+  for (int w = blockIdx.x; w < count * S; w += gridDim.x) {
+    const int li = w / S, c = w - li * S;
+    const int r = probe_list[li];
+    const ProbeRec pr = reinterpret_cast<const ProbeRec*>(ws + lay.off_prec)[r];
+    const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
+    const int c0 = c * lay.L;
+    const int n = min(lay.L, a.vocab - c0);
+    const float sc = pr.inv_t * kLog2e;
+    float acc[kProbes];
+#pragma unroll
+    for (int i = 0; i < kProbes; ++i) acc[i] = 0.0f;
+    for (int e = 4 * tid; e < n; e += 4 * PT) {
+      float4 f;
+      if (vec && e + 3 < n) {
+        f = *reinterpret_cast<const float4*>(row + c0 + e);
+      } else {
+        f.x = e + 0 < n ? row[c0 + e + 0] : -INFINITY;
+        f.y = e + 1 < n ? row[c0 + e + 1] : -INFINITY;
+        f.z = e + 2 < n ? row[c0 + e + 2] : -INFINITY;
+        f.w = e + 3 < n ? row[c0 + e + 3] : -INFINITY;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float l = lane(f, q);
+        const float wt = __builtin_amdgcn_exp2f((l - pr.m) * sc);
+#pragma unroll
+        for (int i = 0; i < kProbes; ++i) acc[i] += l > pr.pt[i] ? wt : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kProbes; ++i) {
+      const double s = wave_sum(static_cast<double>(acc[i]));
+      if (lane_id == 0) part[i][wave] = s;
+    }
+    __syncthreads();
+    if (tid < kProbes) {
+      double t = 0.0;
+      for (int k = 0; k < PW; ++k) t += part[tid][k];
+      reinterpret_cast<double*>(ws + lay.off_part)[(static_cast<size_t>(li) * S + c) * kProbes + tid] = t;
+    }
+    __syncthreads();
+  }
+}
+
+// Diagnostic routes (same results): TS_SAMPLER_EXACT=1 samples every row with
+// the exact per-row kernel; TS_SAMPLER_FORCE_PROBE=1 sends every top-p-only
+// row through the probe pass.
+bool env_flag(const char* name) {
+  const char* e = getenv(name);
+  return e != nullptr && e[0] == '1';
+}
+
+}  // namespace
+
+size_t sampler_workspace_size(int64_t rows, int64_t vocab, int max_logprobs) {
+  (void)max_logprobs;
+  if (!fast_path_supported(rows, vocab)) return 256;
+  return make_layout(rows, vocab).total;
+}
+
+hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  (void)workspace_bytes;
+  if (a.rows == 0) return hipSuccess;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (env_flag("TS_SAMPLER_EXACT") || !fast_path_supported(a.rows, a.vocab))
+    return launch_sampler_finish(a, nullptr, ws, stream);
+  const FastLayout lay = make_layout(a.rows, a.vocab);
+  const int vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.ld % 4 == 0);
+  const unsigned chunks = static_cast<unsigned>(a.rows) * static_cast<unsigned>(lay.S);
+  hipLaunchKernelGGL(chunk_pass_kernel, dim3(chunks), dim3(AT), 0, stream, a, lay, ws, vec);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int force = env_flag("TS_SAMPLER_FORCE_PROBE") ? 1 : 0;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.rows), dim3(BT), 0, stream, a, lay, ws, force);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned pgrid = chunks < 2048u ? chunks : 2048u;
+  hipLaunchKernelGGL(probe_kernel, dim3(pgrid), dim3(PT), 0, stream, a, lay, ws, vec);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sampler_finish(a, &lay, ws, stream);
+}
+
+}  // namespace ts
