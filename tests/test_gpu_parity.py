@@ -306,6 +306,29 @@ def test_sampler_edge_cases(dev, ts, V, kind, route):
              res.row_status, res.flagged, lse, logits, max_frac=1.0, label=f"{V}/{kind}")
 
 
+@pytest.mark.parametrize("layout", ["crowded", "spread"])
+def test_sampler_large_targets(dev, ts, layout, route):
+    """Large top-k / top-N rows: with the largest logits crowded into one
+    stretch of the vocabulary, every chunk's share of the list is too short
+    and the row must still come out exact."""
+    rng = np.random.default_rng(11 if layout == "crowded" else 12)
+    rows, V, max_lp = 8, 70000, 300
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    if layout == "crowded":
+        for r in range(rows):
+            start = int(rng.integers(0, V - 3000))
+            logits[r, start:start + 3000] += 6.0
+    params = workloads.random_params(rng, rows, V, max_lp)
+    params["top_k"] = np.array([1000, 300, 65, 1024, 0, 1000, 200, 700], dtype=np.int32)
+    params["n_logprobs"] = np.array([300, 0, 300, 5, 300, 100, 65, 299], dtype=np.int32)
+    params["temperature"][:] = 0.9
+    say("sampler large targets", layout, route)
+    got = _run_sampler(ts, dev, logits, params, 3, max_lp)
+    res, lse = _oracle_ref(logits, params, 3, max_lp)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=layout)
+
+
 def test_sampler_bad_rows(dev, ts, route):
     rng = np.random.default_rng(0)
     rows, V = 12, 500

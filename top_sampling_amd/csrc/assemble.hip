@@ -7,6 +7,7 @@
 // HBM-bound copy: every byte is read once and written once.  One workgroup
 // copies one 4096-float column chunk of one slice for a stride of rows;
 // 16-byte loads and stores when every slice allows them.
+#include "device_common.hpp"
 #include "ts_internal.hpp"
 
 namespace ts {
@@ -40,12 +41,12 @@ __global__ __launch_bounds__(kAsmThreads) void assemble_kernel(AssembleSlices s,
 #pragma unroll
       for (int j = 0; j < kAsmChunk / 4 / kAsmThreads; ++j) {
         const int i = threadIdx.x + j * kAsmThreads;
-        v[j] = (i < n4) ? s4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        v[j] = load_stream4(reinterpret_cast<const float*>(s4 + (i < n4 ? i : 0)));
       }
 #pragma unroll
       for (int j = 0; j < kAsmChunk / 4 / kAsmThreads; ++j) {
         const int i = threadIdx.x + j * kAsmThreads;
-        if (i < n4) d4[i] = v[j];
+        if (i < n4) store_stream4(reinterpret_cast<float*>(d4 + i), v[j]);
       }
     } else {
       for (int i = threadIdx.x; i < n; i += kAsmThreads) dst[i] = src[i];

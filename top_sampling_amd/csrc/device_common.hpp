@@ -87,6 +87,26 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * kLog2e);
 }
 
+// ------------------------------------------------------------ streaming loads
+// Non-temporal loads for data each kernel reads once: the lines are not kept
+// in the caches, so a stream does not evict (and write back) other data.  On
+// MI355X this doubles the read rate of a one-pass scan.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+  const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+
+__device__ __forceinline__ float load_stream(const float* p) {
+  return __builtin_nontemporal_load(p);
+}
+
+__device__ __forceinline__ void store_stream4(float* p, const float4& v) {
+  const f32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<f32x4_t*>(p));
+}
+
 // ------------------------------------------------------------ reductions
 // Ordering of (key, id) candidates: larger key first, lower id on ties.
 __device__ __forceinline__ bool better(float ka, int ia, float kb, int ib) {

@@ -49,6 +49,19 @@ __device__ __forceinline__ int cand_target(int kind, const ts_row_params& p, int
   return M < V ? M : V;
 }
 
+// How many of its largest logits one of S chunks lists.  Up to 64 every chunk
+// lists the row's whole target M, so the union of the lists holds the row's M
+// largest whatever their distribution.  Above 64 a chunk lists twice its
+// share, at least 64: the union then holds the row's M largest unless they
+// crowd into a few chunks, which the merge detects (fewer than M entries
+// above the highest chunk threshold) and hands to the exact kernel.
+__device__ __forceinline__ int chunk_target(int M, int S) {
+  if (M <= 64) return M;
+  int mc = (2 * M + S - 1) / S;
+  mc = mc > 64 ? mc : 64;
+  return mc < M ? mc : M;
+}
+
 __device__ __forceinline__ int row_kind(const ts_row_params& p, int V, int max_logprobs) {
   if (!params_ok(p, max_logprobs)) return KIND_BAD;
   if (p.temperature < TS_GREEDY_EPS || p.top_k == 1) return KIND_GREEDY;
@@ -87,15 +100,14 @@ __device__ __forceinline__ float gumbel_key(float l, float m, float inv_t, uint6
 }
 
 // ------------------------------------------------------------ workspace layout
-constexpr int kCandCap = 1536;    // logit candidates per chunk
-constexpr int kKeyCap = 32;       // Gumbel-key candidates per chunk (top-p-only rows)
-constexpr int kKeyTarget = 8;     // chunk keys above which the key list is complete
+constexpr int kCandCap = 4096;    // logit candidates per chunk
+constexpr int kKeyCap = 64;       // Gumbel-key candidates per chunk (top-p-only rows)
 constexpr int kProbes = 8;        // probe points per top-p-only row
 constexpr int kMaxChunks = 128;   // chunks per row
 constexpr int kChunkThreads = 256;
 constexpr int kChunkVec = 16;     // float4 per thread
 constexpr int kChunkMax = kChunkThreads * kChunkVec * 4;  // 16384 logits
-constexpr int kListMax = 4096;    // merged candidates a row may keep in LDS
+constexpr int kListMax = 2048;    // merged candidates a row may keep in LDS
 constexpr float kKeyMargin = 1e-4f;  // rounding margin between chunk-local and row keys
 
 struct ChunkRec {  // one per (row, chunk); 64 bytes

@@ -46,7 +46,7 @@ constexpr int AT = kChunkThreads;
 constexpr int AW = AT / kWave;
 constexpr int AV = kChunkVec;
 constexpr int RB = 2048;
-constexpr int BT = 1024;
+constexpr int BT = 256;
 constexpr int BW = BT / kWave;
 constexpr int PT = 256;
 constexpr int PW = PT / kWave;
@@ -103,32 +103,10 @@ __device__ uint32_t lds_kth_largest(const uint32_t* keys, int nk, uint32_t M, ui
   return prefix;
 }
 
-// Visit the valid logits (l, id) of this thread's 16 float4.
-#define FOR_VALID(BODY)                                       \
-  _Pragma("unroll") for (int j = 0; j < AV; ++j) {            \
-    const int e = 4 * (j * AT + tid);                         \
-    if (e + 3 < n) {                                          \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {         \
-        const float l = lane(v[j], q);                        \
-        const int id = c0 + e + q;                            \
-        (void)id;                                             \
-        BODY                                                  \
-      }                                                       \
-    } else if (e < n) {                                       \
-      _Pragma("unroll") for (int q = 0; q < 4; ++q) {         \
-        if (e + q < n) {                                      \
-          const float l = lane(v[j], q);                      \
-          const int id = c0 + e + q;                          \
-          (void)id;                                           \
-          BODY                                                \
-        }                                                     \
-      }                                                       \
-    }                                                         \
-  }
-
 // ------------------------------------------------------------------ A: chunks
 struct ChunkSmem {
   uint32_t hist[RB];
+  uint32_t keys4[4 * AT];  // per-thread top-4 keys (block-level selection)
   int klist[kKeyCap];
   float wthr[AW];
   float rm[AW], rs[AW], rt[AW];
@@ -139,6 +117,47 @@ struct ChunkSmem {
   uint32_t sel_d, sel_above;
   int ncand, nkey;
 };
+
+__device__ __forceinline__ void set_lane(float4& f, int q, float x) {
+  if (q == 0) f.x = x;
+  else if (q == 1) f.y = x;
+  else if (q == 2) f.z = x;
+  else f.w = x;
+}
+
+// The chunk into registers: logit e = 4 * (j * AT + tid) + q of the chunk in
+// lane q of v[j]; slots past the chunk end hold -inf.  Every load is issued
+// unconditionally (out-of-range slots re-read the chunk's last element), so
+// all sixteen are in flight together, as non-temporal (streaming) loads.
+// VEC: 16-byte aligned rows and n % 4 == 0.
+template <bool VEC>
+__device__ __forceinline__ void load_chunk(float4 (&v)[AV], const float* __restrict__ src, int n,
+                                           int tid) {
+  if (VEC) {
+    const int n4 = n >> 2;
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const int i4 = j * AT + tid;
+      const bool ok = i4 < n4;
+      const float4 f = load_stream4(src + 4 * (ok ? i4 : n4 - 1));
+      v[j].x = ok ? f.x : -INFINITY;
+      v[j].y = ok ? f.y : -INFINITY;
+      v[j].z = ok ? f.z : -INFINITY;
+      v[j].w = ok ? f.w : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const int e = 4 * (j * AT + tid);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool ok = e + q < n;
+        const float x = load_stream(src + (ok ? e + q : n - 1));
+        set_lane(v[j], q, ok ? x : -INFINITY);
+      }
+    }
+  }
+}
 
 // (m, s, t): a maximum with sum exp(l - m) and sum exp((l - m) / T); merging
 // two rescales both sums to the larger maximum.
@@ -165,8 +184,41 @@ __device__ __forceinline__ float wave_qth4(const float (&t)[4], int q) {
   return __shfl(mine, idx >> 2, kWave);
 }
 
-__global__ __launch_bounds__(AT) void chunk_pass_kernel(SamplerArgs a, FastLayout lay,
-                                                        uint8_t* __restrict__ ws, int vec) {
+// Smallest 23-bit uniform index m = x >> 9 a token needs so that its key
+// x_tok + g(u) can exceed `bar`, given x_tok <= xm: g(u) > bar - x_tok needs
+// u > exp(-exp(xm - bar)).  The bound is lowered by a relative 2^-10 and one
+// unit, far beyond the error of the hardware exponentials, so no token that
+// could exceed the bar is skipped.
+__device__ __forceinline__ uint32_t u_floor_bits(float xm, float bar) {
+  const float e1 = __builtin_amdgcn_exp2f((xm - bar) * kLog2e);
+  const float u0 = __builtin_amdgcn_exp2f(-e1 * kLog2e) * (1.0f - 0.0009765625f);
+  const float th = u0 * 8388608.0f - 1.0f;
+  return th > 0.0f ? static_cast<uint32_t>(th) : 0u;
+}
+
+__device__ __forceinline__ void insert3(float key, int id, float (&k)[3], int (&i)[3]) {
+  if (!better(key, id, k[2], i[2])) return;
+  if (better(key, id, k[1], i[1])) {
+    k[2] = k[1];
+    i[2] = i[1];
+    if (better(key, id, k[0], i[0])) {
+      k[1] = k[0];
+      i[1] = i[0];
+      k[0] = key;
+      i[0] = id;
+    } else {
+      k[1] = key;
+      i[1] = id;
+    }
+  } else {
+    k[2] = key;
+    i[2] = id;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLayout lay,
+                                                        uint8_t* __restrict__ ws) {
   __shared__ ChunkSmem sh;
   const int S = lay.S;
   const int bid = blockIdx.x;
@@ -184,25 +236,12 @@ __global__ __launch_bounds__(AT) void chunk_pass_kernel(SamplerArgs a, FastLayou
   const bool topp = kind == KIND_TOPP;
   const float inv_t = kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature;
 
-  // The chunk: 16 float4 per thread, logit e = 4 * (j * AT + tid) + q.
   float4 v[AV];
-#pragma unroll
-  for (int j = 0; j < AV; ++j) {
-    const int e = 4 * (j * AT + tid);
-    if (vec && e + 3 < n) {
-      v[j] = *reinterpret_cast<const float4*>(row + c0 + e);
-    } else {
-      v[j].x = e + 0 < n ? row[c0 + e + 0] : -INFINITY;
-      v[j].y = e + 1 < n ? row[c0 + e + 1] : -INFINITY;
-      v[j].z = e + 2 < n ? row[c0 + e + 2] : -INFINITY;
-      v[j].w = e + 3 < n ? row[c0 + e + 3] : -INFINITY;
-    }
-  }
+  load_chunk<VEC>(v, row + c0, n, tid);
 
-  // Per-thread largest value (or largest four when M > 256).  Out-of-chunk
-  // slots hold -inf, which changes no maximum and adds no mass.
-  const int M = cand_target(kind, p, V);
-  const bool four = M > 256;
+  // Per-thread largest value (largest four when M > 64).
+  const int M = chunk_target(cand_target(kind, p, V), S);
+  const bool four = M > 64 && M < n;
   float t[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   if (four) {
 #pragma unroll
@@ -258,6 +297,23 @@ __global__ __launch_bounds__(AT) void chunk_pass_kernel(SamplerArgs a, FastLayou
     sh.rt[wave] = lt;
     sh.rb[wave] = flag;
   }
+  if (tid == 0) {
+    sh.ncand = 0;
+    sh.nkey = 0;
+  }
+  // Logit candidate threshold tf: at least M logits of the chunk are >= tf.
+  // M <= 64: every wave holds ceil(M/4) per-thread maxima >= its own q-th
+  // largest, so the smallest of the four wave values works.  64 < M <= 256:
+  // the same over per-thread top-4 values.  M > 256: the M-th largest of the
+  // block's 4 * 256 top-4 values, by radix selection in LDS.
+  if (M < n && M <= 256) {
+    const int q = (M + AW - 1) / AW;
+    const float tw = four ? wave_qth4(t, q) : wave_qth(t[0], q);
+    if (lane_id == 0) sh.wthr[wave] = tw;
+  } else if (M < n) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sh.keys4[4 * tid + i] = order_key(t[i]);
+  }
   __syncthreads();
   float cmax = sh.rm[0], s = sh.rs[0], tmass = sh.rt[0];
   int bad = sh.rb[0];
@@ -271,171 +327,118 @@ __global__ __launch_bounds__(AT) void chunk_pass_kernel(SamplerArgs a, FastLayou
     return;
   }
   if (!topp) tmass = 0.0f;
-
-  // Logit candidate threshold tf: every wave holds ceil(M/4) per-thread
-  // values >= its own q-th largest, so at least M logits are >= the smallest
-  // of the four.  The list takes every logit >= tf.
   float tf = -INFINITY;
-  if (M < n) {
-    const int q = (M + AW - 1) / AW;
-    const float tw = four ? wave_qth4(t, q) : wave_qth(t[0], q);
-    if (lane_id == 0) sh.wthr[wave] = tw;
-  }
-  if (tid == 0) {
-    sh.ncand = 0;
-    sh.nkey = 0;
-  }
-  __syncthreads();
-  if (M < n) {
+  if (M < n && M <= 256) {
     tf = sh.wthr[0];
 #pragma unroll
     for (int w = 1; w < AW; ++w) tf = fminf(tf, sh.wthr[w]);
+  } else if (M < n) {
+    const uint32_t kk = lds_kth_largest<AT>(sh.keys4, 4 * AT, static_cast<uint32_t>(M), sh.hist,
+                                            sh.ru, &sh.sel_d, &sh.sel_above);
+    tf = key_floor_value(kk);
   }
+
+  // Every valid logit >= tf goes to the chunk's candidate list.
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws + lay.off_cand) +
                              static_cast<size_t>(bid) * kCandCap;
-  FOR_VALID(if (l >= tf) {
-    const int slot = atomicAdd(&sh.ncand, 1);
-    if (slot < kCandCap) cand[slot] = pack_cand(order_key(l), id);
-  })
-  __syncthreads();
-  uint32_t kt = order_key(tf);
-  bool ovf = sh.ncand > kCandCap;
-  if (ovf) {
-    // Too many ties or a flat chunk: radix selection over every logit.
-    uint32_t prefix = 0u, pmask = 0u, rem = static_cast<uint32_t>(M), above = 0u, cnt = 0u;
-    for (int rd = 0; rd < 3; ++rd) {
-      const int shift = rd == 0 ? 21 : (rd == 1 ? 10 : 0);
-      const int width = rd == 2 ? 10 : 11;
-      const uint32_t dmask = (1u << width) - 1u;
-      for (int b = tid; b < RB; b += AT) sh.hist[b] = 0u;
-      __syncthreads();
-      FOR_VALID({
-        const uint32_t key = order_key(l);
-        if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
-      })
-      __syncthreads();
-      select_digit_top<AT, RB / AT>(sh.hist, 1 << width, rem, sh.ru, &sh.sel_d, &sh.sel_above);
-      const uint32_t d = sh.sel_d, ab = sh.sel_above, hd = sh.hist[d];
-      __syncthreads();
-      above += ab;
-      rem -= ab;
-      prefix |= d << shift;
-      pmask |= dmask << shift;
-      cnt = above + hd;
-      if (cnt <= static_cast<uint32_t>(kCandCap)) break;
+#pragma unroll
+  for (int j = 0; j < AV; ++j) {
+    const float4 f = v[j];
+    if (fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)) >= tf) {
+      const int e = 4 * (j * AT + tid);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float l = lane(f, q);
+        if (l >= tf && e + q < n) {
+          const int slot = atomicAdd(&sh.ncand, 1);
+          if (slot < kCandCap) cand[slot] = pack_cand(order_key(l), c0 + e + q);
+        }
+      }
     }
-    kt = prefix;
-    ovf = cnt > static_cast<uint32_t>(kCandCap);
-    if (tid == 0) sh.ncand = 0;
-    __syncthreads();
-    if (!ovf) {
-      FOR_VALID(if (order_key(l) >= kt) {
-        const int slot = atomicAdd(&sh.ncand, 1);
-        cand[slot] = pack_cand(order_key(l), id);
-      })
-    }
-    __syncthreads();
   }
 
   // Gumbel keys relative to the chunk maximum: x = (l - cmax) / T, key = x + g.
   float kfloor = INFINITY;
-  bool key_ovf = false;
   if (kind == KIND_FULL || topp) {
     const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
-    // Full rows: the chunk maximum's key is at least the smallest Gumbel
-    // value, so no token whose key cannot reach it needs its noise.
+    // Full rows keep each thread's best key; the chunk maximum's key is at
+    // least the smallest Gumbel value, so no token below that bar needs its
+    // noise.  Top-p-only rows keep each thread's best three.
+    float kb[3] = {-INFINITY, -INFINITY, -INFINITY};
+    int ib[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
     const float bar0 = topp ? -INFINITY : kMinGumbel;
-    float k1 = -INFINITY, k2 = -INFINITY;
-    int i1 = 0x7fffffff, i2 = 0x7fffffff;
 #pragma unroll
     for (int j = 0; j < AV; ++j) {
       const int e = 4 * (j * AT + tid);
-      if (e >= n) continue;
       float x[4];
-      float xm = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x[q] = e + q < n ? (lane(v[j], q) - cmax) * inv_t : -INFINITY;
-        xm = fmaxf(xm, x[q]);
-      }
-      // A key is x + g with g below kGumbelMax: skip the noise when no token
-      // of the four can enter this thread's best one (or two).
-      if (xm + kGumbelMax < fmaxf(bar0, topp ? k2 : k1)) continue;
+      for (int q = 0; q < 4; ++q) x[q] = (lane(v[j], q) - cmax) * inv_t;
+      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      const float bar = fmaxf(bar0, topp ? kb[2] : kb[0]);
+      if (xm + kGumbelMax < bar) continue;  // also skips all-padding slots
+      const uint32_t th = u_floor_bits(xm, bar);
       const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (x[q] == -INFINITY) continue;
+        if ((w.v[q] >> 9) < th || x[q] == -INFINITY) continue;
         const float key = x[q] + gumbel_from_word(w.v[q]);
         const int id = c0 + e + q;
-        if (better(key, id, k1, i1)) {
-          k2 = k1;
-          i2 = i1;
-          k1 = key;
-          i1 = id;
-        } else if (topp && better(key, id, k2, i2)) {
-          k2 = key;
-          i2 = id;
+        if (topp) {
+          insert3(key, id, kb, ib);
+        } else if (better(key, id, kb[0], ib[0])) {
+          kb[0] = key;
+          ib[0] = id;
         }
       }
     }
     int* klist_out = reinterpret_cast<int*>(ws + lay.off_key) + static_cast<size_t>(bid) * kKeyCap;
     if (!topp) {
+      float k1 = kb[0];
+      int i1 = ib[0];
       block_best<AT>(k1, i1, sh.rf, sh.ri);
       if (tid == 0 && i1 != 0x7fffffff) {
         klist_out[0] = i1;
         sh.nkey = 1;
       }
       kfloor = k1;
-      __syncthreads();
     } else {
-      // Floor: each wave's second-best per-thread key, the smallest of the
-      // four; at least kKeyTarget threads have a best key at or above it.
-      // Every token at or above the floor is listed: a thread's best if it
-      // qualifies, and all of a thread's qualifying tokens when its second
-      // best qualifies too (the thread recomputes its keys).
-      const float tw = wave_qth(k1, kKeyTarget / AW);
+      // Floor F >= every thread's third-best key, so the tokens with key >=
+      // F all sit in the threads' top-three lists; F is also raised to the
+      // smallest of the four waves' third-largest best keys to keep the
+      // list short (at least twelve entries when it is raised).
+      const float f0 = block_max<AT>(kb[2], sh.rf);
+      const float tw = wave_qth(kb[0], 3);
       if (lane_id == 0) sh.wthr[wave] = tw;
       __syncthreads();
-      kfloor = sh.wthr[0];
+      float g = sh.wthr[0];
 #pragma unroll
-      for (int w = 1; w < AW; ++w) kfloor = fminf(kfloor, sh.wthr[w]);
-      if (k2 > -INFINITY && k2 >= kfloor) {
+      for (int w = 1; w < AW; ++w) g = fminf(g, sh.wthr[w]);
+      kfloor = fmaxf(f0, g);
 #pragma unroll
-        for (int j = 0; j < AV; ++j) {
-          const int e = 4 * (j * AT + tid);
-          if (e >= n) continue;
-          const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (e + q >= n) continue;
-            const float x = (lane(v[j], q) - cmax) * inv_t;
-            if (x == -INFINITY) continue;
-            const float key = x + gumbel_from_word(w.v[q]);
-            if (key >= kfloor) {
-              const int slot = atomicAdd(&sh.nkey, 1);
-              if (slot < kKeyCap) sh.klist[slot] = c0 + e + q;
-            }
-          }
+      for (int i = 0; i < 3; ++i) {
+        if (ib[i] != 0x7fffffff && kb[i] >= kfloor) {
+          const int slot = atomicAdd(&sh.nkey, 1);
+          if (slot < kKeyCap) sh.klist[slot] = ib[i];
         }
-      } else if (k1 > -INFINITY && k1 >= kfloor) {
-        const int slot = atomicAdd(&sh.nkey, 1);
-        if (slot < kKeyCap) sh.klist[slot] = i1;
       }
       __syncthreads();
-      key_ovf = sh.nkey > kKeyCap;
-      if (!key_ovf && tid < sh.nkey) klist_out[tid] = sh.klist[tid];
+      if (sh.nkey <= kKeyCap && tid < sh.nkey) klist_out[tid] = sh.klist[tid];
     }
   }
+  __syncthreads();
   if (tid == 0) {
+    const bool ovf = sh.ncand > kCandCap, key_ovf = sh.nkey > kKeyCap;
     ChunkRec o;
     o.cmax = cmax;
     o.sumexp = s;
     o.tmass = tmass;
-    o.kt = kt;
+    o.kt = order_key(tf);
     o.ncand = ovf ? 0 : sh.ncand;
     o.status = (ovf || key_ovf) ? 2 : 0;
     o.nkey = key_ovf ? 0 : sh.nkey;
     o.kfloor = kfloor;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.pad[i] = 0;
     *rec = o;
   }
 }
@@ -617,7 +620,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   }
   __syncthreads();
   const int U = sh.nlist;
-  if (U > kListMax) {
+  if (U > kListMax || U < cand_target(kind, p, V)) {
     if (tid == 0) push_row(&ctr[0], exact_list, r);
     return;
   }
@@ -798,12 +801,12 @@ __global__ __launch_bounds__(PT) void probe_kernel(SamplerArgs a, FastLayout lay
     for (int e = 4 * tid; e < n; e += 4 * PT) {
       float4 f;
       if (vec && e + 3 < n) {
-        f = *reinterpret_cast<const float4*>(row + c0 + e);
+        f = load_stream4(row + c0 + e);
       } else {
-        f.x = e + 0 < n ? row[c0 + e + 0] : -INFINITY;
-        f.y = e + 1 < n ? row[c0 + e + 1] : -INFINITY;
-        f.z = e + 2 < n ? row[c0 + e + 2] : -INFINITY;
-        f.w = e + 3 < n ? row[c0 + e + 3] : -INFINITY;
+        f.x = e + 0 < n ? load_stream(row + c0 + e + 0) : -INFINITY;
+        f.y = e + 1 < n ? load_stream(row + c0 + e + 1) : -INFINITY;
+        f.z = e + 2 < n ? load_stream(row + c0 + e + 2) : -INFINITY;
+        f.w = e + 3 < n ? load_stream(row + c0 + e + 3) : -INFINITY;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -852,9 +855,13 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
   if (env_flag("TS_SAMPLER_EXACT") || !fast_path_supported(a.rows, a.vocab))
     return launch_sampler_finish(a, nullptr, ws, stream);
   const FastLayout lay = make_layout(a.rows, a.vocab);
-  const int vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.ld % 4 == 0);
+  const int vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.ld % 4 == 0) &&
+                  (a.vocab % 4 == 0);
   const unsigned chunks = static_cast<unsigned>(a.rows) * static_cast<unsigned>(lay.S);
-  hipLaunchKernelGGL(chunk_pass_kernel, dim3(chunks), dim3(AT), 0, stream, a, lay, ws, vec);
+  if (vec)
+    hipLaunchKernelGGL(chunk_pass_kernel<true>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
+  else
+    hipLaunchKernelGGL(chunk_pass_kernel<false>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int force = env_flag("TS_SAMPLER_FORCE_PROBE") ? 1 : 0;
