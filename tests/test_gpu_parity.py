@@ -55,7 +55,21 @@ def _bits(t):
 
 
 # ------------------------------------------------------------------ GEMM
-def test_gemm_tiny_workload(dev, ts):
+# Every projection tile shape (see the dispatch in lmhead_gemm.hip); "" is the
+# size-based default.
+GEMM_TILES = ["", "1", "2", "3", "4", "5"]
+
+
+@pytest.fixture(params=GEMM_TILES)
+def gemm_tile(request, monkeypatch):
+    if request.param:
+        monkeypatch.setenv("TS_GEMM_TILE", request.param)
+    else:
+        monkeypatch.delenv("TS_GEMM_TILE", raising=False)
+    return request.param
+
+
+def test_gemm_tiny_workload(dev, ts, gemm_tile):
     w = workloads.get("tiny")
     xb, wb = workloads.make_projection_host(w)
     say("gemm tiny", xb.shape, wb.shape)
@@ -67,8 +81,9 @@ def test_gemm_tiny_workload(dev, ts):
 
 @pytest.mark.parametrize("rows,vocab,hidden", [
     (1, 300, 64), (4, 4096, 256), (63, 1000, 520), (65, 513, 136), (129, 777, 264),
-    (257, 1031, 1032), (300, 2000, 8), (640, 700, 4096)])
-def test_gemm_ragged(dev, ts, rows, vocab, hidden):
+    (257, 1031, 1032), (300, 2000, 8), (640, 700, 4096), (65, 513, 128), (257, 1031, 1024),
+    (333, 300, 192), (700, 1500, 64)])
+def test_gemm_ragged(dev, ts, rows, vocab, hidden, gemm_tile):
     rng = np.random.default_rng(rows * 7 + vocab)
     xb = workloads.bf16_bits_from_f32(rng.standard_normal((rows, hidden)).astype(np.float32))
     wb = workloads.bf16_bits_from_f32(
@@ -80,7 +95,7 @@ def test_gemm_ragged(dev, ts, rows, vocab, hidden):
     assert err <= LOGIT_TOL, err
 
 
-def test_gemm_slices_into_wide_buffer(dev, ts):
+def test_gemm_slices_into_wide_buffer(dev, ts, gemm_tile):
     """Vocabulary slices written through ld_logits into one buffer equal one
     full projection bit for bit, and columns outside the slices are untouched."""
     import torch
@@ -102,14 +117,19 @@ def test_gemm_slices_into_wide_buffer(dev, ts):
     assert torch.all(wide[:, vocab:] == 7.0)
 
 
-@pytest.mark.parametrize("name", ["decode", "spec_decode", "large"])
-def test_gemm_full_size_sampled(dev, ts, name):
+@pytest.mark.parametrize("name,tile", [("decode", ""), ("spec_decode", ""), ("large", ""),
+                                       ("spec_decode", "3"), ("large", "4")])
+def test_gemm_full_size_sampled(dev, ts, name, tile, monkeypatch):
     """Full-size projection in the launch configuration the bench times,
     checked on sampled rows and columns (including the ragged tails)."""
     import torch
 
+    if tile:
+        monkeypatch.setenv("TS_GEMM_TILE", tile)
+    else:
+        monkeypatch.delenv("TS_GEMM_TILE", raising=False)
     w = workloads.get(name)
-    say("gemm full", name)
+    say("gemm full", name, tile)
     x, wt = workloads.make_projection_device(w, dev)
     out = ts.lmhead_logits_local(x, wt)
     torch.cuda.synchronize()

@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the sampling path runs in the HIP
 kernels behind the C ABI (``include/top_sampling.h``).  PyTorch supplies device
 memory and the current stream.  Importing this package fails if the library is
-not built (``python -m top_sampling_amd.build``); there is no fallback.
+not built (``python top_sampling_amd/build.py``); there is no fallback.
 
 Calls mirror the C entry points:
   lmhead_logits_local            local vocabulary projection, bf16 -> fp32
@@ -54,7 +54,7 @@ def _load() -> ctypes.CDLL:
 
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m top_sampling_amd.build` (hipcc, gfx950)")
+            f"{LIB_PATH} is not built; run `python top_sampling_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SYMBOLS.items():
         fn = getattr(lib, name)

@@ -1,7 +1,8 @@
 """Build ``libtopsampling.so`` (gfx950 only) in-tree with hipcc.
 
-Usage: ``python -m top_sampling_amd.build`` (or ``build()`` from Python).
-Every call recompiles every source.
+Usage: ``python top_sampling_amd/build.py`` (or ``build()`` after loading this
+file by path; importing the package loads the library, so this script never
+imports it).  Every call recompiles every source.
 """
 from __future__ import annotations
 
