@@ -40,7 +40,7 @@ def parse():
                     choices=["decode", "spec_decode", "rank_share", "large"])
     ap.add_argument("--slices", type=int, default=4, help="vocabulary slices (TP ranks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=128,
+    ap.add_argument("--cpu-rows", type=int, default=640,
                     help="rows of the workload the CPU oracle is timed on")
     return ap.parse_args()
 
@@ -73,6 +73,30 @@ def cpu_baseline(x, wt, logits_sample, params, max_logprobs, rows: int):
                    f"({t1 - t0:.1f}s, BLAS threads {threads}) + full-sort sampler "
                    f"({t2 - t1:.1f}s, 1 thread)"),
     }
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per projection launch from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when
+    the summary is for another workload or the kernel source has changed
+    since the counters were taken."""
+    import hashlib
+
+    if workload != "spec_decode":
+        return None
+    path = os.path.join(ROOT, "profiles", "spec_decode_step_hbm_traffic.md")
+    src = os.path.join(ROOT, "top_sampling_amd", "csrc", "lmhead_gemm.hip")
+    try:
+        text = open(path).read()
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    for ln in text.splitlines():
+        f = ln.split()
+        if len(f) == 3 and f[0] == "lmhead_gemm" and f[1].startswith("traffic_bytes_per_launch="):
+            if f[2] == f"source_sha256_16={digest}":
+                return int(f[1].split("=", 1)[1])
+    return None
 
 
 def main():
@@ -151,7 +175,8 @@ def main():
     if flops:
         roof = {"kernel": "lmhead_gemm", "bound": "mfma", "achieved": round(gemm_tflops, 1),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+                "traffic": recorded_traffic(w.name)}
     else:
         roof = {"kernel": "sampler", "bound": "hbm", "achieved": round(smp_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(smp_gbs / HBM_PEAK_GBS, 4),
