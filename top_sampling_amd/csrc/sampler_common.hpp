@@ -51,13 +51,13 @@ __device__ __forceinline__ int cand_target(int kind, const ts_row_params& p, int
 
 // How many of its largest logits one of S chunks lists.  Up to 64 every chunk
 // lists the row's whole target M, so the union of the lists holds the row's M
-// largest whatever their distribution.  Above 64 a chunk lists twice its
+// largest whatever their distribution.  Above 64 a chunk lists 1.5 times its
 // share, at least 64: the union then holds the row's M largest unless they
 // crowd into a few chunks, which the merge detects (fewer than M entries
 // above the highest chunk threshold) and hands to the exact kernel.
 __device__ __forceinline__ int chunk_target(int M, int S) {
   if (M <= 64) return M;
-  int mc = (2 * M + S - 1) / S;
+  int mc = (3 * M + 2 * S - 1) / (2 * S);
   mc = mc > 64 ? mc : 64;
   return mc < M ? mc : M;
 }
@@ -188,25 +188,10 @@ inline bool fast_path_supported(int64_t rows, int64_t vocab) {
 typedef double double4v __attribute__((ext_vector_type(4)));
 typedef double double2v __attribute__((ext_vector_type(2)));
 
-// Sort n (a power of two) packed candidates in LDS, largest first.
-template <int NT>
-__device__ void bitonic_sort_desc(unsigned long long* s, int n) {
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < n; i += NT) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long a = s[i], b = s[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (a < b) : (a > b)) {
-            s[i] = b;
-            s[ixj] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int mask) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), mask, kWave);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), mask, kWave);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
 }
 
 __device__ __forceinline__ int next_pow2(int x) {

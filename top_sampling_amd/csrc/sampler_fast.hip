@@ -448,8 +448,11 @@ constexpr int kUnionMax = 1 << 20;  // candidates a merge workgroup walks
 
 struct MergeSmem {
   unsigned long long list[kListMax];
-  uint32_t hist[RB];
-  ChunkRec recs[kMaxChunks];
+  union {
+    ChunkRec recs[kMaxChunks];  // read once at the start of the merge
+    uint32_t hist[RB];          // radix bins, used afterwards
+  };
+  int nkey[kMaxChunks];         // the chunks' Gumbel-key list lengths
   int pos[kMaxChunks + 1];
   double dscan[BW];
   float rf[BW];
@@ -463,6 +466,129 @@ struct MergeSmem {
 };
 
 __device__ __forceinline__ void push_row(int* ctr, int* list, int r) { list[atomicAdd(ctr, 1)] = r; }
+
+// Bitonic sort of n (a power of two, <= kListMax) packed candidates in LDS,
+// largest first.  Each thread takes up to kListMax / (2 BT) compare-exchange
+// pairs per stage, loads all of them before comparing, so a stage costs one
+// LDS round trip and one barrier.
+__device__ void lds_bitonic_desc(unsigned long long* s, int n) {
+  constexpr int PAIRS = kListMax / (2 * BT);
+  const int tid = threadIdx.x, half = n >> 1;
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      int lo[PAIRS];
+      unsigned long long a[PAIRS], b[PAIRS];
+#pragma unroll
+      for (int t = 0; t < PAIRS; ++t) {
+        const int q = tid + t * BT;
+        lo[t] = ((q & ~(j - 1)) << 1) | (q & (j - 1));  // j is a power of two
+        if (q < half) {
+          a[t] = s[lo[t]];
+          b[t] = s[lo[t] + j];
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < PAIRS; ++t) {
+        const int q = tid + t * BT;
+        if (q < half) {
+          const bool desc = (lo[t] & k) == 0;
+          if (desc ? (a[t] < b[t]) : (a[t] > b[t])) {
+            s[lo[t]] = b[t];
+            s[lo[t] + j] = a[t];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Keeps the entries of sh.list[0, U) (all with key >= floor_key) that are at
+// least the need-th largest, plus whatever shares its radix bin when the list
+// is long (at most need + 64 entries, or the power of two the sort pads to,
+// unless ties force more), and leaves them
+// in sh.list sorted largest first; returns their count.  Radix selection on
+// the key offset above the floor, digits from its highest set bit; sorting by
+// rank (entries are unique: the low word holds the inverted token id).
+__device__ int trim_and_sort(MergeSmem& sh, int U, int need, uint32_t floor_key) {
+  const int tid = threadIdx.x;
+  int cap = need + 64;
+  if (cap > 256) cap = cap <= 1024 ? 1024 : kListMax;  // what the sort pads to anyway
+  int C = U;
+  if (U > cap) {
+    uint32_t rmax = 0u;
+    for (int i = tid; i < U; i += BT) rmax = max(rmax, cand_key(sh.list[i]) - floor_key);
+    if (tid == 0) sh.rmax = 0u;
+    __syncthreads();
+    atomicMax(&sh.rmax, rmax);
+    __syncthreads();
+    rmax = sh.rmax;
+    const int hb = rmax == 0u ? -1 : 31 - __builtin_clz(rmax);
+    uint32_t prefix = 0u, rem = static_cast<uint32_t>(need), above = 0u;
+    int lowbit = hb + 1;
+    while (lowbit > 0) {
+      const int width = lowbit < 11 ? lowbit : 11;
+      const int shift = lowbit - width;
+      const uint32_t dmask = (1u << width) - 1u;
+      const uint32_t hi_pref = lowbit >= 32 ? 0u : (prefix >> lowbit);
+      for (int b = tid; b < RB; b += BT) sh.hist[b] = 0u;
+      __syncthreads();
+      for (int i = tid; i < U; i += BT) {
+        const uint32_t off = cand_key(sh.list[i]) - floor_key;
+        if ((lowbit >= 32 ? 0u : (off >> lowbit)) == hi_pref)
+          atomicAdd(&sh.hist[(off >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      select_digit_top<BT, RB / BT>(sh.hist, 1 << width, rem, sh.ru, &sh.sel_d, &sh.sel_above);
+      const uint32_t d = sh.sel_d, ab = sh.sel_above, hd = sh.hist[d];
+      __syncthreads();
+      above += ab;
+      rem -= ab;
+      prefix |= d << shift;
+      lowbit = shift;
+      if (above + hd <= static_cast<uint32_t>(cap)) break;
+    }
+    // Compact the entries >= floor + prefix to the front, in place: every
+    // thread reads its entries before any is rewritten.
+    const uint32_t fl2 = floor_key + prefix;
+    unsigned long long keep[kListMax / BT];
+#pragma unroll
+    for (int t = 0; t < kListMax / BT; ++t) {
+      const int i = tid + t * BT;
+      keep[t] = i < U ? sh.list[i] : 0ull;
+    }
+    if (tid == 0) sh.nlist = 0;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kListMax / BT; ++t)
+      if (keep[t] != 0ull && cand_key(keep[t]) >= fl2) sh.list[atomicAdd(&sh.nlist, 1)] = keep[t];
+    __syncthreads();
+    C = sh.nlist;
+  }
+  if (C <= BT) {
+    // Rank sort: entry x goes to position #{y > x} (read all, then write).
+    const unsigned long long x = tid < C ? sh.list[tid] : 0ull;
+    int rank = 0;
+    if (tid < C) {
+      int j = 0;
+      for (; j + 4 <= C; j += 4) {
+        rank += (sh.list[j] > x) + (sh.list[j + 1] > x) + (sh.list[j + 2] > x) +
+                (sh.list[j + 3] > x);
+      }
+      for (; j < C; ++j) rank += sh.list[j] > x;
+    }
+    __syncthreads();
+    if (tid < C) sh.list[rank] = x;
+    __syncthreads();
+    return C;
+  }
+  int n2 = 1;
+  while (n2 < C) n2 <<= 1;
+  for (int i = C + tid; i < n2; i += BT) sh.list[i] = 0ull;
+  __syncthreads();
+  lds_bitonic_desc(sh.list, n2);
+  return C;
+}
 
 // force: bit 0 sends every top-p-only row through the probe pass (a
 // diagnostic route; the result is the same).
@@ -486,7 +612,10 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   }
   const ChunkRec* recs = reinterpret_cast<const ChunkRec*>(ws + lay.off_chunk) +
                          static_cast<size_t>(r) * S;
-  for (int c = tid; c < S; c += BT) sh.recs[c] = recs[c];
+  for (int c = tid; c < S; c += BT) {
+    sh.recs[c] = recs[c];
+    sh.nkey[c] = recs[c].nkey;
+  }
   __syncthreads();
   const float inv_t = kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature;
   if (tid == 0) {
@@ -619,15 +748,21 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     }
   }
   __syncthreads();
-  const int U = sh.nlist;
+  int U = sh.nlist;
   if (U > kListMax || U < cand_target(kind, p, V)) {
     if (tid == 0) push_row(&ctr[0], exact_list, r);
     return;
   }
-  const int np2 = next_pow2(U > 0 ? U : 1);
-  for (int i = U + tid; i < np2; i += BT) sh.list[i] = 0ull;
-  __syncthreads();
-  bitonic_sort_desc<BT>(sh.list, np2);
+  // Only a prefix of the sorted list is used: the top N, the top-k set, or
+  // the head of a top-p-only row (64 entries; a boundary further down goes to
+  // the probe pass).  Trim to that prefix plus ties, then sort it.
+  {
+    const int n_eff0 = p.n_logprobs < V ? p.n_logprobs : V;
+    int need = n_eff0 > 1 ? n_eff0 : 1;
+    if (kind == KIND_TOPK && p.top_k > need) need = p.top_k;
+    if (kind == KIND_TOPP && need < 64) need = 64;
+    U = trim_and_sort(sh, U, need < U ? need : U, floor_key);
+  }
   // Top-N log-probabilities.
   const int n_eff = p.n_logprobs < V ? p.n_logprobs : V;
   const int64_t obase = static_cast<int64_t>(r) * a.max_logprobs;
@@ -650,7 +785,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     float gk = -INFINITY;
     int gi = 0x7fffffff;
     for (int c = tid; c < S; c += BT) {
-      if (sh.recs[c].nkey < 1) continue;
+      if (sh.nkey[c] < 1) continue;
       const int id = keys[static_cast<size_t>(c) * kKeyCap];
       const float key = gumbel_key(row[id], m, inv_t, p.seed, grow, id);
       if (better(key, id, gk, gi)) {
@@ -735,7 +870,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       const int kspan = S * kKeyCap;
       for (int g = tid; g < kspan; g += BT) {
         const int c = g / kKeyCap, i = g - c * kKeyCap;
-        if (i >= sh.recs[c].nkey) continue;
+        if (i >= sh.nkey[c]) continue;
         const int id = keys[g];
         const float key = gumbel_key(row[id], m, inv_t, p.seed, grow, id);
         if (key >= kmin) {
@@ -749,10 +884,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
         if (tid == 0) push_row(&ctr[0], exact_list, r);
         return;
       }
-      const int kp2 = next_pow2(nk);
-      for (int i = nk + tid; i < kp2; i += BT) sh.list[i] = 0ull;
-      __syncthreads();
-      bitonic_sort_desc<BT>(sh.list, kp2);
+      trim_and_sort(sh, nk, nk, 0u);
       if (tid == 0) {
         ProbeRec pr;
         pr.z = sh.z;
