@@ -50,7 +50,6 @@ constexpr int BT = 256;
 constexpr int BW = BT / kWave;
 constexpr int PT = 256;
 constexpr int PW = PT / kWave;
-constexpr int PER = kListMax / BT;  // list entries per merge thread
 
 __device__ __forceinline__ float lane(const float4& f, int q) {
   return q == 0 ? f.x : (q == 1 ? f.y : (q == 2 ? f.z : f.w));
@@ -170,18 +169,33 @@ __device__ __forceinline__ void merge_stats(float& m, float& s, float& t, float 
   m = mm;
 }
 
-// The q-th largest (1-based, q <= 64) per-thread value of this wave.
+// The q-th largest (1 <= q <= 64) per-thread value of this wave: the largest
+// order key K with at least q lanes at or above it, built bit by bit from
+// the top with one ballot per bit (no data moves between lanes).
 __device__ __forceinline__ float wave_qth(float x, int q) {
-  return __shfl(wave_sort_desc(x), q - 1, kWave);
+  const uint32_t k = order_key(x);
+  uint32_t K = 0u;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = K | (1u << b);
+    if (__popcll(__ballot(k >= cand)) >= q) K = cand;
+  }
+  return key_to_float(K);
 }
 
-// The q-th largest (q <= 256) of the wave's per-thread top-4 values.
+// The same over the wave's per-thread top-4 values (q <= 256).
 __device__ __forceinline__ float wave_qth4(const float (&t)[4], int q) {
-  float v[4] = {t[0], t[1], t[2], t[3]};
-  wave_sort4_desc(v);
-  const int idx = q - 1, i = idx & 3;
-  const float mine = i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
-  return __shfl(mine, idx >> 2, kWave);
+  const uint32_t k0 = order_key(t[0]), k1 = order_key(t[1]), k2 = order_key(t[2]),
+                 k3 = order_key(t[3]);
+  uint32_t K = 0u;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = K | (1u << b);
+    const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand)) +
+                    __popcll(__ballot(k2 >= cand)) + __popcll(__ballot(k3 >= cand));
+    if (cnt >= q) K = cand;
+  }
+  return key_to_float(K);
 }
 
 // Smallest 23-bit uniform index m = x >> 9 a token needs so that its key
@@ -239,16 +253,38 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   float4 v[AV];
   load_chunk<VEC>(v, row + c0, n, tid);
 
-  // Per-thread largest value (largest four when M > 64).
+  // One pass over the thread's logits in load order, so each float4 is used
+  // as soon as it lands: the thread maximum with sum exp(l - max) (and, for
+  // top-p-only rows, sum exp((l - max) / T)) rescaled whenever the maximum
+  // grows, and the thread's four largest values when M > 64.  A NaN logit
+  // makes the sum NaN; +inf makes it NaN too (inf - inf); a thread holding
+  // only -inf and NaN scans for NaN afterwards.
   const int M = chunk_target(cand_target(kind, p, V), S);
   const bool four = M > 64 && M < n;
   float t[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  if (four) {
+  float lm = -INFINITY, ls = 0.0f, lt = 0.0f;
+  const float sc = inv_t * kLog2e;
 #pragma unroll
-    for (int j = 0; j < AV; ++j)
+  for (int j = 0; j < AV; ++j) {
+    const float4 f = v[j];
+    const float m4 = fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w));
+    if (m4 > lm) {
+      if (lm > -INFINITY) {
+        ls *= fast_exp(lm - m4);
+        if (topp) lt *= __builtin_amdgcn_exp2f((lm - m4) * sc);
+      }
+      lm = m4;
+    }
+    if (lm > -INFINITY) {
+      ls += fast_exp(f.x - lm) + fast_exp(f.y - lm) + fast_exp(f.z - lm) + fast_exp(f.w - lm);
+      if (topp)
+        lt += __builtin_amdgcn_exp2f((f.x - lm) * sc) + __builtin_amdgcn_exp2f((f.y - lm) * sc) +
+              __builtin_amdgcn_exp2f((f.z - lm) * sc) + __builtin_amdgcn_exp2f((f.w - lm) * sc);
+    }
+    if (four) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float x = lane(v[j], q);
+        float x = lane(f, q);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float hi = fmaxf(t[i], x);
@@ -256,30 +292,11 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
           t[i] = hi;
         }
       }
-  } else {
-#pragma unroll
-    for (int j = 0; j < AV; ++j)
-      t[0] = fmaxf(fmaxf(t[0], fmaxf(v[j].x, v[j].y)), fmaxf(v[j].z, v[j].w));
-  }
-
-  // Thread statistics relative to the thread maximum, then one block
-  // reduction of (max, sum exp, sum exp/T).  A NaN logit makes the sum NaN;
-  // +inf makes the maximum infinite; a thread holding only -inf and NaN
-  // scans for NaN.
-  float lm = t[0], ls = 0.0f, lt = 0.0f;
-  int flag = lm == INFINITY ? 1 : 0;
-  if (lm > -INFINITY && lm < INFINITY) {
-    const float sc = inv_t * kLog2e;
-#pragma unroll
-    for (int j = 0; j < AV; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float d = lane(v[j], q) - lm;
-        ls += fast_exp(d);
-        if (topp) lt += __builtin_amdgcn_exp2f(d * sc);
-      }
     }
-  } else if (lm == -INFINITY) {
+  }
+  if (!four) t[0] = lm;
+  int flag = lm == INFINITY ? 1 : 0;
+  if (lm == -INFINITY) {
 #pragma unroll
     for (int j = 0; j < AV; ++j)
       flag |= (isnan(v[j].x) || isnan(v[j].y) || isnan(v[j].z) || isnan(v[j].w)) ? 1 : 0;
@@ -357,9 +374,63 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     }
   }
 
+  __syncthreads();
+  if (tid == 0) {
+    const bool ovf = sh.ncand > kCandCap;
+    ChunkRec o;
+    o.cmax = cmax;
+    o.sumexp = s;
+    o.tmass = tmass;
+    o.kt = order_key(tf);
+    o.ncand = ovf ? 0 : sh.ncand;
+    o.status = ovf ? 2 : 0;
+    o.nkey = 0;  // the noise pass fills the Gumbel-key list
+    o.kfloor = INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o.pad[i] = 0;
+    *rec = o;
+  }
+}
+
+// ------------------------------------------------------------------- N: noise
+// Gumbel keys of full-vocabulary and top-p-only rows, one workgroup per
+// chunk of such a row (the others exit at once); keys are taken relative to
+// the chunk maximum the chunk pass recorded: x = (l - cmax) / T, key = x + g.
+struct NoiseSmem {
+  int klist[kKeyCap];
+  float wthr[AW];
+  float rf[AW];
+  int ri[AW];
+  int nkey;
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(AT) void noise_kernel(SamplerArgs a, FastLayout lay,
+                                                   uint8_t* __restrict__ ws) {
+  __shared__ NoiseSmem sh;
+  const int S = lay.S;
+  const int bid = blockIdx.x;
+  const int r = bid / S, c = bid - r * S;
+  const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
+  const ts_row_params p = a.params[r];
+  const int V = a.vocab;
+  const int kind = row_kind(p, V, a.max_logprobs);
+  if (kind != KIND_FULL && kind != KIND_TOPP) return;
+  ChunkRec* rec = reinterpret_cast<ChunkRec*>(ws + lay.off_chunk) + bid;
+  if (rec->status != 0) return;  // NaN / +inf or candidate overflow: the row goes elsewhere
+  const float cmax = rec->cmax;
+  const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
+  const int c0 = c * lay.L;
+  const int n = min(lay.L, V - c0);
+  const bool topp = kind == KIND_TOPP;
+  const float inv_t = 1.0f / p.temperature;
+  if (tid == 0) sh.nkey = 0;
+  float4 v[AV];
+  load_chunk<VEC>(v, row + c0, n, tid);
+  __syncthreads();
   // Gumbel keys relative to the chunk maximum: x = (l - cmax) / T, key = x + g.
   float kfloor = INFINITY;
-  if (kind == KIND_FULL || topp) {
+  {
     const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
     // Full rows keep each thread's best key; the chunk maximum's key is at
     // least the smallest Gumbel value, so no token below that bar needs its
@@ -427,19 +498,10 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   }
   __syncthreads();
   if (tid == 0) {
-    const bool ovf = sh.ncand > kCandCap, key_ovf = sh.nkey > kKeyCap;
-    ChunkRec o;
-    o.cmax = cmax;
-    o.sumexp = s;
-    o.tmass = tmass;
-    o.kt = order_key(tf);
-    o.ncand = ovf ? 0 : sh.ncand;
-    o.status = (ovf || key_ovf) ? 2 : 0;
-    o.nkey = key_ovf ? 0 : sh.nkey;
-    o.kfloor = kfloor;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o.pad[i] = 0;
-    *rec = o;
+    const bool key_ovf = sh.nkey > kKeyCap;
+    rec->nkey = key_ovf ? 0 : sh.nkey;
+    rec->kfloor = kfloor;
+    if (key_ovf) rec->status = 2;
   }
 }
 
@@ -449,17 +511,21 @@ constexpr int kUnionMax = 1 << 20;  // candidates a merge workgroup walks
 struct MergeSmem {
   unsigned long long list[kListMax];
   union {
-    ChunkRec recs[kMaxChunks];  // read once at the start of the merge
-    uint32_t hist[RB];          // radix bins, used afterwards
+    ChunkRec recs[kMaxChunks];     // read once at the start of the merge
+    uint32_t hist[RB];             // radix bins (counts), used afterwards
+    unsigned long long mhist[RB];  // radix bins (fixed-point mass)
   };
   int nkey[kMaxChunks];         // the chunks' Gumbel-key list lengths
   int pos[kMaxChunks + 1];
+  unsigned long long uscan[BW];
   double dscan[BW];
+  unsigned long long sel_above64;
+  int sel_found;
   float rf[BW];
   int ri[BW];
   uint32_t ru[BW];
   uint32_t sel_d, sel_above, rmax;
-  int nlist, jstar, status, total;
+  int nlist, status, total;
   float m, lse, kmin;
   uint32_t floor_key;
   double z;
@@ -501,6 +567,102 @@ __device__ void lds_bitonic_desc(unsigned long long* s, int n) {
       __syncthreads();
     }
   }
+}
+
+__device__ __forceinline__ int digit_shift(int rd) { return rd == 0 ? 21 : (rd == 1 ? 10 : 0); }
+__device__ __forceinline__ int digit_width(int rd) { return rd == 2 ? 10 : 11; }
+
+// Order key of the k-th largest entry of sh.list[0, U) (1 <= k <= U): radix
+// selection over the 32-bit key, 11/11/10-bit digits.
+__device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u, pmask = 0u, rem = static_cast<uint32_t>(k);
+  for (int rd = 0; rd < 3; ++rd) {
+    const int shift = digit_shift(rd), width = digit_width(rd);
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int b = tid; b < RB; b += BT) sh.hist[b] = 0u;
+    __syncthreads();
+    for (int i = tid; i < U; i += BT) {
+      const uint32_t key = cand_key(sh.list[i]);
+      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+    }
+    __syncthreads();
+    select_digit_top<BT, RB / BT>(sh.hist, 1 << width, rem, sh.ru, &sh.sel_d, &sh.sel_above);
+    const uint32_t d = sh.sel_d, ab = sh.sel_above;
+    __syncthreads();
+    rem -= ab;
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+  }
+  return prefix;
+}
+
+// Fixed-point (2^-40) temperature-scaled weight exp((l - m) / T) of a listed
+// logit, l <= m.
+__device__ __forceinline__ unsigned long long list_mass(uint32_t key, float m, float inv_t) {
+  return fixed_mass(fast_exp((key_to_float(key) - m) * inv_t));
+}
+
+// Top-p boundary among the entries of sh.list[0, U) with key >= kmin: the
+// largest key t whose entries at or above it carry mass >= target (fixed
+// point), i.e. the key of the first sorted position where the cumulative
+// mass reaches the target.  Radix selection with mass-weighted bins, from
+// the top digit down.  *found = 0 if the eligible entries' whole mass stays
+// below the target.
+__device__ uint32_t list_mass_key(MergeSmem& sh, int U, uint32_t kmin, float m, float inv_t,
+                                  double target, int* found) {
+  constexpr int BPT = RB / BT;
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u, pmask = 0u;
+  double rem = target;
+  for (int rd = 0; rd < 3; ++rd) {
+    const int shift = digit_shift(rd), width = digit_width(rd);
+    const uint32_t dmask = (1u << width) - 1u;
+    const int nb = 1 << width;
+    for (int b = tid; b < RB; b += BT) sh.mhist[b] = 0ull;
+    if (tid == 0) sh.sel_found = 0;
+    __syncthreads();
+    for (int i = tid; i < U; i += BT) {
+      const uint32_t key = cand_key(sh.list[i]);
+      if (key >= kmin && (key & pmask) == prefix)
+        atomicAdd(&sh.mhist[(key >> shift) & dmask], list_mass(key, m, inv_t));
+    }
+    __syncthreads();
+    // Bins from the top digit down, BPT per thread: find d with
+    // above(d) < rem <= above(d) + mass(d).
+    unsigned long long h[BPT];
+    unsigned long long mine = 0ull;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int b = nb - 1 - (tid * BPT + j);
+      h[j] = b >= 0 ? sh.mhist[b] : 0ull;
+      mine += h[j];
+    }
+    unsigned long long tot;
+    unsigned long long ex = block_exclusive_scan<BT, unsigned long long>(mine, sh.uscan, tot);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int b = nb - 1 - (tid * BPT + j);
+      if (b >= 0 && static_cast<double>(ex) < rem && rem <= static_cast<double>(ex + h[j])) {
+        sh.sel_d = static_cast<uint32_t>(b);
+        sh.sel_above64 = ex;
+        sh.sel_found = 1;
+      }
+      ex += h[j];
+    }
+    __syncthreads();
+    if (!sh.sel_found) {
+      *found = 0;
+      return 0u;
+    }
+    const uint32_t d = sh.sel_d;
+    rem -= static_cast<double>(sh.sel_above64);
+    __syncthreads();
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+  }
+  *found = 1;
+  return prefix;
 }
 
 // Keeps the entries of sh.list[0, U) (all with key >= floor_key) that are at
@@ -753,32 +915,24 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     if (tid == 0) push_row(&ctr[0], exact_list, r);
     return;
   }
-  // Only a prefix of the sorted list is used: the top N, the top-k set, or
-  // the head of a top-p-only row (64 entries; a boundary further down goes to
-  // the probe pass).  Trim to that prefix plus ties, then sort it.
-  {
-    const int n_eff0 = p.n_logprobs < V ? p.n_logprobs : V;
-    int need = n_eff0 > 1 ? n_eff0 : 1;
-    if (kind == KIND_TOPK && p.top_k > need) need = p.top_k;
-    if (kind == KIND_TOPP && need < 64) need = 64;
-    U = trim_and_sort(sh, U, need < U ? need : U, floor_key);
-  }
-  // Top-N log-probabilities.
+  // Most rows use a short prefix of the list: the top N, a top-k set of at
+  // most 192, or the 64-entry head of a top-p-only row (its boundary further
+  // down goes to the probe pass).  Those lists are trimmed to the prefix and
+  // sorted, and the top-p boundary is a prefix sum over them.  Longer top-k
+  // sets stay unsorted: the k-th key and the top-p boundary are found by
+  // count- and mass-weighted radix selection.
   const int n_eff = p.n_logprobs < V ? p.n_logprobs : V;
-  const int64_t obase = static_cast<int64_t>(r) * a.max_logprobs;
-  for (int j = tid; j < a.max_logprobs; j += BT) {
-    if (j < n_eff) {
-      const unsigned long long e = sh.list[j];
-      a.topn_ids[obase + j] = cand_id(e);
-      a.topn_logprobs[obase + j] = key_to_float(cand_key(e)) - lse;
-    } else {
-      a.topn_ids[obase + j] = -1;
-      a.topn_logprobs[obase + j] = -INFINITY;
-    }
-  }
-
   const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
-  int token = cand_id(sh.list[0]);  // greedy: the largest logit, lowest id
+  int need = n_eff > 1 ? n_eff : 1;
+  if (kind == KIND_TOPK && p.top_k > need) need = p.top_k;
+  if (kind == KIND_TOPP && need < 64) need = 64;
+  bool sorted = need <= 192;
+  if (sorted) {
+    U = trim_and_sort(sh, U, need < U ? need : U, floor_key);
+    sorted = U <= BT;  // long tie runs keep more: those rows take the selection path
+  }
+  int token = -1;
+  bool probe = false;
   if (kind == KIND_FULL) {
     const int* keys = reinterpret_cast<const int*>(ws + lay.off_key) +
                       static_cast<size_t>(r) * S * kKeyCap;
@@ -795,59 +949,83 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     }
     block_best<BT>(gk, gi, sh.rf, sh.ri);
     token = gi;
-  } else if (kind == KIND_TOPK || kind == KIND_TOPP) {
-    // Top-k set: the sorted prefix down to the k-th largest (ties kept).
-    int nK = U;
-    if (kind == KIND_TOPK) {
-      const uint32_t tk = cand_key(sh.list[p.top_k - 1]);
-      int cK = 0;
-      for (int i = tid; i < U; i += BT) cK += cand_key(sh.list[i]) >= tk ? 1 : 0;
-      nK = block_sum<BT, int>(cK, sh.ri);
-    }
-    int nP = nK;
-    bool probe = false;
+  } else if (sorted && (kind == KIND_TOPK || kind == KIND_TOPP)) {
+    // U <= 256 sorted entries, entry i with thread i.
+    const uint32_t kmin = kind == KIND_TOPK ? cand_key(sh.list[p.top_k - 1]) : 0u;
+    uint32_t kept = kmin;
+    const unsigned long long mine = tid < U ? sh.list[tid] : 0ull;
     if (p.top_p < 1.0f) {
-      // Mass prefix over the sorted set, PER consecutive entries per thread.
-      double local = 0.0;
-      double wv[PER];
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int i = tid * PER + j;
-        wv[j] = i < nK ? static_cast<double>(
-                             fast_exp((key_to_float(cand_key(sh.list[i])) - m) * inv_t))
-                       : 0.0;
-        local += wv[j];
-      }
+      const double w = (tid < U && cand_key(mine) >= kmin)
+                           ? static_cast<double>(fast_exp((key_to_float(cand_key(mine)) - m) * inv_t))
+                           : 0.0;
       double total;
-      const double ex = block_exclusive_scan<BT, double>(local, sh.dscan, total);
-      if (tid == 0) {
-        if (kind == KIND_TOPK) sh.z = total;
-        sh.jstar = 0x7fffffff;
+      const double ex = block_exclusive_scan<BT, double>(w, sh.dscan, total);
+      const double target = static_cast<double>(p.top_p) * (kind == KIND_TOPK ? total : sh.z);
+      if (tid == 0) sh.sel_found = 0;
+      __syncthreads();
+      if (w > 0.0 && ex < target && target <= ex + w) {
+        sh.sel_d = cand_key(mine);  // the boundary's key: first cumulative mass >= target
+        sh.sel_found = 1;
       }
       __syncthreads();
-      const double target = static_cast<double>(p.top_p) * sh.z;
-      double cum = ex;
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const int i = tid * PER + j;
-        cum += wv[j];
-        if (i < nK && cum >= target) atomicMin(&sh.jstar, i);
-      }
-      __syncthreads();
-      if (sh.jstar == 0x7fffffff || (kind == KIND_TOPP && (force & 1))) {
+      if (!sh.sel_found || (kind == KIND_TOPP && (force & 1))) {
+        if (kind == KIND_TOPK && !sh.sel_found) {  // cannot happen: the top-k set is all listed
+          if (tid == 0) push_row(&ctr[0], exact_list, r);
+          return;
+        }
         probe = true;
       } else {
-        const uint32_t tp = cand_key(sh.list[sh.jstar]);
-        int cP = 0;
-        for (int i = tid; i < nK; i += BT) cP += cand_key(sh.list[i]) >= tp ? 1 : 0;
-        nP = block_sum<BT, int>(cP, sh.ri);
+        kept = sh.sel_d > kmin ? sh.sel_d : kmin;
       }
     }
     if (!probe) {
       float gk = -INFINITY;
       int gi = 0x7fffffff;
-      for (int i = tid; i < nP; i += BT) {
+      if (tid < U && cand_key(mine) >= kept) {
+        gi = cand_id(mine);
+        gk = gumbel_key(key_to_float(cand_key(mine)), m, inv_t, p.seed, grow, gi);
+      }
+      block_best<BT>(gk, gi, sh.rf, sh.ri);
+      token = gi;
+    }
+  } else if (kind == KIND_TOPK || kind == KIND_TOPP) {
+    const uint32_t kmin = kind == KIND_TOPK ? list_kth_key(sh, U, p.top_k) : 0u;
+    uint32_t kept = kmin;
+    if (p.top_p < 1.0f) {
+      double target;
+      if (kind == KIND_TOPK) {
+        unsigned long long mine = 0ull;
+        for (int i = tid; i < U; i += BT) {
+          const uint32_t key = cand_key(sh.list[i]);
+          if (key >= kmin) mine += list_mass(key, m, inv_t);
+        }
+        target = static_cast<double>(p.top_p) *
+                 static_cast<double>(block_sum<BT, unsigned long long>(mine, sh.uscan));
+      } else {
+        target = static_cast<double>(p.top_p) * sh.z * static_cast<double>(kMassScale);
+      }
+      if (kind == KIND_TOPP && (force & 1)) {
+        probe = true;
+      } else {
+        int found = 0;
+        const uint32_t tp = list_mass_key(sh, U, kmin, m, inv_t, target, &found);
+        if (!found) {
+          if (kind == KIND_TOPK) {  // cannot happen: the top-k set is all listed
+            if (tid == 0) push_row(&ctr[0], exact_list, r);
+            return;
+          }
+          probe = true;
+        } else {
+          kept = tp > kmin ? tp : kmin;
+        }
+      }
+    }
+    if (!probe) {
+      float gk = -INFINITY;
+      int gi = 0x7fffffff;
+      for (int i = tid; i < U; i += BT) {
         const unsigned long long e = sh.list[i];
+        if (cand_key(e) < kept) continue;
         const int id = cand_id(e);
         const float key = gumbel_key(key_to_float(cand_key(e)), m, inv_t, p.seed, grow, id);
         if (better(key, id, gk, gi)) {
@@ -857,51 +1035,71 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       }
       block_best<BT>(gk, gi, sh.rf, sh.ri);
       token = gi;
+    }
+  }
+
+  // Top-N log-probabilities (and the greedy token): the n_eff largest, sorted.
+  if (!sorted && need > 192) {
+    const int nt = n_eff > 1 ? n_eff : 1;
+    trim_and_sort(sh, U, nt < U ? nt : U, floor_key);
+  }
+  const int64_t obase = static_cast<int64_t>(r) * a.max_logprobs;
+  for (int j = tid; j < a.max_logprobs; j += BT) {
+    if (j < n_eff) {
+      const unsigned long long e = sh.list[j];
+      a.topn_ids[obase + j] = cand_id(e);
+      a.topn_logprobs[obase + j] = key_to_float(cand_key(e)) - lse;
     } else {
-      // Top-p-only row whose boundary lies below the listed logits: the
-      // chunks' key candidates, complete above the highest chunk floor,
-      // sorted by row key; the best few become probes.
-      const int* keys = reinterpret_cast<const int*>(ws + lay.off_key) +
-                        static_cast<size_t>(r) * S * kKeyCap;
-      const float kmin = sh.kmin;
-      __syncthreads();
-      if (tid == 0) sh.nlist = 0;
-      __syncthreads();
-      const int kspan = S * kKeyCap;
-      for (int g = tid; g < kspan; g += BT) {
-        const int c = g / kKeyCap, i = g - c * kKeyCap;
-        if (i >= sh.nkey[c]) continue;
-        const int id = keys[g];
-        const float key = gumbel_key(row[id], m, inv_t, p.seed, grow, id);
-        if (key >= kmin) {
-          const int slot = atomicAdd(&sh.nlist, 1);
-          if (slot < kListMax) sh.list[slot] = pack_cand(order_key(key), id);
-        }
+      a.topn_ids[obase + j] = -1;
+      a.topn_logprobs[obase + j] = -INFINITY;
+    }
+  }
+  if (kind == KIND_GREEDY) token = cand_id(sh.list[0]);  // largest logit, lowest id
+
+  if (probe) {
+    // Top-p-only row whose boundary lies below the listed logits: the
+    // chunks' key candidates, complete above the highest chunk floor,
+    // sorted by row key; the best few become probes.
+    const int* keys = reinterpret_cast<const int*>(ws + lay.off_key) +
+                      static_cast<size_t>(r) * S * kKeyCap;
+    const float kmin = sh.kmin;
+    __syncthreads();
+    if (tid == 0) sh.nlist = 0;
+    __syncthreads();
+    const int kspan = S * kKeyCap;
+    for (int g = tid; g < kspan; g += BT) {
+      const int c = g / kKeyCap, i = g - c * kKeyCap;
+      if (i >= sh.nkey[c]) continue;
+      const int id = keys[g];
+      const float key = gumbel_key(row[id], m, inv_t, p.seed, grow, id);
+      if (key >= kmin) {
+        const int slot = atomicAdd(&sh.nlist, 1);
+        if (slot < kListMax) sh.list[slot] = pack_cand(order_key(key), id);
       }
-      __syncthreads();
-      const int nk = sh.nlist;
-      if (nk == 0 || nk > kListMax) {
-        if (tid == 0) push_row(&ctr[0], exact_list, r);
-        return;
-      }
-      trim_and_sort(sh, nk, nk, 0u);
-      if (tid == 0) {
-        ProbeRec pr;
-        pr.z = sh.z;
-        pr.m = m;
-        pr.lse = lse;
-        pr.inv_t = inv_t;
-        pr.npts = nk < kProbes ? nk : kProbes;
-        for (int i = 0; i < kProbes; ++i) {
-          const int id = i < pr.npts ? cand_id(sh.list[i]) : 0;
-          pr.id[i] = id;
-          pr.pt[i] = i < pr.npts ? row[id] : INFINITY;
-        }
-        reinterpret_cast<ProbeRec*>(ws + lay.off_prec)[r] = pr;
-        push_row(&ctr[1], probe_list, r);
-      }
+    }
+    __syncthreads();
+    const int nk = sh.nlist;
+    if (nk == 0 || nk > kListMax) {
+      if (tid == 0) push_row(&ctr[0], exact_list, r);
       return;
     }
+    trim_and_sort(sh, nk, nk, 0u);
+    if (tid == 0) {
+      ProbeRec pr;
+      pr.z = sh.z;
+      pr.m = m;
+      pr.lse = lse;
+      pr.inv_t = inv_t;
+      pr.npts = nk < kProbes ? nk : kProbes;
+      for (int i = 0; i < kProbes; ++i) {
+        const int id = i < pr.npts ? cand_id(sh.list[i]) : 0;
+        pr.id[i] = id;
+        pr.pt[i] = i < pr.npts ? row[id] : INFINITY;
+      }
+      reinterpret_cast<ProbeRec*>(ws + lay.off_prec)[r] = pr;
+      push_row(&ctr[1], probe_list, r);
+    }
+    return;
   }
   if (tid == 0) {
     a.token_ids[r] = token;
@@ -995,6 +1193,12 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
   else
     hipLaunchKernelGGL(chunk_pass_kernel<false>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (vec)
+    hipLaunchKernelGGL(noise_kernel<true>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
+  else
+    hipLaunchKernelGGL(noise_kernel<false>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int force = env_flag("TS_SAMPLER_FORCE_PROBE") ? 1 : 0;
   hipLaunchKernelGGL(merge_kernel, dim3(a.rows), dim3(BT), 0, stream, a, lay, ws, force);
