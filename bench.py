@@ -84,7 +84,7 @@ def recorded_traffic(workload: str):
 
     if workload != "spec_decode":
         return None
-    path = os.path.join(ROOT, "profiles", "spec_decode_step_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", "spec_decode_step_hbm_traffic.txt")
     src = os.path.join(ROOT, "top_sampling_amd", "csrc", "lmhead_gemm.hip")
     try:
         text = open(path).read()
