@@ -9,6 +9,9 @@ A step is one pass of the whole hot path over one batch of synthetic input:
      batch buffer [rows, V] (receive side of the all-to-all);
   3. sampler_sample: temperature / top-k / top-p / log-probabilities /
      Gumbel-max sampling of every row.
+After the timed steps, sampler_sample_slices (the sampler reading the slices
+in place, with no stitching copy) is timed on its own over the same number of
+steps and reported beside the per-kernel times.
 Default workload: speculative decode, 128 requests x (4 draft + 1) = 640 rows,
 H = 4096, V = 151,936 (4 slices of 37,984).
 
@@ -166,6 +169,27 @@ def main():
     asm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     smp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
 
+    # The same slices sampled in place (no stitching copy), timed on its own.
+    ws_sl = torch.empty(max(256, ts.sampler_workspace_bytes_slices(rows, widths, w.max_logprobs)),
+                        dtype=torch.uint8, device=dev)
+    out_sl = ts.allocate_sample_output(rows, w.max_logprobs, dev)
+
+    def sample_slices():
+        ts.sampler_sample_slices(slices, params, 0, w.max_logprobs, out=out_sl, workspace=ws_sl,
+                                 stream=stream)
+
+    for _ in range(max(1, args.warmup)):
+        sample_slices()
+    ev_sl = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for a, b in ev_sl:
+        a.record(stream)
+        sample_slices()
+        b.record(stream)
+    torch.cuda.synchronize()
+    sl_ms = sum(a.elapsed_time(b) for a, b in ev_sl) / args.steps
+    n_diff = int((out_sl.token_ids != out.token_ids).sum())
+
     flops = 2.0 * rows * vocab * w.hidden if w.hidden else 0.0
     sampler_bytes = 4.0 * rows * vocab + rows * (24 + 12 + 8 * w.max_logprobs)
     asm_bytes = 2 * 4.0 * rows * vocab
@@ -206,6 +230,10 @@ def main():
             "sampler": {"ms": round(smp_ms, 4), "gbs": round(smp_gbs, 1),
                         "frac_hbm_peak": round(smp_gbs / HBM_PEAK_GBS, 4),
                         "rows_per_s": round(rows / (smp_ms * 1e-3), 1)},
+            "sampler_slices": {"ms": round(sl_ms, 4), "gbs": round(sampler_bytes / (sl_ms * 1e-3) / 1e9, 1),
+                               "frac_hbm_peak": round(sampler_bytes / (sl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "saves_ms_vs_assemble_then_sample": round(asm_ms + smp_ms - sl_ms, 4),
+                               "token_ids_differing_from_stitched": n_diff},
         },
         "roofline": roof,
     }

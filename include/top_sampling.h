@@ -150,6 +150,38 @@ int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_
                    size_t workspace_bytes, void* stream);
 
 /*
+ * sampler_workspace_bytes_slices: device workspace sampler_sample_slices
+ * needs (host-only computation).  slice_cols is a HOST array of n_slices
+ * entries.
+ */
+size_t sampler_workspace_bytes_slices(int64_t rows, const int64_t* slice_cols, int32_t n_slices,
+                                      int32_t max_logprobs);
+
+/*
+ * sampler_sample_slices: sampler_sample over a rank's batch slice that is
+ * still held as the vocabulary slices the exchange delivered, without
+ * stitching them into one buffer first (the step after the all-to-all on
+ * the page "Qwen4Exp batch-sharded sampling: inside vLLM PR #61018", section
+ * "What batch-sharded sampling is, in one paragraph": each rank receives the
+ * vocabulary slices of its requests).  Global column off_s + c of row r is
+ * slices[s][r * slice_ld[s] + c], off_s = slice_cols[0] + ... +
+ * slice_cols[s-1]; vocab = the sum of slice_cols.
+ *   slices      HOST array of n_slices DEVICE pointers (fp32, read only)
+ *   slice_cols, slice_ld   HOST arrays of n_slices entries
+ * Every other argument, output and the results are those of sampler_sample
+ * on the stitched [rows, vocab] buffer; the workspace is sized by
+ * sampler_workspace_bytes_slices.  1 <= n_slices <= TS_MAX_SLICES.  Slices
+ * that start at a column not a multiple of 4 take the exact per-row kernel
+ * (same results, slower).
+ */
+int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
+                          const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                          const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                          int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                          float* topn_logprobs, int32_t* row_status, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * sampler_assemble_vocab_slices: out[r, off_s + c] = slice_s[r, c] with
  * off_s = slice_cols[0] + ... + slice_cols[s-1].
  *   slices      HOST array of n_slices DEVICE pointers, slice s fp32

@@ -172,3 +172,48 @@ def test_params_layout_roundtrip():
     assert raw.shape[0] == 24 * p.shape[0]
     back = raw.view(workloads.PARAMS_DTYPE)
     assert np.array_equal(back["seed"], p["seed"])
+
+
+def _sample_slices(ptrs, cols, lds, **kw):
+    a = dict(rows=8, params=FAKE, row_offset=0, max_logprobs=5, tok=FAKE, tlp=FAKE, tid=FAKE,
+             tnlp=FAKE, status=FAKE, ws=None, ws_bytes=0)
+    a.update(kw)
+    n = len(ptrs)
+    P = (ctypes.c_void_p * max(n, 1))(*ptrs)
+    C = (ctypes.c_int64 * max(n, 1))(*cols)
+    L = (ctypes.c_int64 * max(n, 1))(*lds)
+    return ts.lib.sampler_sample_slices(P, C, L, a.get("n", n), a["rows"], a["params"],
+                                        a["row_offset"], a["max_logprobs"], a["tok"], a["tlp"],
+                                        a["tid"], a["tnlp"], a["status"], a["ws"], a["ws_bytes"],
+                                        None)
+
+
+def test_sampler_slices_validation():
+    two = ([FAKE, FAKE * 2], [40, 60], [40, 60])
+    assert _sample_slices([], [], []) == ts.TS_EINVAL
+    assert _sample_slices([FAKE] * 65, [4] * 65, [4] * 65) == ts.TS_EUNSUPPORTED
+    assert _sample_slices([FAKE, FAKE * 2], [40, -1], [40, 4]) == ts.TS_EINVAL
+    assert _sample_slices([FAKE, FAKE * 2], [40, 60], [40, 59]) == ts.TS_EINVAL   # ld < width
+    assert _sample_slices([FAKE, None], [40, 60], [40, 60]) == ts.TS_EINVAL       # NULL slice
+    assert _sample_slices([FAKE, FAKE + 2], [40, 60], [40, 60]) == ts.TS_EUNSUPPORTED
+    assert _sample_slices([FAKE, FAKE * 2], [0, 0], [0, 0]) == ts.TS_EINVAL       # vocab 0
+    assert _sample_slices(*two, rows=-1) == ts.TS_EINVAL
+    assert _sample_slices(*two, max_logprobs=-1) == ts.TS_EINVAL
+    assert _sample_slices(*two, row_offset=-1) == ts.TS_EINVAL
+    assert _sample_slices(*two, params=None) == ts.TS_EINVAL
+    assert _sample_slices(*two) == ts.TS_EWORKSPACE
+    assert _sample_slices(*two, ws=FAKE, ws_bytes=255) == ts.TS_EWORKSPACE
+    # An empty slice may be NULL; rows == 0 is a no-op.
+    assert _sample_slices([FAKE, None, FAKE * 2], [40, 0, 60], [40, 0, 60]) == ts.TS_EWORKSPACE
+    assert _sample_slices(*two, rows=0, params=None, tok=None) == ts.TS_OK
+
+
+def test_slices_workspace_query():
+    V = 151936
+    assert ts.sampler_workspace_bytes_slices(640, [V], 20) == ts.sampler_workspace_bytes(640, V, 20)
+    four = ts.sampler_workspace_bytes_slices(640, [V // 4] * 4, 20)
+    assert four >= ts.sampler_workspace_bytes(640, V, 20)
+    assert ts.sampler_workspace_bytes_slices(640, [V // 64] * 64, 20) > 0
+    assert ts.sampler_workspace_bytes_slices(640, [], 20) == 0
+    assert ts.sampler_workspace_bytes_slices(640, [10, -1], 20) == 0
+    assert ts.sampler_workspace_bytes_slices(640, [4] * 65, 20) == 0

@@ -434,3 +434,133 @@ def test_gumbel_noise_on_flat_rows(dev, ts, route):
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
              res.row_status, res.flagged, lse, logits, max_frac=1.0, label="flat")
     assert res.flagged.sum() <= 1
+
+
+# ------------------------------------------------ sampler over vocab slices
+def _run_sampler_slices(ts, dev, logits_np, widths, params, row_offset, max_logprobs, ld_extra=0):
+    """sampler_sample_slices over ``logits_np`` cut column-wise into ``widths``
+    (each slice its own buffer; with ld_extra, a NaN-padded wider buffer)."""
+    import torch
+
+    rows, vocab = logits_np.shape
+    assert sum(widths) == vocab
+    cuts = np.concatenate([[0], np.cumsum(widths)]).astype(np.int64)
+    full = torch.from_numpy(np.ascontiguousarray(logits_np)).to(dev)
+    slices = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        if ld_extra:
+            buf = torch.full((rows, b - a + ld_extra), float("nan"), device=dev)
+            buf[:, :b - a] = full[:, a:b]
+            slices.append(buf[:, :b - a])
+        else:
+            slices.append(full[:, a:b].contiguous())
+    del full
+    p = ts.params_to_device(params, dev)
+    out = ts.sampler_sample_slices(slices, p, row_offset=row_offset, max_logprobs=max_logprobs)
+    torch.cuda.synchronize()
+    return {k: getattr(out, k).cpu().numpy() for k in
+            ("token_ids", "token_logprobs", "topn_ids", "topn_logprobs", "row_status")}
+
+
+def _even_widths(V, n, align=1):
+    base = V // n // align * align
+    w = [base] * n
+    w[-1] += V - base * n
+    return w
+
+
+@pytest.mark.parametrize("name,n", [("spec_decode", 4), ("spec_decode", 8), ("rank_share", 0),
+                                    ("large", 8)])
+def test_sampler_slices_workloads(dev, ts, name, n, route):
+    """The receive side without the stitching copy: the sampler reads the
+    vocabulary slices where the exchange left them."""
+    w = workloads.get(name)
+    exp = _load_expected(name)
+    params = workloads.make_params(w)
+    logits = workloads.make_logits(w)
+    widths = list(w.slice_cols) if n == 0 else _even_widths(w.vocab, n)
+    say("sampler slices", name, widths, route)
+    got = _run_sampler_slices(ts, dev, logits, widths, params, 0, w.max_logprobs)
+    flagged = exp["flag_top_p"] | exp["flag_tie"]
+    mism = _compare(got, exp["token_ids"], exp["token_logprobs"], exp["topn_ids"],
+                    exp["topn_logprobs"], exp["row_status"], flagged, exp["lse"], logits,
+                    label=f"{name}/slices")
+    say(f"{name}/slices/{route}: flagged={int(flagged.sum())} mismatched_flagged={mism}")
+
+
+SLICE_LAYOUTS = {
+    "one": lambda V: [V],
+    "aligned4": lambda V: _even_widths(V, 4, align=4),
+    "ragged_tail": lambda V: [4, 1236] + _even_widths(V - 1240, 2, align=4),
+    "misaligned": lambda V: [V // 3 + 1, V // 3 - 2, V - 2 * (V // 3) + 1],
+    "empties": lambda V: [0, V // 2 // 4 * 4, 0, V - V // 2 // 4 * 4, 0],
+    "many64": lambda V: _even_widths(V, 64, align=4),
+    "many64_odd": lambda V: [469] * 63 + [V - 469 * 63],
+}
+
+
+@pytest.mark.parametrize("layout", list(SLICE_LAYOUTS))
+@pytest.mark.parametrize("kind", ["normal", "neginf", "ints"])
+def test_sampler_slices_layouts(dev, ts, layout, kind, route):
+    rng = np.random.default_rng(len(layout) * 7 + len(kind))
+    rows = 20
+    V = 30011 if layout in ("ragged_tail", "misaligned", "many64_odd") else 30008
+    logits = _edge_case(rng, V, rows, kind)
+    params = workloads.random_params(rng, rows, V, 9)
+    widths = SLICE_LAYOUTS[layout](V)
+    say("sampler slice layout", layout, kind, route, widths[:6])
+    ld_extra = {"normal": 0, "neginf": 4, "ints": 5}[kind]
+    got = _run_sampler_slices(ts, dev, logits, widths, params, 11, 9, ld_extra=ld_extra)
+    res, lse = _oracle_ref(logits, params, 11, 9)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=f"{layout}/{kind}")
+
+
+@pytest.mark.parametrize("V,widths", [(1, [1]), (3, [1, 1, 1]), (7, [0, 4, 3]), (9, [4, 4, 1]),
+                                      (1000, [1000, 0])])
+def test_sampler_slices_tiny(dev, ts, V, widths, route):
+    rng = np.random.default_rng(V)
+    rows = 10
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    params = workloads.random_params(rng, rows, V, 3)
+    say("sampler slices tiny", V, widths, route)
+    got = _run_sampler_slices(ts, dev, logits, widths, params, 0, 3)
+    res, lse = _oracle_ref(logits, params, 0, 3)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=f"tiny{V}")
+
+
+@pytest.mark.parametrize("layout", ["crowded", "spread"])
+def test_sampler_slices_large_targets(dev, ts, layout, route):
+    """Large top-k / top-N with the heavy stretch of the row inside one slice
+    or across a slice boundary."""
+    rng = np.random.default_rng(21 if layout == "crowded" else 22)
+    rows, V, max_lp = 8, 70000, 300
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    if layout == "crowded":
+        for r in range(rows):
+            start = 17500 * (r % 4) - 1500 if r % 4 else 100
+            logits[r, start:start + 3000] += 6.0
+    params = workloads.random_params(rng, rows, V, max_lp)
+    params["top_k"] = np.array([1000, 300, 65, 1024, 0, 1000, 200, 700], dtype=np.int32)
+    params["n_logprobs"] = np.array([300, 0, 300, 5, 300, 100, 65, 299], dtype=np.int32)
+    params["temperature"][:] = 0.9
+    say("sampler slices large targets", layout, route)
+    got = _run_sampler_slices(ts, dev, logits, [17500] * 4, params, 3, max_lp)
+    res, lse = _oracle_ref(logits, params, 3, max_lp)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=layout)
+
+
+def test_sampler_one_slice_matches_buffer_call(dev, ts):
+    """One slice is the stitched buffer itself: same chunking, so the two
+    calls agree bit for bit."""
+    rng = np.random.default_rng(31)
+    rows, V = 48, 40000
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    params = workloads.random_params(rng, rows, V, 6)
+    say("sampler one slice vs buffer")
+    a = _run_sampler(ts, dev, logits, params, 7, 6)
+    b = _run_sampler_slices(ts, dev, logits, [V], params, 7, 6)
+    for k in a:
+        assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k

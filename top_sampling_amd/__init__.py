@@ -10,7 +10,9 @@ Calls mirror the C entry points:
   sampler_assemble_vocab_slices  stitch received vocabulary slices
   sampler_sample                 per-row temperature / top-k / top-p /
                                  logprobs / Gumbel-max sampling
-  sampler_workspace_bytes        workspace size query
+  sampler_sample_slices          the same, reading the received vocabulary
+                                 slices in place (no stitched buffer)
+  sampler_workspace_bytes(_slices)  workspace size queries
 and ``compute_logits_local`` returns the rank's own ``[rows, V_local]`` slice,
 the local-logits hook of batch-sharded sampling (page "Qwen4Exp batch-sharded
 sampling: inside vLLM PR #61018", section "Why three lines were the whole
@@ -40,6 +42,9 @@ SYMBOLS = {
     "sampler_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "sampler_sample": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _I32, _VP, _VP, _VP, _VP,
                                       _VP, _VP, _SZ, _VP]),
+    "sampler_workspace_bytes_slices": (_SZ, [_I64, _VP, _I32, _I32]),
+    "sampler_sample_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _I32, _VP, _VP,
+                                             _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sampler_assemble_vocab_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _VP]),
     "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ts_last_error": (ctypes.c_char_p, []),
@@ -136,21 +141,12 @@ def compute_logits_local(hidden, lm_head, out=None, stream=None):
 def sampler_assemble_vocab_slices(slices, out=None, stream=None):
     """``out[:, off_s:off_s+cols_s] = slices[s]`` (bit-exact)."""
     torch = _torch()
-    n = len(slices)
-    if n < 1:
-        raise ValueError("need at least one slice")
-    rows = slices[0].shape[0]
-    for s in slices:
-        if s.dtype != torch.float32 or s.dim() != 2 or s.shape[0] != rows or s.stride(1) != 1:
-            raise ValueError("slices must be fp32 [rows, cols_s] with unit column stride")
+    n, rows, ptrs, cols, lds = _slice_arrays(slices)
     total = sum(int(s.shape[1]) for s in slices)
     if out is None:
         out = torch.empty(rows, total, dtype=torch.float32, device=slices[0].device)
     if out.shape != (rows, total) or out.stride(1) != 1 or out.dtype != torch.float32:
         raise ValueError("out must be fp32 [rows, sum cols] with unit column stride")
-    ptrs = (ctypes.c_void_p * n)(*[_ptr(s) for s in slices])
-    cols = (ctypes.c_int64 * n)(*[int(s.shape[1]) for s in slices])
-    lds = (ctypes.c_int64 * n)(*[int(s.stride(0)) for s in slices])
     _check(lib.sampler_assemble_vocab_slices(ptrs, cols, lds, n, rows, _ptr(out), out.stride(0),
                                              _stream_ptr(stream)))
     return out
@@ -213,6 +209,51 @@ def sampler_sample(logits, params, row_offset: int = 0, max_logprobs: int = 0, o
         workspace = allocate_workspace(rows, vocab, max_logprobs, logits.device)
     _check(lib.sampler_sample(
         _ptr(logits), rows, vocab, logits.stride(0), _ptr(params), row_offset, max_logprobs,
+        _ptr(out.token_ids), _ptr(out.token_logprobs),
+        _ptr(out.topn_ids) if max_logprobs > 0 else None,
+        _ptr(out.topn_logprobs) if max_logprobs > 0 else None,
+        _ptr(out.row_status), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+    return out
+
+
+def _slice_arrays(slices):
+    torch = _torch()
+    n = len(slices)
+    if n < 1 or n > TS_MAX_SLICES:
+        raise ValueError(f"need 1..{TS_MAX_SLICES} slices")
+    rows = slices[0].shape[0]
+    for s in slices:
+        if s.dtype != torch.float32 or s.dim() != 2 or s.shape[0] != rows or s.stride(1) != 1:
+            raise ValueError("slices must be fp32 [rows, cols_s] with unit column stride")
+    ptrs = (ctypes.c_void_p * n)(*[_ptr(s) for s in slices])
+    cols = (ctypes.c_int64 * n)(*[int(s.shape[1]) for s in slices])
+    lds = (ctypes.c_int64 * n)(*[max(int(s.stride(0)), int(s.shape[1])) for s in slices])
+    return n, rows, ptrs, cols, lds
+
+
+def sampler_workspace_bytes_slices(rows: int, slice_cols, max_logprobs: int) -> int:
+    n = len(slice_cols)
+    cols = (ctypes.c_int64 * max(n, 1))(*[int(c) for c in slice_cols])
+    return int(lib.sampler_workspace_bytes_slices(rows, cols, n, max_logprobs))
+
+
+def sampler_sample_slices(slices, params, row_offset: int = 0, max_logprobs: int = 0, out=None,
+                          workspace=None, stream=None) -> SampleOutput:
+    """``sampler_sample`` over the column-wise concatenation of ``slices``
+    (fp32 ``[rows, cols_s]`` each), read in place.  Token ids are global
+    columns of that concatenation."""
+    torch = _torch()
+    n, rows, ptrs, cols, lds = _slice_arrays(slices)
+    if params.dtype != torch.uint8 or params.numel() != PARAMS_BYTES * rows:
+        raise ValueError("params must be rows x 24 bytes (uint8)")
+    device = slices[0].device
+    if out is None:
+        out = allocate_sample_output(rows, max_logprobs, device)
+    if workspace is None:
+        nb = max(256, sampler_workspace_bytes_slices(rows, list(cols), max_logprobs))
+        workspace = torch.empty(nb, dtype=torch.uint8, device=device)
+    _check(lib.sampler_sample_slices(
+        ptrs, cols, lds, n, rows, _ptr(params), row_offset, max_logprobs,
         _ptr(out.token_ids), _ptr(out.token_logprobs),
         _ptr(out.topn_ids) if max_logprobs > 0 else None,
         _ptr(out.topn_logprobs) if max_logprobs > 0 else None,

@@ -75,17 +75,26 @@ int lmhead_logits_local(const void* hidden, int64_t rows, int64_t hidden_dim, in
 
 size_t sampler_workspace_bytes(int64_t rows, int64_t vocab, int32_t max_logprobs) {
   if (rows < 0 || vocab < 0 || max_logprobs < 0) return 0;
-  return ts::sampler_workspace_size(rows, vocab, max_logprobs);
+  return ts::sampler_workspace_size(rows, &vocab, 1, max_logprobs);
 }
 
-int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_logits,
-                   const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
-                   int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
-                   float* topn_logprobs, int32_t* row_status, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-  if (rows < 0 || vocab < 0)
-    return fail(TS_EINVAL, "negative size (rows=%lld vocab=%lld)", (long long)rows,
-                (long long)vocab);
+size_t sampler_workspace_bytes_slices(int64_t rows, const int64_t* slice_cols, int32_t n_slices,
+                                      int32_t max_logprobs) {
+  if (rows < 0 || max_logprobs < 0 || n_slices < 1 || n_slices > TS_MAX_SLICES || !slice_cols)
+    return 0;
+  for (int i = 0; i < n_slices; ++i)
+    if (slice_cols[i] < 0) return 0;
+  return ts::sampler_workspace_size(rows, slice_cols, n_slices, max_logprobs);
+}
+
+namespace {
+
+// Validates everything but the logits, fills `a` and launches.
+int sample_common(ts::SamplerArgs& a, const int64_t* cols, int64_t rows, int64_t vocab,
+                  const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                  int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                  float* topn_logprobs, int32_t* row_status, void* workspace,
+                  size_t workspace_bytes, void* stream) {
   if (max_logprobs < 0) return fail(TS_EINVAL, "max_logprobs < 0");
   if (max_logprobs > TS_MAX_LOGPROBS)
     return fail(TS_EUNSUPPORTED, "max_logprobs %d above %d", max_logprobs, TS_MAX_LOGPROBS);
@@ -93,21 +102,15 @@ int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_
   if (rows > kMaxDim || vocab > kMaxDim) return fail(TS_EUNSUPPORTED, "size above 2^31-1");
   if (rows == 0) return TS_OK;
   if (vocab == 0) return fail(TS_EINVAL, "vocab == 0 with rows > 0");
-  if (ld_logits < vocab) return fail(TS_EINVAL, "ld_logits %lld < vocab %lld",
-                                     (long long)ld_logits, (long long)vocab);
-  if (!logits || !params || !token_ids) return fail(TS_EINVAL, "NULL logits/params/token_ids");
+  if (!params || !token_ids) return fail(TS_EINVAL, "NULL params/token_ids");
   if (max_logprobs > 0 && (!topn_ids || !topn_logprobs))
     return fail(TS_EINVAL, "NULL top-N outputs with max_logprobs > 0");
-  if (!aligned(logits, 4) || !aligned(params, 8) || !aligned(token_ids, 4))
-    return fail(TS_EUNSUPPORTED, "misaligned pointer");
-  const size_t need = ts::sampler_workspace_size(rows, vocab, max_logprobs);
+  if (!aligned(params, 8) || !aligned(token_ids, 4)) return fail(TS_EUNSUPPORTED, "misaligned pointer");
+  const size_t need = ts::sampler_workspace_size(rows, cols, a.lv.n, max_logprobs);
   if (!workspace || workspace_bytes < need)
     return fail(TS_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(TS_EUNSUPPORTED, "workspace not 256-byte aligned");
-  ts::SamplerArgs a;
-  a.logits = logits;
-  a.ld = ld_logits;
   a.rows = static_cast<int>(rows);
   a.vocab = static_cast<int>(vocab);
   a.params = params;
@@ -120,7 +123,67 @@ int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_
   a.row_status = row_status;
   const hipError_t e =
       ts::launch_sampler(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
-  return hip_status(e, "sampler_sample launch");
+  return hip_status(e, "sampler launch");
+}
+
+}  // namespace
+
+int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_logits,
+                   const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                   int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                   float* topn_logprobs, int32_t* row_status, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (rows < 0 || vocab < 0)
+    return fail(TS_EINVAL, "negative size (rows=%lld vocab=%lld)", (long long)rows,
+                (long long)vocab);
+  if (rows > 0 && vocab > 0) {
+    if (ld_logits < vocab)
+      return fail(TS_EINVAL, "ld_logits %lld < vocab %lld", (long long)ld_logits,
+                  (long long)vocab);
+    if (!logits) return fail(TS_EINVAL, "NULL logits");
+    if (!aligned(logits, 4)) return fail(TS_EUNSUPPORTED, "misaligned pointer");
+  }
+  ts::SamplerArgs a{};
+  a.lv.n = 1;
+  a.lv.ptr[0] = logits;
+  a.lv.ld[0] = ld_logits;
+  a.lv.off[0] = 0;
+  a.lv.off[1] = vocab;
+  return sample_common(a, &vocab, rows, vocab, params, row_offset, max_logprobs, token_ids,
+                       token_logprobs, topn_ids, topn_logprobs, row_status, workspace,
+                       workspace_bytes, stream);
+}
+
+int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
+                          const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                          const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                          int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                          float* topn_logprobs, int32_t* row_status, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (n_slices < 1 || n_slices > TS_MAX_SLICES)
+    return fail(n_slices < 1 ? TS_EINVAL : TS_EUNSUPPORTED, "n_slices %d not in [1, %d]",
+                n_slices, TS_MAX_SLICES);
+  if (rows < 0) return fail(TS_EINVAL, "rows < 0");
+  if (!slices || !slice_cols || !slice_ld) return fail(TS_EINVAL, "NULL slice arrays");
+  ts::SamplerArgs a{};
+  a.lv.n = n_slices;
+  int64_t total = 0;
+  for (int i = 0; i < n_slices; ++i) {
+    const int64_t c = slice_cols[i];
+    if (c < 0) return fail(TS_EINVAL, "slice %d has negative width", i);
+    if (slice_ld[i] < c) return fail(TS_EINVAL, "slice %d leading dimension below its width", i);
+    if (rows > 0 && c > 0 && !slices[i]) return fail(TS_EINVAL, "slice %d is NULL", i);
+    if (slices[i] && !aligned(slices[i], 4)) return fail(TS_EUNSUPPORTED, "slice %d misaligned", i);
+    a.lv.ptr[i] = slices[i];
+    a.lv.ld[i] = slice_ld[i];
+    a.lv.off[i] = total;
+    total += c;
+    if (total > kMaxDim) return fail(TS_EUNSUPPORTED, "size above 2^31-1");
+  }
+  a.lv.off[n_slices] = total;
+  return sample_common(a, slice_cols, rows, total, params, row_offset, max_logprobs, token_ids,
+                       token_logprobs, topn_ids, topn_logprobs, row_status, workspace,
+                       workspace_bytes, stream);
 }
 
 int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* slice_cols,

@@ -132,16 +132,22 @@ struct ProbeRec {  // a top-p-only row whose boundary lies below the listed logi
 
 struct FastLayout {
   int S;  // chunks per row
-  int L;  // logits per chunk (multiple of 4; the last chunk may be shorter)
+  int L;  // logits per chunk (multiple of 4; a slice's last chunk may be shorter)
+  int nsl;                      // column slices
+  int cbase[TS_MAX_SLICES + 1];  // first chunk of each slice (chunks never straddle slices)
   size_t off_ctr, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Chunks per row: at most kChunkMax logits each, enough workgroups to fill
-// the chip (about 1024), chunks of at least 1024 logits, at most kMaxChunks.
-inline FastLayout make_layout(int64_t rows, int64_t vocab) {
+// the chip (about 1024), chunks of at least 1024 logits, at most kMaxChunks;
+// every slice is cut into chunks of its own.  S == 0 marks a shape the chunked
+// path does not take.
+inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n) {
   FastLayout l{};
+  int64_t vocab = 0;
+  for (int s = 0; s < n; ++s) vocab += cols[s];
   int64_t S = (vocab + kChunkMax - 1) / kChunkMax;
   int64_t want = rows > 0 ? (1024 + rows - 1) / rows : 1;
   int64_t most = vocab / 1024 > 0 ? vocab / 1024 : 1;
@@ -150,14 +156,26 @@ inline FastLayout make_layout(int64_t rows, int64_t vocab) {
   if (S < want) S = want;
   if (S < 1) S = 1;
   int64_t L = (vocab + S - 1) / S;
+  if (n > 1 && n < kMaxChunks) {
+    // Each slice adds at most one partial chunk: keep the total within kMaxChunks.
+    const int64_t Lmin = (vocab + (kMaxChunks - n) - 1) / (kMaxChunks - n);
+    if (L < Lmin) L = Lmin;
+  }
   L = (L + 3) / 4 * 4;
   if (L < 4) L = 4;
-  S = (vocab + L - 1) / L;
-  if (S < 1) S = 1;
-  l.S = static_cast<int>(S);
   l.L = static_cast<int>(L);
+  l.nsl = n;
+  int64_t total = 0;
+  l.cbase[0] = 0;
+  for (int s = 0; s < n; ++s) {
+    total += (cols[s] + L - 1) / L;
+    l.cbase[s + 1] = static_cast<int>(total < (1 << 30) ? total : (1 << 30));
+  }
+  l.S = (L > kChunkMax || total > kMaxChunks || n >= kMaxChunks || total < 1)
+            ? 0
+            : static_cast<int>(total);
   const size_t R = static_cast<size_t>(rows);
-  const size_t RS = R * static_cast<size_t>(S);
+  const size_t RS = R * static_cast<size_t>(l.S);
   size_t off = 0;
   l.off_ctr = off;  // [0] exact rows, [1] probe rows
   off = align_up(off + 256, 256);
@@ -179,9 +197,54 @@ inline FastLayout make_layout(int64_t rows, int64_t vocab) {
   return l;
 }
 
-inline bool fast_path_supported(int64_t rows, int64_t vocab) {
-  if (vocab > static_cast<int64_t>(kChunkMax) * kMaxChunks) return false;
-  return rows * static_cast<int64_t>(make_layout(rows, vocab).S) <= 0x7fffffff;
+// The chunked path needs every slice to start at a column that is a multiple
+// of 4 (a float4 of a chunk then holds one Philox block of four tokens).
+inline bool fast_path_supported(int64_t rows, const int64_t* cols, int n) {
+  const FastLayout l = make_layout(rows, cols, n);
+  if (l.S == 0) return false;
+  int64_t off = 0;
+  for (int s = 0; s < n; ++s) {
+    if (cols[s] > 0 && off % 4 != 0) return false;
+    off += cols[s];
+  }
+  return rows * static_cast<int64_t>(l.S) <= 0x7fffffff;
+}
+
+// --------------------------------------------------------- logits access
+// Slice holding global column col (empty slices are skipped).
+__device__ __forceinline__ int slice_of(const LogitsView& lv, int col) {
+  int lo = 0, hi = lv.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (lv.off[mid] <= col) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float logit_at(const LogitsView& lv, int r, int col) {
+  const int s = slice_of(lv, col);
+  return lv.ptr[s][static_cast<int64_t>(r) * lv.ld[s] + (col - lv.off[s])];
+}
+
+// Chunk c of row r: its first logit, its length and its first global column.
+struct ChunkGeo {
+  const float* src;
+  int n;
+  int gofs;
+};
+
+__device__ __forceinline__ ChunkGeo chunk_geo(const LogitsView& lv, const FastLayout& lay, int r,
+                                              int c) {
+  int s = 0;
+  while (s + 1 < lay.nsl && c >= lay.cbase[s + 1]) ++s;
+  const int c0 = (c - lay.cbase[s]) * lay.L;
+  const int cols = static_cast<int>(lv.off[s + 1] - lv.off[s]);
+  ChunkGeo g;
+  g.n = min(lay.L, cols - c0);
+  g.gofs = static_cast<int>(lv.off[s]) + c0;
+  g.src = lv.ptr[s] + static_cast<int64_t>(r) * lv.ld[s] + c0;
+  return g;
 }
 
 // ---------------------------------------------------------- block utilities

@@ -41,14 +41,34 @@ struct FallbackSmem {
   uint32_t sel_above;
   unsigned long long sel_above_q;
   int list_n;
+  LogitsView lv;  // the slice table, read with per-thread indices from here
 };
+
+// Copies the slice table out of the kernel arguments with constant indices
+// only.  Indexing the by-value argument with a run-time slice number makes the
+// compiler copy the whole argument block into per-lane scratch memory.
+__device__ __forceinline__ void stage_view(const LogitsView& src, LogitsView& dst) {
+  if (threadIdx.x == 0) {
+    dst.n = src.n;
+    dst.off[0] = src.off[0];
+#pragma unroll
+    for (int s = 0; s < TS_MAX_SLICES; ++s) {
+      if (s < src.n) {
+        dst.ptr[s] = src.ptr[s];
+        dst.ld[s] = src.ld[s];
+        dst.off[s + 1] = src.off[s + 1];
+      }
+    }
+  }
+  __syncthreads();
+}
 
 __device__ __forceinline__ int digit_shift(int rd) { return rd == 0 ? 21 : (rd == 1 ? 10 : 0); }
 __device__ __forceinline__ int digit_width(int rd) { return rd == 2 ? 10 : 11; }
 
 // Same search over fixed-point masses: the bin where the mass counted from the
 // top first reaches `rem`.
-__device__ void select_digit_mass(FallbackSmem& sh, int nb, unsigned long long rem) {
+__device__ __forceinline__ void select_digit_mass(FallbackSmem& sh, int nb, unsigned long long rem) {
   const int t = threadIdx.x;
   const int b0 = nb - 1 - 2 * t, b1 = nb - 2 - 2 * t;
   const unsigned long long h0 = b0 >= 0 ? sh.ex.mass[b0] : 0ull;
@@ -65,9 +85,21 @@ __device__ void select_digit_mass(FallbackSmem& sh, int nb, unsigned long long r
   __syncthreads();
 }
 
+// Calls f(i, l) for the logits of row r, each thread taking every XT-th
+// column of each slice.
+template <typename F>
+__device__ __forceinline__ void for_row(const LogitsView& lv, int r, F&& f) {
+  for (int s = 0; s < lv.n; ++s) {
+    const float* __restrict__ src = lv.ptr[s] + static_cast<int64_t>(r) * lv.ld[s];
+    const int base = static_cast<int>(lv.off[s]);
+    const int cols = static_cast<int>(lv.off[s + 1] - lv.off[s]);
+    for (int j = threadIdx.x; j < cols; j += XT) f(base + j, src[j]);
+  }
+}
+
 // The k-th largest key of the row (1 <= k <= V): K with
 // #(key > K) < k <= #(key >= K).  Returns K, gt = #(key > K), eq = #(key == K).
-__device__ void radix_kth(const float* __restrict__ row, int V, uint32_t k, FallbackSmem& sh,
+__device__ __forceinline__ void radix_kth(const LogitsView& lv, int r, uint32_t k, FallbackSmem& sh,
                           uint32_t& K, uint32_t& gt, uint32_t& eq) {
   uint32_t prefix = 0, pmask = 0, rem = k, above = 0, last = 0;
   for (int rd = 0; rd < 3; ++rd) {
@@ -75,10 +107,10 @@ __device__ void radix_kth(const float* __restrict__ row, int V, uint32_t k, Fall
     const uint32_t dmask = (1u << width) - 1u;
     for (int b = threadIdx.x; b < RBINS; b += XT) sh.ex.cnt[b] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < V; i += XT) {
-      const uint32_t key = order_key(row[i]);
+    for_row(lv, r, [&](int, float l) {
+      const uint32_t key = order_key(l);
       if ((key & pmask) == prefix) atomicAdd(&sh.ex.cnt[(key >> shift) & dmask], 1u);
-    }
+    });
     __syncthreads();
     select_digit_top<XT, 2>(sh.ex.cnt, 1 << width, rem, sh.ru, &sh.sel_digit, &sh.sel_above);
     const uint32_t d = sh.sel_digit, a = sh.sel_above;
@@ -96,7 +128,7 @@ __device__ void radix_kth(const float* __restrict__ row, int V, uint32_t k, Fall
 
 // The largest key K such that the fixed-point mass of {key >= max(K, floor)}
 // reaches `target` (1 <= target <= mass of {key >= floor}).
-__device__ uint32_t radix_mass(const float* __restrict__ row, int V, uint32_t floor_key, float m,
+__device__ __forceinline__ uint32_t radix_mass(const LogitsView& lv, int r, uint32_t floor_key, float m,
                                float inv_t, unsigned long long target, FallbackSmem& sh) {
   uint32_t prefix = 0, pmask = 0;
   unsigned long long rem = target;
@@ -105,12 +137,11 @@ __device__ uint32_t radix_mass(const float* __restrict__ row, int V, uint32_t fl
     const uint32_t dmask = (1u << width) - 1u;
     for (int b = threadIdx.x; b < RBINS; b += XT) sh.ex.mass[b] = 0ull;
     __syncthreads();
-    for (int i = threadIdx.x; i < V; i += XT) {
-      const float l = row[i];
+    for_row(lv, r, [&](int, float l) {
       const uint32_t key = order_key(l);
       if (key >= floor_key && (key & pmask) == prefix)
         atomicAdd(&sh.ex.mass[(key >> shift) & dmask], fixed_mass(expf((l - m) * inv_t)));
-    }
+    });
     __syncthreads();
     select_digit_mass(sh, 1 << width, rem);
     const uint32_t d = sh.sel_digit;
@@ -123,7 +154,7 @@ __device__ uint32_t radix_mass(const float* __restrict__ row, int V, uint32_t fl
   return prefix;
 }
 
-__device__ void write_bad_row(const SamplerArgs& a, int r, int status) {
+__device__ __forceinline__ void write_bad_row(const SamplerArgs& a, int r, int status) {
   const float qnan = __builtin_nanf("");
   for (int j = threadIdx.x; j < a.max_logprobs; j += XT) {
     a.topn_ids[static_cast<int64_t>(r) * a.max_logprobs + j] = -1;
@@ -137,10 +168,10 @@ __device__ void write_bad_row(const SamplerArgs& a, int r, int status) {
 }
 
 // The whole row from scratch.
-__device__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
+__device__ __forceinline__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
   const int tid = threadIdx.x;
   const int V = a.vocab;
-  const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
+  const LogitsView& lv = sh.lv;
   const ts_row_params p = a.params[r];
 
   if (!params_ok(p, a.max_logprobs)) {
@@ -152,15 +183,14 @@ __device__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
   uint32_t bk = 0u;
   int bi = 0x7fffffff;
   int bad = 0;
-  for (int i = tid; i < V; i += XT) {
-    const float l = row[i];
+  for_row(lv, r, [&](int i, float l) {
     bad |= (isnan(l) || (isinf(l) && l > 0.0f)) ? 1 : 0;
     const uint32_t key = order_key(l);
     if (better_u(key, i, bk, bi)) {
       bk = key;
       bi = i;
     }
-  }
+  });
   bad = block_sum<XT, int>(bad, sh.ri);
   block_best_u<XT>(bk, bi, sh.ru, sh.ri);
   const float m = key_to_float(bk);
@@ -172,7 +202,7 @@ __device__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
 
   // Pass 2: log-sum-exp of the raw logits (fixed per-thread order, fixed tree).
   float s = 0.0f;
-  for (int i = tid; i < V; i += XT) s += expf(row[i] - m);
+  for_row(lv, r, [&](int, float l) { s += expf(l - m); });
   s = block_sum<XT, float>(s, sh.rf_);
   const float lse = m + logf(s);
 
@@ -185,23 +215,23 @@ __device__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
   }
   if (n > 0) {
     uint32_t kn, gt, eq;
-    radix_kth(row, V, static_cast<uint32_t>(n), sh, kn, gt, eq);
+    radix_kth(lv, r, static_cast<uint32_t>(n), sh, kn, gt, eq);
     const uint32_t need = static_cast<uint32_t>(n) - gt;  // ties at kn taken by lowest id
     if (tid == 0) sh.list_n = 0;
     __syncthreads();
-    for (int i = tid; i < V; i += XT) {
-      const uint32_t key = order_key(row[i]);
+    for_row(lv, r, [&](int i, float l) {
+      const uint32_t key = order_key(l);
       if (key > kn || (eq == need && key == kn)) {
         const int slot = atomicAdd(&sh.list_n, 1);
         sh.ex.list_key[slot] = key;
         sh.ex.list_id[slot] = i;
       }
-    }
+    });
     if (eq != need) {
       uint32_t taken = 0;
       for (int base = 0; base < V && taken < need; base += XT) {
         const int i = base + tid;
-        const bool f = i < V && order_key(row[i]) == kn;
+        const bool f = i < V && order_key(logit_at(lv, r, i)) == kn;
         uint32_t tot;
         const uint32_t ex = block_exclusive_scan<XT, uint32_t>(f ? 1u : 0u, sh.ru, tot);
         if (f && taken + ex < need) {
@@ -233,22 +263,21 @@ __device__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
     uint32_t kk = 0u;
     if (p.top_k > 0 && p.top_k < V) {
       uint32_t gt, eq;
-      radix_kth(row, V, static_cast<uint32_t>(p.top_k), sh, kk, gt, eq);
+      radix_kth(lv, r, static_cast<uint32_t>(p.top_k), sh, kk, gt, eq);
     }
     // Top-p threshold key on the temperature-scaled top-k distribution.
     uint32_t kp = 0u;
     if (p.top_p < 1.0f) {
       unsigned long long z = 0ull;
-      for (int i = tid; i < V; i += XT) {
-        const float l = row[i];
+      for_row(lv, r, [&](int, float l) {
         if (order_key(l) >= kk) z += fixed_mass(expf((l - m) * inv_t));
-      }
+      });
       z = block_sum<XT, unsigned long long>(z, sh.rq);
       const double tgt = ceil(static_cast<double>(p.top_p) * static_cast<double>(z));
       unsigned long long target = static_cast<unsigned long long>(tgt);
       if (target < 1ull) target = 1ull;
       if (target > z) target = z;
-      kp = radix_mass(row, V, kk, m, inv_t, target, sh);
+      kp = radix_mass(lv, r, kk, m, inv_t, target, sh);
     }
     const uint32_t thr = kk > kp ? kk : kp;
     // Gumbel-max over the kept set, four consecutive tokens per Philox call.
@@ -263,7 +292,7 @@ __device__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int v = 4 * q + j;
-        l4[j] = v < V ? row[v] : -INFINITY;
+        l4[j] = v < V ? logit_at(lv, r, v) : -INFINITY;
         in[j] = v < V && order_key(l4[j]) >= thr;
         any |= in[j];
       }
@@ -284,16 +313,16 @@ __device__ void exact_row(const SamplerArgs& a, int r, FallbackSmem& sh) {
   }
   if (tid == 0) {
     a.token_ids[r] = token;
-    if (a.token_logprobs) a.token_logprobs[r] = row[token] - lse;
+    if (a.token_logprobs) a.token_logprobs[r] = logit_at(lv, r, token) - lse;
     if (a.row_status) a.row_status[r] = TS_ROW_OK;
   }
 }
 
 // Probe row: the first probe (best Gumbel key first) whose mass-above is below
 // p times the total is the winner.
-__device__ void finish_probe_row(const SamplerArgs& a, const FastLayout& lay, const uint8_t* ws,
+__device__ __forceinline__ void finish_probe_row(const SamplerArgs& a, const FastLayout& lay, const uint8_t* ws,
                                  int li, int r, FallbackSmem& sh) {
-  const ProbeRec pr = reinterpret_cast<const ProbeRec*>(ws + lay.off_prec)[r];
+  const ProbeRec& pr = reinterpret_cast<const ProbeRec*>(ws + lay.off_prec)[r];
   const ts_row_params p = a.params[r];
   const double* part = reinterpret_cast<const double*>(ws + lay.off_part) +
                        static_cast<size_t>(li) * lay.S * kProbes;
@@ -315,9 +344,8 @@ __device__ void finish_probe_row(const SamplerArgs& a, const FastLayout& lay, co
     return;
   }
   if (threadIdx.x == 0) {
-    const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
     a.token_ids[r] = win;
-    if (a.token_logprobs) a.token_logprobs[r] = row[win] - pr.lse;
+    if (a.token_logprobs) a.token_logprobs[r] = logit_at(sh.lv, r, win) - pr.lse;
     if (a.row_status) a.row_status[r] = TS_ROW_OK;
   }
 }
@@ -328,6 +356,7 @@ __global__ __launch_bounds__(XT) void sampler_finish_kernel(SamplerArgs a, FastL
                                                             uint8_t* ws, int all_rows) {
   __shared__ FallbackSmem sh;
   const int b = blockIdx.x;
+  stage_view(a.lv, sh.lv);
   if (all_rows) {
     exact_row(a, b, sh);
     return;

@@ -3,38 +3,44 @@
 // The sampler runs on the rank's slice of requests: batch x (speculative
 // tokens + 1) rows of full-vocabulary fp32 logits (page "Qwen4Exp
 // batch-sharded sampling: inside vLLM PR #61018", section "What
-// batch-sharded sampling is, in one paragraph").  It is HBM-bound: every
-// logit is read from HBM once, except the rows of the probe pass below.
+// batch-sharded sampling is, in one paragraph").  The logits are read where
+// they lie: one buffer, or the vocabulary slices the exchange delivered
+// (LogitsView; chunks never straddle two slices).  It is HBM-bound: every
+// logit is read from HBM once by the chunk pass; the noise and probe passes
+// re-read only the rows that need them.
 //
 // A  chunk pass   one 256-thread workgroup per (row, chunk of <= 16384
-//                 logits), the chunk held in registers (16 float4 per thread,
-//                 two workgroups per CU).  Per chunk:
-//                   - max and sum exp(l - max) (hardware exp2); a NaN or +inf
-//                     shows up as a NaN sum;
-//                   - a logit candidate list holding at least the chunk's M
-//                     largest, M = max(n_logprobs, top_k) (64 for top-p-only
-//                     rows): the threshold is the M-th largest per-thread
-//                     maximum (or of the per-thread top two), found by LDS
-//                     radix selection over 256 or 512 values; M of the
-//                     chunk's logits are at or above it by construction;
-//                   - full-vocabulary rows: the chunk's best Gumbel key;
-//                   - top-p-only rows: every token whose Gumbel key is at or
-//                     above the 8th largest per-thread best key (a complete
-//                     list above that floor), and the temperature-scaled mass.
+//                 logits), the chunk held in registers (16 float4 per
+//                 thread).  Per chunk, in one pass over the loaded values:
+//                   - max, sum exp(l - max) and, for top-p-only rows, sum
+//                     exp((l - max) / T), rescaled as the maximum grows; a
+//                     NaN or +inf shows up as a NaN sum;
+//                   - a logit candidate list holding at least the chunk's
+//                     share of the row's M largest, M = max(n_logprobs,
+//                     top_k) (64 for top-p-only rows): the threshold is the
+//                     q-th largest per-thread maximum (or top-4 value) of
+//                     each wave, found with one ballot per key bit, or an
+//                     LDS radix selection for large M.
+// N  noise        one workgroup per chunk of a full-vocabulary or top-p-only
+//                 row: Philox4x32-10 Gumbel keys, skipped for tokens whose
+//                 uniform cannot lift them over the running bar; every key
+//                 above the chunk's floor goes to a short key list.
 // B  merge        one 256-thread workgroup per row: log-sum-exp; the union of
-//                 logit candidates above the highest chunk threshold (radix
-//                 selection trims it to the row's M largest when needed) is
-//                 exactly the row's logits above it, sorted in LDS (bitonic).
-//                 Top-N, greedy, top-k, top-p and Gumbel-max are exact on that
-//                 prefix.  A top-p-only row whose boundary lies below it takes
-//                 the row's best Gumbel keys as probes.
+//                 logit candidates above the highest chunk threshold is
+//                 exactly the row's logits above it.  Short prefixes (top N,
+//                 top-k up to 192, the head of a top-p row) are trimmed and
+//                 sorted in LDS; longer top-k sets are settled by count- and
+//                 mass-weighted radix selection without sorting.  Top-N,
+//                 greedy, top-k, top-p and Gumbel-max are exact on the list.
+//                 A top-p-only row whose boundary lies below the list takes
+//                 its best Gumbel keys as probes.
 // P  probe        chunk-parallel re-read of probe rows only: the mass of the
 //                 logits strictly above each probe's logit.  Token v is kept
 //                 by top-p iff that mass is below p times the total, so the
 //                 first probe (by key) that is kept is the Gumbel-max winner.
 // X  finish       (sampler_exact.hip) settles probe rows; rows that no fast
-//                 route settles (candidate overflow, top_k > 1024, no kept
-//                 probe) run the exact per-row kernel.
+//                 route settles (candidate or key overflow, top_k > 1024, no
+//                 kept probe) run the exact per-row kernel.
 #include <stdlib.h>
 
 #include "sampler_common.hpp"
@@ -244,14 +250,14 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   const int kind = row_kind(p, V, a.max_logprobs);
   if (kind == KIND_BAD || kind == KIND_EXACT) return;
   ChunkRec* rec = reinterpret_cast<ChunkRec*>(ws + lay.off_chunk) + bid;
-  const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
-  const int c0 = c * lay.L;
-  const int n = min(lay.L, V - c0);
+  const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
+  const int c0 = geo.gofs;  // global column of the chunk's first logit
+  const int n = geo.n;
   const bool topp = kind == KIND_TOPP;
   const float inv_t = kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature;
 
   float4 v[AV];
-  load_chunk<VEC>(v, row + c0, n, tid);
+  load_chunk<VEC>(v, geo.src, n, tid);
 
   // One pass over the thread's logits in load order, so each float4 is used
   // as soon as it lands: the thread maximum with sum exp(l - max) (and, for
@@ -419,14 +425,14 @@ __global__ __launch_bounds__(AT) void noise_kernel(SamplerArgs a, FastLayout lay
   ChunkRec* rec = reinterpret_cast<ChunkRec*>(ws + lay.off_chunk) + bid;
   if (rec->status != 0) return;  // NaN / +inf or candidate overflow: the row goes elsewhere
   const float cmax = rec->cmax;
-  const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
-  const int c0 = c * lay.L;
-  const int n = min(lay.L, V - c0);
+  const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
+  const int c0 = geo.gofs;  // global column of the chunk's first logit (a multiple of 4)
+  const int n = geo.n;
   const bool topp = kind == KIND_TOPP;
   const float inv_t = 1.0f / p.temperature;
   if (tid == 0) sh.nkey = 0;
   float4 v[AV];
-  load_chunk<VEC>(v, row + c0, n, tid);
+  load_chunk<VEC>(v, geo.src, n, tid);
   __syncthreads();
   // Gumbel keys relative to the chunk maximum: x = (l - cmax) / T, key = x + g.
   float kfloor = INFINITY;
@@ -763,7 +769,6 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   int* ctr = reinterpret_cast<int*>(ws + lay.off_ctr);
   int* exact_list = reinterpret_cast<int*>(ws + lay.off_exact);
   int* probe_list = reinterpret_cast<int*>(ws + lay.off_probe);
-  const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
   if (kind == KIND_BAD) {
     write_bad<BT>(a, r, TS_ROW_BAD_PARAMS);
     return;
@@ -941,7 +946,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     for (int c = tid; c < S; c += BT) {
       if (sh.nkey[c] < 1) continue;
       const int id = keys[static_cast<size_t>(c) * kKeyCap];
-      const float key = gumbel_key(row[id], m, inv_t, p.seed, grow, id);
+      const float key = gumbel_key(logit_at(a.lv, r, id), m, inv_t, p.seed, grow, id);
       if (better(key, id, gk, gi)) {
         gk = key;
         gi = id;
@@ -1071,7 +1076,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       const int c = g / kKeyCap, i = g - c * kKeyCap;
       if (i >= sh.nkey[c]) continue;
       const int id = keys[g];
-      const float key = gumbel_key(row[id], m, inv_t, p.seed, grow, id);
+      const float key = gumbel_key(logit_at(a.lv, r, id), m, inv_t, p.seed, grow, id);
       if (key >= kmin) {
         const int slot = atomicAdd(&sh.nlist, 1);
         if (slot < kListMax) sh.list[slot] = pack_cand(order_key(key), id);
@@ -1094,7 +1099,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       for (int i = 0; i < kProbes; ++i) {
         const int id = i < pr.npts ? cand_id(sh.list[i]) : 0;
         pr.id[i] = id;
-        pr.pt[i] = i < pr.npts ? row[id] : INFINITY;
+        pr.pt[i] = i < pr.npts ? logit_at(a.lv, r, id) : INFINITY;
       }
       reinterpret_cast<ProbeRec*>(ws + lay.off_prec)[r] = pr;
       push_row(&ctr[1], probe_list, r);
@@ -1103,7 +1108,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   }
   if (tid == 0) {
     a.token_ids[r] = token;
-    if (a.token_logprobs) a.token_logprobs[r] = row[token] - lse;
+    if (a.token_logprobs) a.token_logprobs[r] = logit_at(a.lv, r, token) - lse;
     if (a.row_status) a.row_status[r] = TS_ROW_OK;
   }
 }
@@ -1121,9 +1126,9 @@ __global__ __launch_bounds__(PT) void probe_kernel(SamplerArgs a, FastLayout lay
     const int li = w / S, c = w - li * S;
     const int r = probe_list[li];
     const ProbeRec pr = reinterpret_cast<const ProbeRec*>(ws + lay.off_prec)[r];
-    const float* __restrict__ row = a.logits + static_cast<int64_t>(r) * a.ld;
-    const int c0 = c * lay.L;
-    const int n = min(lay.L, a.vocab - c0);
+    const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
+    const float* __restrict__ src = geo.src;
+    const int n = geo.n;
     const float sc = pr.inv_t * kLog2e;
     float acc[kProbes];
 #pragma unroll
@@ -1131,12 +1136,12 @@ __global__ __launch_bounds__(PT) void probe_kernel(SamplerArgs a, FastLayout lay
     for (int e = 4 * tid; e < n; e += 4 * PT) {
       float4 f;
       if (vec && e + 3 < n) {
-        f = load_stream4(row + c0 + e);
+        f = load_stream4(src + e);
       } else {
-        f.x = e + 0 < n ? load_stream(row + c0 + e + 0) : -INFINITY;
-        f.y = e + 1 < n ? load_stream(row + c0 + e + 1) : -INFINITY;
-        f.z = e + 2 < n ? load_stream(row + c0 + e + 2) : -INFINITY;
-        f.w = e + 3 < n ? load_stream(row + c0 + e + 3) : -INFINITY;
+        f.x = e + 0 < n ? load_stream(src + e + 0) : -INFINITY;
+        f.y = e + 1 < n ? load_stream(src + e + 1) : -INFINITY;
+        f.z = e + 2 < n ? load_stream(src + e + 2) : -INFINITY;
+        f.w = e + 3 < n ? load_stream(src + e + 3) : -INFINITY;
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -1171,10 +1176,11 @@ bool env_flag(const char* name) {
 
 }  // namespace
 
-size_t sampler_workspace_size(int64_t rows, int64_t vocab, int max_logprobs) {
+size_t sampler_workspace_size(int64_t rows, const int64_t* slice_cols, int n_slices,
+                              int max_logprobs) {
   (void)max_logprobs;
-  if (!fast_path_supported(rows, vocab)) return 256;
-  return make_layout(rows, vocab).total;
+  if (!fast_path_supported(rows, slice_cols, n_slices)) return 256;
+  return make_layout(rows, slice_cols, n_slices).total;
 }
 
 hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspace_bytes,
@@ -1182,11 +1188,18 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
   (void)workspace_bytes;
   if (a.rows == 0) return hipSuccess;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  if (env_flag("TS_SAMPLER_EXACT") || !fast_path_supported(a.rows, a.vocab))
+  int64_t cols[TS_MAX_SLICES];
+  for (int s = 0; s < a.lv.n; ++s) cols[s] = a.lv.off[s + 1] - a.lv.off[s];
+  if (env_flag("TS_SAMPLER_EXACT") || !fast_path_supported(a.rows, cols, a.lv.n))
     return launch_sampler_finish(a, nullptr, ws, stream);
-  const FastLayout lay = make_layout(a.rows, a.vocab);
-  const int vec = (reinterpret_cast<uintptr_t>(a.logits) % 16 == 0) && (a.ld % 4 == 0) &&
-                  (a.vocab % 4 == 0);
+  const FastLayout lay = make_layout(a.rows, cols, a.lv.n);
+  // float4 loads: every slice 16-byte aligned with rows and widths of whole float4s.
+  int vec = 1;
+  for (int s = 0; s < a.lv.n; ++s) {
+    if (cols[s] == 0) continue;
+    vec &= (reinterpret_cast<uintptr_t>(a.lv.ptr[s]) % 16 == 0) && (a.lv.ld[s] % 4 == 0) &&
+           (cols[s] % 4 == 0);
+  }
   const unsigned chunks = static_cast<unsigned>(a.rows) * static_cast<unsigned>(lay.S);
   if (vec)
     hipLaunchKernelGGL(chunk_pass_kernel<true>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);

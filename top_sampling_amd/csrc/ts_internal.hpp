@@ -16,9 +16,18 @@ hipError_t launch_lmhead_gemm(const uint16_t* hidden, int64_t ld_hidden, const u
                               int vocab, int hidden_dim, hipStream_t stream);
 
 // ------------------------------------------------------------------- sampler
+// The sampler's logits: n column slices side by side, slice s holding global
+// columns [off[s], off[s + 1]) of every row at ptr[s] + row * ld[s].  A single
+// buffer is the one-slice case.
+struct LogitsView {
+  const float* ptr[TS_MAX_SLICES];
+  int64_t ld[TS_MAX_SLICES];
+  int64_t off[TS_MAX_SLICES + 1];
+  int n;
+};
+
 struct SamplerArgs {
-  const float* logits;
-  int64_t ld;
+  LogitsView lv;
   int rows;
   int vocab;
   const ts_row_params* params;
@@ -31,7 +40,8 @@ struct SamplerArgs {
   int32_t* row_status;    // may be null
 };
 
-size_t sampler_workspace_size(int64_t rows, int64_t vocab, int max_logprobs);
+size_t sampler_workspace_size(int64_t rows, const int64_t* slice_cols, int n_slices,
+                              int max_logprobs);
 hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
