@@ -82,6 +82,11 @@ __device__ __forceinline__ float gumbel_from_word(uint32_t x) {
   return __builtin_amdgcn_logf(a) * -kLn2;
 }
 
+// A value every lane of the wave holds, moved to a scalar register.
+__device__ __forceinline__ float uniform_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
+}
+
 // exp(x) for x <= 0 through the hardware base-2 exponential (v_exp_f32).
 __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * kLog2e);

@@ -84,7 +84,7 @@ __device__ void write_bad(const SamplerArgs& a, int r, int status) {
 // The M-th largest of nk keys in LDS (1 <= M <= nk), by radix selection
 // (11/11/10-bit digits).
 template <int NT>
-__device__ uint32_t lds_kth_largest(const uint32_t* keys, int nk, uint32_t M, uint32_t* hist,
+__device__ __forceinline__ uint32_t lds_kth_largest(const uint32_t* keys, int nk, uint32_t M, uint32_t* hist,
                                     uint32_t* scratch, uint32_t* sel_d, uint32_t* sel_above) {
   uint32_t prefix = 0u, pmask = 0u, rem = M;
   for (int rd = 0; rd < 3; ++rd) {
@@ -120,6 +120,7 @@ struct ChunkSmem {
   int ri[AW];
   uint32_t ru[AW];
   uint32_t sel_d, sel_above;
+  int wcnt[AW];
   int ncand, nkey;
 };
 
@@ -247,47 +248,35 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   if (bid == 0 && tid < 2) reinterpret_cast<int*>(ws + lay.off_ctr)[tid] = 0;
   const ts_row_params p = a.params[r];
   const int V = a.vocab;
-  const int kind = row_kind(p, V, a.max_logprobs);
+  // Row-uniform values in scalar registers, so the per-kind paths below are
+  // real branches rather than flattened selects.
+  const int kind = __builtin_amdgcn_readfirstlane(row_kind(p, V, a.max_logprobs));
   if (kind == KIND_BAD || kind == KIND_EXACT) return;
   ChunkRec* rec = reinterpret_cast<ChunkRec*>(ws + lay.off_chunk) + bid;
   const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
   const int c0 = geo.gofs;  // global column of the chunk's first logit
   const int n = geo.n;
   const bool topp = kind == KIND_TOPP;
-  const float inv_t = kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature;
+  const float inv_t = uniform_f32(kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature);
 
   float4 v[AV];
   load_chunk<VEC>(v, geo.src, n, tid);
 
-  // One pass over the thread's logits in load order, so each float4 is used
-  // as soon as it lands: the thread maximum with sum exp(l - max) (and, for
-  // top-p-only rows, sum exp((l - max) / T)) rescaled whenever the maximum
-  // grows, and the thread's four largest values when M > 64.  A NaN logit
-  // makes the sum NaN; +inf makes it NaN too (inf - inf); a thread holding
-  // only -inf and NaN scans for NaN afterwards.
-  const int M = chunk_target(cand_target(kind, p, V), S);
+  // The thread maximum, each float4 taken as soon as it lands (with the
+  // thread's four largest values when M > 64); then sum exp(l - max) and, for
+  // top-p-only rows, sum exp((l - max) / T) relative to that maximum.  A NaN
+  // logit makes the sum NaN; +inf makes it NaN too (inf - inf); a thread
+  // holding only -inf and NaN scans for NaN afterwards.
+  const int M = __builtin_amdgcn_readfirstlane(chunk_target(cand_target(kind, p, V), S));
   const bool four = M > 64 && M < n;
   float t[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float lm = -INFINITY, ls = 0.0f, lt = 0.0f;
   const float sc = inv_t * kLog2e;
+  if (four) {
 #pragma unroll
-  for (int j = 0; j < AV; ++j) {
-    const float4 f = v[j];
-    const float m4 = fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w));
-    if (m4 > lm) {
-      if (lm > -INFINITY) {
-        ls *= fast_exp(lm - m4);
-        if (topp) lt *= __builtin_amdgcn_exp2f((lm - m4) * sc);
-      }
-      lm = m4;
-    }
-    if (lm > -INFINITY) {
-      ls += fast_exp(f.x - lm) + fast_exp(f.y - lm) + fast_exp(f.z - lm) + fast_exp(f.w - lm);
-      if (topp)
-        lt += __builtin_amdgcn_exp2f((f.x - lm) * sc) + __builtin_amdgcn_exp2f((f.y - lm) * sc) +
-              __builtin_amdgcn_exp2f((f.z - lm) * sc) + __builtin_amdgcn_exp2f((f.w - lm) * sc);
-    }
-    if (four) {
+    for (int j = 0; j < AV; ++j) {
+      const float4 f = v[j];
+      lm = fmaxf(lm, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float x = lane(f, q);
@@ -297,6 +286,31 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
           x = fminf(t[i], x);
           t[i] = hi;
         }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const float4 f = v[j];
+      lm = fmaxf(lm, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
+    }
+  }
+  if (lm > -INFINITY) {
+    // exp(l - m) as 2^(l log2 e - m log2 e): one fused multiply-add per logit.
+    const float nl = -lm * kLog2e;
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const float4 f = v[j];
+      ls += __builtin_amdgcn_exp2f(fmaf(f.x, kLog2e, nl)) + __builtin_amdgcn_exp2f(fmaf(f.y, kLog2e, nl)) +
+            __builtin_amdgcn_exp2f(fmaf(f.z, kLog2e, nl)) + __builtin_amdgcn_exp2f(fmaf(f.w, kLog2e, nl));
+    }
+    if (topp) {
+      const float nt = -lm * sc;
+#pragma unroll
+      for (int j = 0; j < AV; ++j) {
+        const float4 f = v[j];
+        lt += __builtin_amdgcn_exp2f(fmaf(f.x, sc, nt)) + __builtin_amdgcn_exp2f(fmaf(f.y, sc, nt)) +
+              __builtin_amdgcn_exp2f(fmaf(f.z, sc, nt)) + __builtin_amdgcn_exp2f(fmaf(f.w, sc, nt));
       }
     }
   }
@@ -361,34 +375,58 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     tf = key_floor_value(kk);
   }
 
-  // Every valid logit >= tf goes to the chunk's candidate list.
-  unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws + lay.off_cand) +
-                             static_cast<size_t>(bid) * kCandCap;
+  // Every valid logit >= tf goes to the chunk's candidate list.  Slots come
+  // from a block-wide exclusive scan of the per-thread counts, so writing a
+  // candidate costs no LDS round trip.
+  unsigned long long cm = 0ull;  // bit 4j + q: lane q of v[j] is a candidate
 #pragma unroll
   for (int j = 0; j < AV; ++j) {
-    const float4 f = v[j];
-    if (fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)) >= tf) {
+    const int e = 4 * (j * AT + tid);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (lane(v[j], q) >= tf && e + q < n) cm |= 1ull << (4 * j + q);
+  }
+  const int cnt = __popcll(cm);
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(incl, d, kWave);
+    if (lane_id >= d) incl += t;
+  }
+  if (lane_id == kWave - 1) sh.wcnt[wave] = incl;
+  __syncthreads();
+  int slot = incl - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < AW; ++w) {
+    const int c = sh.wcnt[w];
+    slot += w < wave ? c : 0;
+    total += c;
+  }
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws + lay.off_cand) +
+                             static_cast<size_t>(bid) * kCandCap;
+  if (cm != 0ull) {
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      if (((cm >> (4 * j)) & 0xFull) == 0ull) continue;
       const int e = 4 * (j * AT + tid);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float l = lane(f, q);
-        if (l >= tf && e + q < n) {
-          const int slot = atomicAdd(&sh.ncand, 1);
-          if (slot < kCandCap) cand[slot] = pack_cand(order_key(l), c0 + e + q);
+        if ((cm >> (4 * j + q)) & 1ull) {
+          if (slot < kCandCap) cand[slot] = pack_cand(order_key(lane(v[j], q)), c0 + e + q);
+          ++slot;
         }
       }
     }
   }
 
-  __syncthreads();
   if (tid == 0) {
-    const bool ovf = sh.ncand > kCandCap;
+    const bool ovf = total > kCandCap;
     ChunkRec o;
     o.cmax = cmax;
     o.sumexp = s;
     o.tmass = tmass;
     o.kt = order_key(tf);
-    o.ncand = ovf ? 0 : sh.ncand;
+    o.ncand = ovf ? 0 : total;
     o.status = ovf ? 2 : 0;
     o.nkey = 0;  // the noise pass fills the Gumbel-key list
     o.kfloor = INFINITY;
