@@ -118,7 +118,7 @@ def test_gemm_slices_into_wide_buffer(dev, ts, gemm_tile):
 
 
 @pytest.mark.parametrize("name,tile", [("decode", ""), ("spec_decode", ""), ("large", ""),
-                                       ("spec_decode", "3"), ("large", "4")])
+                                       ("draft", ""), ("spec_decode", "3"), ("large", "4")])
 def test_gemm_full_size_sampled(dev, ts, name, tile, monkeypatch):
     """Full-size projection in the launch configuration the bench times,
     checked on sampled rows and columns (including the ragged tails)."""
@@ -248,7 +248,7 @@ def route(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "spec_decode", "rank_share", "large"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "spec_decode", "rank_share", "large", "draft"])
 def test_sampler_workloads(dev, ts, name, route):
     import torch
 
@@ -564,3 +564,36 @@ def test_sampler_one_slice_matches_buffer_call(dev, ts):
     b = _run_sampler_slices(ts, dev, logits, [V], params, 7, 6)
     for k in a:
         assert np.array_equal(a[k].view(np.uint32), b[k].view(np.uint32)), k
+
+
+@pytest.mark.parametrize("in_place", [True, False])
+def test_sampler_draft_share(dev, ts, in_place, route):
+    """Sharded draft logits: one tensor-parallel rank's share of the draft
+    step, received as eight vocabulary slices and sampled with the share's
+    global row offset, draws exactly the draft step's tokens for those rows."""
+    import torch
+
+    w = workloads.get("draft_share")
+    parent = workloads.get(w.parent)
+    exp = _load_expected(parent.name)
+    sl = slice(w.row_offset, w.row_offset + w.rows)
+    logits = workloads.make_logits(w)
+    params = workloads.make_params(w)
+    say("draft share", in_place, route, logits.shape, w.slice_cols[:2])
+    if in_place:
+        got = _run_sampler_slices(ts, dev, logits, w.slice_cols, params, w.row_offset,
+                                  w.max_logprobs)
+    else:
+        cuts = np.concatenate([[0], np.cumsum(w.slice_cols)])
+        full = torch.from_numpy(logits).to(dev)
+        slices = [full[:, a:b].contiguous() for a, b in zip(cuts[:-1], cuts[1:])]
+        batch = ts.sampler_assemble_vocab_slices(slices)
+        out = ts.sampler_sample(batch, ts.params_to_device(params, dev), w.row_offset,
+                                w.max_logprobs)
+        torch.cuda.synchronize()
+        got = {k: getattr(out, k).cpu().numpy() for k in
+               ("token_ids", "token_logprobs", "topn_ids", "topn_logprobs", "row_status")}
+    flagged = exp["flag_top_p"][sl] | exp["flag_tie"][sl]
+    _compare(got, exp["token_ids"][sl], exp["token_logprobs"][sl], exp["topn_ids"][sl],
+             exp["topn_logprobs"][sl], exp["row_status"][sl], flagged, exp["lse"][sl], logits,
+             max_frac=1.0, label="draft_share")

@@ -140,16 +140,20 @@ struct FastLayout {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Chunks per row: at most kChunkMax logits each, enough workgroups to fill
-// the chip (about 1024), chunks of at least 1024 logits, at most kMaxChunks;
-// every slice is cut into chunks of its own.  S == 0 marks a shape the chunked
-// path does not take.
+// Chunks per row: at most kChunkMax logits each, at least about one chunk
+// workgroup per compute unit (kWantChunks), chunks of at least 1024 logits, at
+// most kMaxChunks; every slice is cut into chunks of its own.  Few rows get no
+// more chunks than that: the merge of a row walks every chunk's candidates,
+// so for small batches it, not the read, sets the time.  S == 0 marks a shape
+// the chunked path does not take.
+constexpr int64_t kWantChunks = 256;
+
 inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n) {
   FastLayout l{};
   int64_t vocab = 0;
   for (int s = 0; s < n; ++s) vocab += cols[s];
   int64_t S = (vocab + kChunkMax - 1) / kChunkMax;
-  int64_t want = rows > 0 ? (1024 + rows - 1) / rows : 1;
+  int64_t want = rows > 0 ? (kWantChunks + rows - 1) / rows : 1;
   int64_t most = vocab / 1024 > 0 ? vocab / 1024 : 1;
   if (want > most) want = most;
   if (want > kMaxChunks) want = kMaxChunks;

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five sampling workloads.
+"""Seeded synthetic inputs for the sampling workloads.
 
 This module is the only code shared by the CPU oracle (``oracle/``) and the
 GPU path (``top_sampling_amd``).  It draws inputs and nothing else: it holds no
@@ -55,10 +55,16 @@ class Workload:
     requests: int | None = None
     spec_tokens: int = 0
     description: str = ""
+    # A rank's share of another workload: rows [row_offset, row_offset + rows)
+    # of `parent`, with the parent's logits and parameters.
+    parent: str | None = None
+    row_offset: int = 0
 
     @property
     def logit_std(self) -> float:
         """Standard deviation of one projected logit: sqrt(H) * sigma_x * sigma_w."""
+        if self.parent:
+            return WORKLOADS[self.parent].logit_std
         return math.sqrt(self.hidden) * self.x_std * self.w_std if self.hidden else 1.0
 
     @property
@@ -96,6 +102,23 @@ WORKLOADS: dict[str, Workload] = {
             description="1024 rows, H=8192, V=262144 bf16; quarters: greedy / p=0.95 / "
             "k=5 at T=1.5 / full vocabulary; 20 logprobs",
         ),
+        # The drafter's logits (page "Qwen4Exp batch-sharded sampling: inside
+        # vLLM PR #61018", section "What batch-sharded sampling is, in one
+        # paragraph": sharded draft logits are named as future work; the MTP
+        # drafter's logits path is flagged unverified): one draft position per
+        # request, the full vocabulary, the target's lm_head shape.
+        Workload(
+            "draft", 5, rows=128, vocab=151936, hidden=4096, x_std=1.0, w_std=0.02,
+            max_logprobs=0, requests=128,
+            description="draft step: 128 requests x 1 draft row, H=4096, V=151936 bf16; "
+            "per-request T~U[0,1.2], k in {0,1,20,50,1000}, p~U[0.5,1]; no top-N logprobs",
+        ),
+        Workload(
+            "draft_share", 5, rows=16, vocab=151936, hidden=None, max_logprobs=0, n_slices=8,
+            parent="draft", row_offset=48,
+            description="sharded draft logits, tp=8: rank 3's 16 draft rows (48-63 of the "
+            "draft step) received as 8 vocab slices of 18992, sampled with row_offset 48",
+        ),
     ]
 }
 
@@ -111,6 +134,8 @@ def _rng(w: Workload, stream: int) -> np.random.Generator:
 # ---------------------------------------------------------------- parameters
 def make_params(w: Workload) -> np.ndarray:
     """Per-row sampling parameters as a ``PARAMS_DTYPE`` record array."""
+    if w.parent:
+        return make_params(WORKLOADS[w.parent])[w.row_offset:w.row_offset + w.rows].copy()
     p = np.zeros(w.rows, dtype=PARAMS_DTYPE)
     g = _rng(w, 1)
     if w.name == "tiny":
@@ -123,14 +148,14 @@ def make_params(w: Workload) -> np.ndarray:
         p["top_p"] = 0.8
         p["n_logprobs"] = 5
         p["seed"] = g.integers(0, 2**64, size=w.rows, dtype=np.uint64)
-    elif w.name in ("spec_decode", "rank_share"):
+    elif w.name in ("spec_decode", "rank_share", "draft"):
         n_req = w.requests if w.requests else w.rows
         per = w.rows // n_req
         t = g.uniform(0.0, 1.2, size=n_req).astype(np.float32)
         k = g.choice(np.array([0, 1, 20, 50, 1000], dtype=np.int32), size=n_req)
         pp = g.uniform(0.5, 1.0, size=n_req).astype(np.float32)
         nl = (g.integers(0, 21, size=n_req) if w.name == "spec_decode"
-              else np.full(n_req, 5)).astype(np.int32)
+              else np.full(n_req, min(5, w.max_logprobs))).astype(np.int32)
         sd = g.integers(0, 2**64, size=n_req, dtype=np.uint64)
         for name, v in (("temperature", t), ("top_k", k), ("top_p", pp),
                         ("n_logprobs", nl), ("seed", sd)):
@@ -159,6 +184,10 @@ def make_logits(w: Workload, rows: slice | None = None) -> np.ndarray:
     (+15) in ceil(1% of rows) rows.  Rows are drawn from per-row streams, so a
     row range gives the same values as slicing the whole array.
     """
+    if w.parent:
+        rr = range(w.rows)[rows] if rows is not None else range(w.rows)
+        ro = w.row_offset
+        return make_logits(WORKLOADS[w.parent], slice(ro + rr.start, ro + rr.stop, rr.step))
     rr = range(w.rows)[rows] if rows is not None else range(w.rows)
     out = np.empty((len(rr), w.vocab), dtype=np.float32)
     for i, r in enumerate(rr):
