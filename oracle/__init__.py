@@ -41,7 +41,8 @@ in the design notes of the repository):
       seed and countered on (token id / 4, global row); lowest id on ties;
   R7  invalid parameters give row status 1, a NaN or +inf logit or a row
       with no finite logit gives row status 2; such rows return token -1 and
-      NaN log-probabilities; unused top-N slots hold id -1, log-prob -inf.
+      NaN log-probabilities; unused top-N slots hold id -1, log-prob -inf;
+  R10 the FP8 projection is W8A8 with per-row fp32 scales (see below).
 
 Parity of every function here is pinned by tests in ``tests/test_oracle_pins.py``
 (published Philox known-answer vectors, exact integer dot products, O(V^2)
@@ -90,6 +91,86 @@ def lmhead_logits(hidden_bits: np.ndarray, lm_head_bits: np.ndarray,
     for v0 in range(0, vocab, vocab_chunk):
         w = decode_bf16(lm_head_bits[v0:v0 + vocab_chunk])
         out[:, v0:v0 + w.shape[0]] = x @ w.T
+    return out
+
+
+# -------------------------------------------------------- FP8 projection
+# The pages' measured deployment is an FP8 checkpoint and their patch cluster
+# includes a kernel that unpacks e4m3 bytes (page "Qwen4Exp batch-sharded
+# sampling: inside vLLM PR #61018", sections "The 1.5% estimate, and the
+# measurement next to it" and "The patch cluster"); they state no scaling
+# scheme.  Reading R10: W8A8 with one fp32 scale per row on both operands --
+# every lm_head row and every hidden-state row is stored as OCP E4M3 codes
+# times its own scale amax / 448, and the projection sums the products of the
+# decoded codes and applies both scales.
+E4M3_MAX = 448.0
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP 8-bit floating point E4M3 (the variant without infinities) ->
+    float64: one sign bit, four exponent bits with bias 7, three mantissa
+    bits.  Exponent field 0 holds subnormals m/8 * 2^-6; the two all-ones
+    patterns (S.1111.111) are NaN; the largest magnitude is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS = decode_e4m3(np.arange(0x7F, dtype=np.uint8))  # codes 0x00..0x7E, increasing
+
+
+def encode_e4m3(x: np.ndarray) -> np.ndarray:
+    """The E4M3 code nearest to each value; halfway cases go to the code with
+    an even mantissa; magnitudes of 448 and above (infinities included)
+    saturate to 448; NaN gives 0x7F.  The sign bit is the input's, so -0.0
+    gives 0x80."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = np.abs(a - _E4M3_POS[lo])
+    d_hi = np.abs(_E4M3_POS[hi] - a)
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a >= E4M3_MAX, 0x7E, pick)
+    code = pick.astype(np.uint8) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_rows_e4m3(bits: np.ndarray):
+    """bf16 ``[rows, cols]`` -> (E4M3 codes ``[rows, cols]``, fp32 scales ``[rows]``).
+
+    Per row: amax = the largest |x| (NaN ignored), scale = amax / 448 in fp32
+    (1 for a row of zeros), code = encode_e4m3(x / scale) with the division in
+    fp32.  The codes are decided in fp32 because the kernel divides in fp32; a
+    float64 quotient could round to a different code."""
+    x32 = decode_bf16(bits).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        amax = np.nanmax(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
+    amax = np.nan_to_num(amax, nan=0.0).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        q = (x32 / scale[:, None]).astype(np.float32)
+    return encode_e4m3(q.astype(np.float64)), scale
+
+
+def lmhead_logits_e4m3(hidden_codes: np.ndarray, hidden_scales: np.ndarray,
+                       lm_head_codes: np.ndarray, lm_head_scales: np.ndarray,
+                       vocab_chunk: int = 8192) -> np.ndarray:
+    """logits[r, v] = s_x[r] * s_w[v] * sum_h dec(X[r, h]) * dec(W[v, h]) in
+    float64, over the rank's own vocabulary slice (no gather)."""
+    x = decode_e4m3(hidden_codes)
+    xs = np.asarray(hidden_scales, dtype=np.float64)
+    vocab = lm_head_codes.shape[0]
+    assert lm_head_codes.shape[1] == x.shape[1]
+    out = np.empty((x.shape[0], vocab), dtype=np.float64)
+    for v0 in range(0, vocab, vocab_chunk):
+        w = decode_e4m3(lm_head_codes[v0:v0 + vocab_chunk])
+        ws = np.asarray(lm_head_scales[v0:v0 + vocab_chunk], dtype=np.float64)
+        out[:, v0:v0 + w.shape[0]] = (x @ w.T) * xs[:, None] * ws[None, :]
     return out
 
 

@@ -343,3 +343,105 @@ def test_workload_params_in_domain():
         for r in p:
             assert oracle.params_valid(float(r["temperature"]), int(r["top_k"]),
                                        float(r["top_p"]), int(r["n_logprobs"]), w.max_logprobs)
+
+
+# ------------------------------------------------------------- FP8 (E4M3)
+def test_e4m3_decode_matches_torch_and_the_format():
+    """Every code against torch's float8_e4m3fn (a library decoding of the
+    same OCP format), plus values fixed by the bit layout itself."""
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    d = oracle.decode_e4m3(codes)
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(d), np.isnan(t))
+    assert np.array_equal(d[~np.isnan(d)], t[~np.isnan(t)])
+    assert np.isnan(d).sum() == 2 and np.isnan(d[0x7F]) and np.isnan(d[0xFF])
+    fixed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, v in fixed.items():
+        assert d[c] == v, hex(c)
+    assert np.signbit(d[0x80]) and d[0x80] == 0.0
+
+
+def test_e4m3_encode_round_trip_and_saturation():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(oracle.encode_e4m3(oracle.decode_e4m3(codes)), codes)
+    big = np.array([448.0, 449.0, 463.9, 464.0, 1e6, np.inf, -500.0, -np.inf])
+    assert oracle.encode_e4m3(big).tolist() == [0x7E] * 6 + [0xFE] * 2
+    assert oracle.encode_e4m3(np.array([np.nan]))[0] == 0x7F
+
+
+def test_e4m3_encode_matches_torch_rounding():
+    """Nearest code with ties to even, against torch's conversion, on random
+    values, every exact midpoint between neighbouring codes, and the
+    subnormal range (all inside +-448, where torch does not overflow)."""
+    import torch
+
+    rng = np.random.default_rng(5)
+    pos = oracle.decode_e4m3(np.arange(0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = np.concatenate([
+        rng.uniform(-448, 448, 20000), rng.normal(0, 1, 20000), rng.uniform(-2 ** -6, 2 ** -6, 5000),
+        mids, -mids, pos, np.nextafter(mids, 0), np.nextafter(mids, 1000)]).astype(np.float32)
+    got = oracle.encode_e4m3(vals.astype(np.float64))
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:5]
+
+
+def _bf16_bits(x):
+    x32 = np.asarray(x, dtype=np.float32)
+    u = x32.view(np.uint32)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def test_e4m3_quantize_rows_definition():
+    """Per-row amax scaling written out element by element in fp32, and the
+    properties the scheme guarantees: the amax element lands on +-448, a zero
+    row gets scale 1 and zero codes, and decoding reproduces the row within
+    half an E4M3 step."""
+    import struct
+
+    rng = np.random.default_rng(9)
+    x = rng.normal(0, 3, size=(6, 40)).astype(np.float32)
+    x[2] = 0.0
+    x[3, 5] = 1e-30
+    x[4, :3] = [-7.0, 0.0, 7.0]
+    bits = _bf16_bits(x)
+    codes, scales = oracle.quantize_rows_e4m3(bits)
+    xb = oracle.decode_bf16(bits)
+    f32 = lambda v: struct.unpack("f", struct.pack("f", v))[0]  # noqa: E731
+    for r in range(x.shape[0]):
+        amax = max(abs(v) for v in xb[r])
+        s = f32(f32(amax) / 448.0) if amax > 0 else 1.0
+        assert scales[r] == np.float32(s)
+        for h in range(x.shape[1]):
+            q = f32(f32(xb[r, h]) / s)
+            assert codes[r, h] == oracle.encode_e4m3(np.array([q]))[0]
+        dec = oracle.decode_e4m3(codes[r]) * s
+        if amax > 0:
+            assert np.max(np.abs(oracle.decode_e4m3(codes[r]))) == 448.0
+            rel = np.abs(dec - xb[r]) / np.maximum(np.abs(xb[r]), 2.0 ** -6 * s)
+            assert rel.max() <= 2.0 ** -4 + 1e-12
+    assert scales[2] == 1.0 and not codes[2].any()
+
+
+def test_e4m3_projection_exact_on_integer_codes():
+    """Codes whose values are small integers and power-of-two scales make every
+    product and sum exact: the oracle must equal an integer matmul scaled by
+    the two scales, element for element (a transposed operand or a dropped
+    scale breaks it)."""
+    rng = np.random.default_rng(13)
+    ints = np.arange(-8, 9)
+    enc = {int(v): int(oracle.encode_e4m3(np.array([float(v)]))[0]) for v in ints}
+    xi = rng.integers(-8, 9, size=(5, 64))
+    wi = rng.integers(-8, 9, size=(37, 64))
+    xc = np.vectorize(enc.get)(xi).astype(np.uint8)
+    wc = np.vectorize(enc.get)(wi).astype(np.uint8)
+    xs = 2.0 ** rng.integers(-6, 3, size=5)
+    ws = 2.0 ** rng.integers(-9, 1, size=37)
+    got = oracle.lmhead_logits_e4m3(xc, xs.astype(np.float32), wc, ws.astype(np.float32),
+                                    vocab_chunk=16)
+    want = (xi @ wi.T).astype(np.float64) * xs[:, None] * ws[None, :]
+    assert np.array_equal(got, want)
