@@ -13,7 +13,9 @@ After the timed steps, sampler_sample_slices (the sampler reading the slices
 in place, with no stitching copy) is timed on its own over the same number of
 steps and reported beside the per-kernel times.
 Default workload: speculative decode, 128 requests x (4 draft + 1) = 640 rows,
-H = 4096, V = 151,936 (4 slices of 37,984).
+H = 4096, V = 151,936 (4 slices of 37,984).  --workload fp8 runs the pages'
+model shape (H = 2560, V = 248,320 in 8 slices) with an FP8 lm_head: each
+step quantizes the hidden states per row and projects with the E4M3 kernel.
 
 Prints one JSON line.  Per-kernel times come from HIP events recorded on the
 stream the kernels are launched on, over the timed region.
@@ -32,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "sampled rows/s + sampler HBM GB/s + lm_head TFLOP/s at 640 rows x V=151,936"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 def parse():
@@ -41,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="spec_decode",
                     choices=["decode", "spec_decode", "rank_share", "large", "draft",
-                             "draft_share"])
+                             "draft_share", "fp8"])
     ap.add_argument("--slices", type=int, default=4, help="vocabulary slices (TP ranks)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640,
@@ -49,32 +52,49 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(x, wt, logits_sample, params, max_logprobs, rows: int):
+def cpu_baseline(x, wt, wq, wsc, logits_sample, params, max_logprobs, rows: int):
     """The CPU oracle as it stands, timed on a bounded sample of the workload:
-    the float64 projection of `rows` rows against the whole lm_head, then the
-    full-sort sampler on those rows.  Scaled to rows/s."""
+    the float64 projection of `rows` rows against the whole lm_head (for the
+    FP8 workload: the oracle's per-row quantization of those rows, then its
+    projection from the same lm_head codes the GPU uses), then the full-sort
+    sampler on those rows.  Scaled to rows/s."""
     import numpy as np
     import threadpoolctl
 
     import oracle
 
     torch = __import__("torch")
-    xb = x[:rows].view(torch.int16).cpu().numpy().view(np.uint16) if x is not None else None
-    wb = wt.view(torch.int16).cpu().numpy().view(np.uint16) if wt is not None else None
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa: E731
+    xb = bits(x[:rows]) if x is not None else None
+    if wq is not None:
+        wc, ws = wq.cpu().numpy().view(np.uint8), wsc.cpu().numpy()
+
+        def project():
+            q, s = oracle.quantize_rows_e4m3(xb)
+            oracle.lmhead_logits_e4m3(q, s, wc, ws)
+        what = "FP8 quantization and float64 projection"
+    elif wt is not None:
+        wb = bits(wt)
+
+        def project():
+            oracle.lmhead_logits(xb, wb)
+        what = "float64 projection"
+    else:
+        project = None
     threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
         if threadpoolctl.threadpool_info() else 1
     t0 = time.perf_counter()
-    if wb is not None:
-        oracle.lmhead_logits(xb, wb)
+    if project is not None:
+        project()
     t1 = time.perf_counter()
     oracle.sample(logits_sample[:rows], params[:rows], 0, max_logprobs)
     t2 = time.perf_counter()
-    proj = (f"float64 projection against the full lm_head ({t1 - t0:.1f}s, BLAS threads "
-            f"{threads}) + " if wb is not None else "")
+    proj = (f"{what} against the full lm_head ({t1 - t0:.1f}s, BLAS threads {threads}) + "
+            if project is not None else "")
     return {
         "value": rows / (t2 - t0),
         "unit": "rows/s",
-        "cores": int(threads) if wb is not None else 1,
+        "cores": int(threads) if project is not None else 1,
         "kind": "oracle",
         "sample": f"{rows} rows: {proj}full-sort sampler ({t2 - t1:.1f}s, 1 thread)",
     }
@@ -125,13 +145,20 @@ def main():
 
     params_np = workloads.make_params(w)
     params = ts.params_to_device(params_np, dev)
-    n_sl = w.n_slices if w.hidden is None else args.slices
+    n_sl = w.n_slices if (w.hidden is None or w.n_slices > 1) else args.slices
     base, rem = divmod(vocab, n_sl)
     widths = [base + (1 if s < rem else 0) for s in range(n_sl)]
     cuts = np.concatenate([[0], np.cumsum(widths)])
 
+    xq = xsc = wq = wsc = None
     if w.hidden is not None:
         x, wt = workloads.make_projection_device(w, dev)
+        if w.fp8:
+            # The checkpoint's FP8 lm_head: quantized once, outside the timed steps.
+            wq, wsc = ts.quantize_rows_e4m3(wt)
+            xq = torch.empty(rows, w.hidden, dtype=torch.uint8, device=dev)
+            xsc = torch.empty(rows, dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
         local = torch.empty(rows, vocab, dtype=torch.float32, device=dev)
         slices = [local[:, a:b] for a, b in zip(cuts[:-1], cuts[1:])]
     else:
@@ -144,7 +171,12 @@ def main():
     ws = ts.allocate_workspace(rows, vocab, w.max_logprobs, dev)
 
     def step(ev=None):
-        if x is not None:
+        if x is not None and w.fp8:
+            ts.quantize_rows_e4m3(x, out=xq, scales=xsc, stream=stream)
+            if ev is not None:
+                ev[4].record(stream)
+            ts.lmhead_logits_local_e4m3(xq, xsc, wq, wsc, out=local, stream=stream)
+        elif x is not None:
             ts.lmhead_logits_local(x, wt, out=local, stream=stream)
         if ev is not None:
             ev[0].record(stream)
@@ -158,7 +190,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -168,7 +200,12 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    gemm_ms = sum(e[3].elapsed_time(e[0]) for e in evs) / args.steps
+    if w.fp8:  # event 4 separates the per-step quantization of the hidden states
+        quant_ms = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
+        gemm_ms = sum(e[4].elapsed_time(e[0]) for e in evs) / args.steps
+    else:
+        quant_ms = None
+        gemm_ms = sum(e[3].elapsed_time(e[0]) for e in evs) / args.steps
     asm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     smp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
 
@@ -202,17 +239,21 @@ def main():
     asm_gbs = asm_bytes / (asm_ms * 1e-3) / 1e9
     # The projection's algorithmic bytes: hidden and lm_head read once, logits
     # written once.  Below the ridge (peak flop/s over peak bytes/s) HBM bounds it.
-    gemm_bytes = (2.0 * rows * w.hidden + 2.0 * vocab * w.hidden + 4.0 * rows * vocab
-                  if w.hidden else 0.0)
-    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    # FP8 operands are one byte per element plus one fp32 scale per row.
+    eb = 1.0 if w.fp8 else 2.0
+    gemm_bytes = (eb * rows * w.hidden + eb * vocab * w.hidden + 4.0 * rows * vocab
+                  + (4.0 * (rows + vocab) if w.fp8 else 0.0) if w.hidden else 0.0)
+    peak_tf = FP8_PEAK_TFLOPS if w.fp8 else BF16_PEAK_TFLOPS
+    gemm_kernel = "lmhead_e4m3" if w.fp8 else "lmhead_gemm"
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBS * 1e9)
     if flops and flops / gemm_bytes >= ridge:
-        roof = {"kernel": "lmhead_gemm", "bound": "mfma", "achieved": round(gemm_tflops, 1),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4),
+        roof = {"kernel": gemm_kernel, "bound": "mfma", "achieved": round(gemm_tflops, 1),
+                "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(gemm_tflops / peak_tf, 4),
                 "traffic": recorded_traffic(w.name)}
     elif flops:
         gemm_gbs = gemm_bytes / (gemm_ms * 1e-3) / 1e9
-        roof = {"kernel": "lmhead_gemm", "bound": "hbm", "achieved": round(gemm_gbs, 1),
+        roof = {"kernel": gemm_kernel, "bound": "hbm", "achieved": round(gemm_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(w.name)}
     else:
@@ -233,14 +274,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3" if w.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "rows": rows, "hidden": w.hidden, "vocab": vocab,
                    "vocab_slices": n_sl, "max_logprobs": w.max_logprobs,
                    "description": w.description},
         "kernels": {
-            "lmhead_gemm": {"ms": round(gemm_ms, 4), "tflops": gemm_tflops and round(gemm_tflops, 1),
-                            "frac_mfma_peak": gemm_tflops and round(gemm_tflops / BF16_PEAK_TFLOPS, 4)},
+            gemm_kernel: {"ms": round(gemm_ms, 4), "tflops": gemm_tflops and round(gemm_tflops, 1),
+                          "frac_mfma_peak": gemm_tflops and round(gemm_tflops / peak_tf, 4)},
             "assemble": {"ms": round(asm_ms, 4), "gbs": round(asm_gbs, 1),
                          "frac_hbm_peak": round(asm_gbs / HBM_PEAK_GBS, 4)},
             "sampler": {"ms": round(smp_ms, 4), "gbs": round(smp_gbs, 1),
@@ -253,10 +294,12 @@ def main():
         },
         "roofline": roof,
     }
+    if quant_ms is not None:
+        line["kernels"]["quantize_hidden"] = {"ms": round(quant_ms, 4)}
     if not args.no_cpu_baseline:
         sample_rows = min(args.cpu_rows, rows)
         logits_sample = batch[:sample_rows].cpu().numpy()
-        line["cpu_baseline"] = cpu_baseline(x, wt, logits_sample, params_np, w.max_logprobs,
+        line["cpu_baseline"] = cpu_baseline(x, wt, wq, wsc, logits_sample, params_np, w.max_logprobs,
                                             sample_rows)
     print(json.dumps(line), flush=True)
 

@@ -115,6 +115,46 @@ int lmhead_logits_local(const void* hidden, int64_t rows, int64_t hidden_dim,
                         void* stream);
 
 /*
+ * FP8 projection.  The pages' measured deployment is an FP8 checkpoint and
+ * their patch cluster unpacks e4m3 bytes (sections "The 1.5% estimate, and
+ * the measurement next to it" and "The patch cluster"); they state no
+ * scaling scheme.  Reading: W8A8 with one fp32 scale per row on both
+ * operands.  A row x is held as OCP E4M3 codes q (one byte each; no
+ * infinities, largest magnitude 448, 0x7F/0xFF NaN) with x ~ s * dec(q),
+ * s = max|x| / 448.
+ *
+ * quantize_rows_e4m3: per-row dynamic quantization of bf16 data:
+ *   scales[r] = max_c |in[r, c]| / 448 in fp32 (NaN ignored; 1 for a row
+ *   of zeros); out[r, c] = the E4M3 code nearest in[r, c] / scales[r]
+ *   (quotient in fp32), ties to the even code, saturating at +-448, NaN ->
+ *   0x7F.
+ *   in      bf16 [rows, cols], leading dimension ld_in (elements)
+ *   out     codes [rows, cols], leading dimension ld_out (bytes)
+ *   scales  fp32 [rows]
+ * Caller-owned device buffers; in 2-byte and scales 4-byte aligned.
+ *
+ * lmhead_logits_local_e4m3: logits[r, v] = hidden_scales[r] *
+ *   lm_head_scales[v] * sum_h dec(hidden[r, h]) * dec(lm_head[v, h]),
+ *   fp32 accumulation (every product of two E4M3 values is exact in fp32),
+ *   over the rank's own vocabulary slice, never gathered.
+ *   hidden          codes [rows, hidden_dim], leading dimension ld_hidden
+ *   hidden_scales   fp32 [rows]
+ *   lm_head         codes [vocab_local, hidden_dim], leading dimension ld_lm_head
+ *   lm_head_scales  fp32 [vocab_local]
+ *   logits          fp32 [rows, vocab_local], leading dimension ld_logits
+ * Requirements (else TS_EUNSUPPORTED): hidden_dim a multiple of 128,
+ * ld_hidden and ld_lm_head multiples of 16, codes 16-byte aligned, logits
+ * and scales 4-byte aligned.  Other errors and the empty cases as for
+ * lmhead_logits_local.
+ */
+int quantize_rows_e4m3(const void* in, int64_t rows, int64_t cols, int64_t ld_in, void* out,
+                       int64_t ld_out, float* scales, void* stream);
+int lmhead_logits_local_e4m3(const void* hidden, const float* hidden_scales, int64_t rows,
+                             int64_t hidden_dim, int64_t ld_hidden, const void* lm_head,
+                             const float* lm_head_scales, int64_t vocab_local, int64_t ld_lm_head,
+                             float* logits, int64_t ld_logits, void* stream);
+
+/*
  * sampler_workspace_bytes: device workspace sampler_sample needs for these
  * sizes (host-only computation; callable without a GPU).
  */

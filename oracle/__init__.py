@@ -147,10 +147,13 @@ def quantize_rows_e4m3(bits: np.ndarray):
     (1 for a row of zeros), code = encode_e4m3(x / scale) with the division in
     fp32.  The codes are decided in fp32 because the kernel divides in fp32; a
     float64 quotient could round to a different code."""
+    import warnings
+
     x32 = decode_bf16(bits).astype(np.float32)
-    with np.errstate(invalid="ignore"):
+    with np.errstate(invalid="ignore"), warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)  # a row of NaN: amax NaN -> 0 below
         amax = np.nanmax(np.abs(x32), axis=1) if x32.shape[1] else np.zeros(x32.shape[0], np.float32)
-    amax = np.nan_to_num(amax, nan=0.0).astype(np.float32)
+    amax = np.where(np.isnan(amax), np.float32(0.0), amax).astype(np.float32)
     scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
     with np.errstate(invalid="ignore", divide="ignore"):
         q = (x32 / scale[:, None]).astype(np.float32)

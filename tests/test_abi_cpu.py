@@ -217,3 +217,47 @@ def test_slices_workspace_query():
     assert ts.sampler_workspace_bytes_slices(640, [], 20) == 0
     assert ts.sampler_workspace_bytes_slices(640, [10, -1], 20) == 0
     assert ts.sampler_workspace_bytes_slices(640, [4] * 65, 20) == 0
+
+
+def _gemm8(**kw):
+    a = dict(hidden=FAKE, xs=FAKE, rows=4, hidden_dim=256, ld_hidden=256, lm_head=FAKE, ws=FAKE,
+             vocab=64, ld_lm_head=256, logits=FAKE, ld_logits=64)
+    a.update(kw)
+    return ts.lib.lmhead_logits_local_e4m3(a["hidden"], a["xs"], a["rows"], a["hidden_dim"],
+                                           a["ld_hidden"], a["lm_head"], a["ws"], a["vocab"],
+                                           a["ld_lm_head"], a["logits"], a["ld_logits"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=-1), ts.TS_EINVAL),
+    (dict(hidden=None), ts.TS_EINVAL),
+    (dict(xs=None), ts.TS_EINVAL),
+    (dict(ws=None), ts.TS_EINVAL),
+    (dict(ld_hidden=128), ts.TS_EINVAL),
+    (dict(ld_logits=63), ts.TS_EINVAL),
+    (dict(hidden_dim=0), ts.TS_EINVAL),
+    (dict(hidden_dim=192, ld_hidden=256, ld_lm_head=256), ts.TS_EUNSUPPORTED),   # not x128
+    (dict(ld_hidden=264), ts.TS_EUNSUPPORTED),                                  # not x16
+    (dict(hidden=FAKE + 8), ts.TS_EUNSUPPORTED),
+    (dict(xs=FAKE + 2), ts.TS_EUNSUPPORTED),
+    (dict(vocab=1 << 31), ts.TS_EUNSUPPORTED),
+])
+def test_gemm_e4m3_validation(kw, code):
+    assert _gemm8(**kw) == code
+    assert ts.lib.ts_last_error()
+
+
+def test_gemm_e4m3_empty_is_noop():
+    assert _gemm8(rows=0, hidden=None, xs=None) == ts.TS_OK
+    assert _gemm8(vocab=0) == ts.TS_OK
+
+
+def test_quantize_e4m3_validation():
+    q = ts.lib.quantize_rows_e4m3
+    assert q(FAKE, -1, 8, 8, FAKE, 8, FAKE, None) == ts.TS_EINVAL
+    assert q(FAKE, 4, 8, 7, FAKE, 8, FAKE, None) == ts.TS_EINVAL      # ld_in < cols
+    assert q(FAKE, 4, 8, 8, FAKE, 7, FAKE, None) == ts.TS_EINVAL      # ld_out < cols
+    assert q(None, 4, 8, 8, FAKE, 8, FAKE, None) == ts.TS_EINVAL
+    assert q(FAKE, 4, 8, 8, FAKE, 8, None, None) == ts.TS_EINVAL
+    assert q(FAKE + 1, 4, 8, 8, FAKE, 8, FAKE, None) == ts.TS_EUNSUPPORTED
+    assert q(None, 0, 8, 8, None, 8, None, None) == ts.TS_OK

@@ -248,7 +248,8 @@ def route(request, monkeypatch):
     return request.param
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode", "spec_decode", "rank_share", "large", "draft"])
+@pytest.mark.parametrize("name", ["tiny", "decode", "spec_decode", "rank_share", "large", "draft",
+                                  "fp8"])
 def test_sampler_workloads(dev, ts, name, route):
     import torch
 
@@ -470,7 +471,7 @@ def _even_widths(V, n, align=1):
 
 
 @pytest.mark.parametrize("name,n", [("spec_decode", 4), ("spec_decode", 8), ("rank_share", 0),
-                                    ("large", 8)])
+                                    ("large", 8), ("fp8", 0)])
 def test_sampler_slices_workloads(dev, ts, name, n, route):
     """The receive side without the stitching copy: the sampler reads the
     vocabulary slices where the exchange left them."""

@@ -427,6 +427,20 @@ def test_e4m3_quantize_rows_definition():
     assert scales[2] == 1.0 and not codes[2].any()
 
 
+def test_e4m3_quantize_rows_non_finite():
+    """The scale follows amax = the largest |x| with NaN ignored: +inf makes it
+    infinite (finite values then code as signed zeros, inf itself as NaN), a
+    row of NaN gets scale 1 and NaN codes."""
+    x = np.array([[np.inf, 5.0, -0.0, -3.0],
+                  [np.nan, np.nan, np.nan, np.nan],
+                  [np.nan, 2.0, -448.0, 0.5]], dtype=np.float32)
+    codes, scales = oracle.quantize_rows_e4m3(_bf16_bits(x))
+    assert np.isinf(scales[0]) and scales[1] == 1.0 and scales[2] == 1.0
+    assert codes[0].tolist() == [0x7F, 0x00, 0x80, 0x80]
+    assert codes[1].tolist() == [0x7F] * 4
+    assert codes[2].tolist() == [0x7F, 0x40, 0xFE, 0x30]
+
+
 def test_e4m3_projection_exact_on_integer_codes():
     """Codes whose values are small integers and power-of-two scales make every
     product and sum exact: the oracle must equal an integer matmul scaled by

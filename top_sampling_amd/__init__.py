@@ -7,6 +7,8 @@ not built (``python top_sampling_amd/build.py``); there is no fallback.
 
 Calls mirror the C entry points:
   lmhead_logits_local            local vocabulary projection, bf16 -> fp32
+  quantize_rows_e4m3             per-row FP8 (E4M3) quantization of bf16 rows
+  lmhead_logits_local_e4m3       the same projection from FP8 codes and scales
   sampler_assemble_vocab_slices  stitch received vocabulary slices
   sampler_sample                 per-row temperature / top-k / top-p /
                                  logprobs / Gumbel-max sampling
@@ -39,6 +41,9 @@ PARAMS_BYTES = 24
 _VP, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 SYMBOLS = {
     "lmhead_logits_local": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _VP]),
+    "quantize_rows_e4m3": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP]),
+    "lmhead_logits_local_e4m3": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, _VP, _VP, _I64, _I64,
+                                                _VP, _I64, _VP]),
     "sampler_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "sampler_sample": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _I32, _VP, _VP, _VP, _VP,
                                       _VP, _VP, _SZ, _VP]),
@@ -135,6 +140,44 @@ def compute_logits_local(hidden, lm_head, out=None, stream=None):
     """The rank's own vocabulary shard ``[rows, V_local]``: no gather, no
     full-vocabulary buffer anywhere."""
     return lmhead_logits_local(hidden, lm_head, out=out, stream=stream)
+
+
+# ---------------------------------------------------------- FP8 projection
+def quantize_rows_e4m3(x, out=None, scales=None, stream=None):
+    """bf16 ``[rows, cols]`` -> (uint8 E4M3 codes ``[rows, cols]``, fp32 per-row
+    scales ``[rows]``): scale = max|x| / 448, code = nearest E4M3 of x / scale."""
+    torch = _torch()
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be bf16 [rows, cols] with unit column stride")
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty(rows, cols, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    _check(lib.quantize_rows_e4m3(_ptr(x), rows, cols, x.stride(0), _ptr(out), out.stride(0),
+                                  _ptr(scales), _stream_ptr(stream)))
+    return out, scales
+
+
+def lmhead_logits_local_e4m3(hidden, hidden_scales, lm_head, lm_head_scales, out=None,
+                             stream=None):
+    """fp32 ``[rows, V_local]`` = s_x[r] * s_w[v] * (codes_x @ codes_w^T) for
+    uint8 E4M3 codes ``hidden [rows, H]``, ``lm_head [V_local, H]`` and fp32
+    per-row scales: the rank's own vocabulary slice, no gather."""
+    torch = _torch()
+    rows, h = hidden.shape
+    vocab, h2 = lm_head.shape
+    if h != h2 or hidden.dtype != torch.uint8 or lm_head.dtype != torch.uint8:
+        raise ValueError("hidden and lm_head must be uint8 codes with the same hidden size")
+    if hidden.stride(1) != 1 or lm_head.stride(1) != 1:
+        raise ValueError("codes must have unit column stride")
+    if out is None:
+        out = torch.empty(rows, vocab, dtype=torch.float32, device=hidden.device)
+    _check(lib.lmhead_logits_local_e4m3(
+        _ptr(hidden), _ptr(hidden_scales), rows, h, hidden.stride(0), _ptr(lm_head),
+        _ptr(lm_head_scales), vocab, lm_head.stride(0), _ptr(out), out.stride(0),
+        _stream_ptr(stream)))
+    return out
 
 
 # ------------------------------------------------------------------ assembly

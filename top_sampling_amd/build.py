@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtopsampling.so")
-SOURCES = ["api.hip", "lmhead_gemm.hip", "sampler_fast.hip", "sampler_exact.hip", "assemble.hip"]
+SOURCES = ["api.hip", "lmhead_gemm.hip", "lmhead_fp8.hip", "sampler_fast.hip", "sampler_exact.hip",
+           "assemble.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -73,6 +73,57 @@ int lmhead_logits_local(const void* hidden, int64_t rows, int64_t hidden_dim, in
   return hip_status(e, "lmhead_logits_local launch");
 }
 
+int quantize_rows_e4m3(const void* in, int64_t rows, int64_t cols, int64_t ld_in, void* out,
+                       int64_t ld_out, float* scales, void* stream) {
+  if (rows < 0 || cols < 0)
+    return fail(TS_EINVAL, "negative size (rows=%lld cols=%lld)", (long long)rows,
+                (long long)cols);
+  if (rows > kMaxDim || cols > kMaxDim) return fail(TS_EUNSUPPORTED, "size above 2^31-1");
+  if (rows == 0) return TS_OK;
+  if (!in || !out || !scales) return fail(TS_EINVAL, "NULL pointer");
+  if (ld_in < cols || ld_out < cols)
+    return fail(TS_EINVAL, "leading dimension below the row width (ld_in=%lld ld_out=%lld)",
+                (long long)ld_in, (long long)ld_out);
+  if (!aligned(in, 2) || !aligned(scales, 4))
+    return fail(TS_EUNSUPPORTED, "input must be 2-byte aligned, scales 4-byte aligned");
+  const hipError_t e = ts::launch_quantize_rows_e4m3(
+      static_cast<const uint16_t*>(in), ld_in, static_cast<int>(rows), static_cast<int>(cols),
+      static_cast<uint8_t*>(out), ld_out, scales, static_cast<hipStream_t>(stream));
+  return hip_status(e, "quantize_rows_e4m3 launch");
+}
+
+int lmhead_logits_local_e4m3(const void* hidden, const float* hidden_scales, int64_t rows,
+                             int64_t hidden_dim, int64_t ld_hidden, const void* lm_head,
+                             const float* lm_head_scales, int64_t vocab_local, int64_t ld_lm_head,
+                             float* logits, int64_t ld_logits, void* stream) {
+  if (rows < 0 || vocab_local < 0 || hidden_dim < 0)
+    return fail(TS_EINVAL, "negative size (rows=%lld vocab_local=%lld hidden_dim=%lld)",
+                (long long)rows, (long long)vocab_local, (long long)hidden_dim);
+  if (rows > kMaxDim || vocab_local > kMaxDim || hidden_dim > kMaxDim)
+    return fail(TS_EUNSUPPORTED, "size above 2^31-1");
+  if (rows == 0 || vocab_local == 0) return TS_OK;
+  if (hidden_dim == 0) return fail(TS_EINVAL, "hidden_dim == 0 with a non-empty output");
+  if (!hidden || !lm_head || !logits || !hidden_scales || !lm_head_scales)
+    return fail(TS_EINVAL, "NULL pointer");
+  if (ld_hidden < hidden_dim || ld_lm_head < hidden_dim || ld_logits < vocab_local)
+    return fail(TS_EINVAL, "leading dimension below the row width (ld_hidden=%lld ld_lm_head=%lld "
+                "ld_logits=%lld)", (long long)ld_hidden, (long long)ld_lm_head,
+                (long long)ld_logits);
+  if (hidden_dim % 128 || ld_hidden % 16 || ld_lm_head % 16)
+    return fail(TS_EUNSUPPORTED,
+                "hidden_dim must be a multiple of 128, ld_hidden and ld_lm_head of 16");
+  if (!aligned(hidden, 16) || !aligned(lm_head, 16) || !aligned(logits, 4) ||
+      !aligned(hidden_scales, 4) || !aligned(lm_head_scales, 4))
+    return fail(TS_EUNSUPPORTED,
+                "codes must be 16-byte aligned, logits and scales 4-byte aligned");
+  const hipError_t e = ts::launch_lmhead_e4m3(
+      static_cast<const uint8_t*>(hidden), hidden_scales, ld_hidden,
+      static_cast<const uint8_t*>(lm_head), lm_head_scales, ld_lm_head, logits, ld_logits,
+      static_cast<int>(rows), static_cast<int>(vocab_local), static_cast<int>(hidden_dim),
+      static_cast<hipStream_t>(stream));
+  return hip_status(e, "lmhead_logits_local_e4m3 launch");
+}
+
 size_t sampler_workspace_bytes(int64_t rows, int64_t vocab, int32_t max_logprobs) {
   if (rows < 0 || vocab < 0 || max_logprobs < 0) return 0;
   return ts::sampler_workspace_size(rows, &vocab, 1, max_logprobs);

@@ -15,6 +15,16 @@ hipError_t launch_lmhead_gemm(const uint16_t* hidden, int64_t ld_hidden, const u
                               int64_t ld_lm_head, float* logits, int64_t ld_logits, int rows,
                               int vocab, int hidden_dim, hipStream_t stream);
 
+// FP8 (OCP E4M3) projection with per-row fp32 scales, and the per-row
+// quantization of bf16 hidden states into that form.
+hipError_t launch_quantize_rows_e4m3(const uint16_t* in, int64_t ld_in, int rows, int cols,
+                                     uint8_t* out, int64_t ld_out, float* scales,
+                                     hipStream_t stream);
+hipError_t launch_lmhead_e4m3(const uint8_t* hidden, const float* hidden_scales, int64_t ld_hidden,
+                              const uint8_t* lm_head, const float* lm_head_scales,
+                              int64_t ld_lm_head, float* logits, int64_t ld_logits, int rows,
+                              int vocab, int hidden_dim, hipStream_t stream);
+
 // ------------------------------------------------------------------- sampler
 // The sampler's logits: n column slices side by side, slice s holding global
 // columns [off[s], off[s + 1]) of every row at ptr[s] + row * ld[s].  A single

@@ -59,6 +59,9 @@ class Workload:
     # of `parent`, with the parent's logits and parameters.
     parent: str | None = None
     row_offset: int = 0
+    # The projection runs in FP8: bf16 draws quantized per row to OCP E4M3
+    # codes with fp32 scales (lm_head once, hidden states every step).
+    fp8: bool = False
 
     @property
     def logit_std(self) -> float:
@@ -113,6 +116,19 @@ WORKLOADS: dict[str, Workload] = {
             description="draft step: 128 requests x 1 draft row, H=4096, V=151936 bf16; "
             "per-request T~U[0,1.2], k in {0,1,20,50,1000}, p~U[0.5,1]; no top-N logprobs",
         ),
+        # The pages' model shape with its FP8 checkpoint (page "Qwen4Exp
+        # batch-sharded sampling: inside vLLM PR #61018", sections "The patch
+        # cluster" -- vocabulary 248,320, hidden size 2,560 -- and "The 1.5%
+        # estimate, and the measurement next to it" -- FP8 weights, tensor
+        # parallelism 8): the spec-decode batch, eight vocabulary slices of
+        # 31,040.
+        Workload(
+            "fp8", 6, rows=640, vocab=248320, hidden=2560, x_std=1.0, w_std=0.02,
+            max_logprobs=20, n_slices=8, requests=128, spec_tokens=4, fp8=True,
+            description="128 requests x (4 draft + 1) = 640 rows, H=2560, V=248320 "
+            "(8 slices of 31040); bf16 N(0,1) hidden and N(0,0.02) lm_head quantized per row "
+            "to E4M3 with fp32 scales; per-request params as spec_decode",
+        ),
         Workload(
             "draft_share", 5, rows=16, vocab=151936, hidden=None, max_logprobs=0, n_slices=8,
             parent="draft", row_offset=48,
@@ -148,13 +164,13 @@ def make_params(w: Workload) -> np.ndarray:
         p["top_p"] = 0.8
         p["n_logprobs"] = 5
         p["seed"] = g.integers(0, 2**64, size=w.rows, dtype=np.uint64)
-    elif w.name in ("spec_decode", "rank_share", "draft"):
+    elif w.name in ("spec_decode", "rank_share", "draft", "fp8"):
         n_req = w.requests if w.requests else w.rows
         per = w.rows // n_req
         t = g.uniform(0.0, 1.2, size=n_req).astype(np.float32)
         k = g.choice(np.array([0, 1, 20, 50, 1000], dtype=np.int32), size=n_req)
         pp = g.uniform(0.5, 1.0, size=n_req).astype(np.float32)
-        nl = (g.integers(0, 21, size=n_req) if w.name == "spec_decode"
+        nl = (g.integers(0, 21, size=n_req) if w.name in ("spec_decode", "fp8")
               else np.full(n_req, min(5, w.max_logprobs))).astype(np.int32)
         sd = g.integers(0, 2**64, size=n_req, dtype=np.uint64)
         for name, v in (("temperature", t), ("top_k", k), ("top_p", pp),
