@@ -42,7 +42,11 @@ in the design notes of the repository):
   R7  invalid parameters give row status 1, a NaN or +inf logit or a row
       with no finite logit gives row status 2; such rows return token -1 and
       NaN log-probabilities; unused top-N slots hold id -1, log-prob -inf;
-  R10 the FP8 projection is W8A8 with per-row fp32 scales (see below).
+  R10 the FP8 projection is W8A8 with per-row fp32 scales (see below);
+  R11 on request, log-probabilities describe the distribution sampled from:
+      (l - m)/T - ln(sum over the kept set of exp((l - m)/T)) for kept
+      tokens, -inf for the others; a greedy row is a point mass (0 for the
+      chosen token, -inf for the rest); top-N lists the same ids as R5.
 
 Parity of every function here is pinned by tests in ``tests/test_oracle_pins.py``
 (published Philox known-answer vectors, exact integer dot products, O(V^2)
@@ -324,10 +328,12 @@ def kept_set(l: np.ndarray, t: float, k: int, p: float,
 
 
 def sample_row(logits: np.ndarray, temperature: float, top_k: int, top_p: float,
-               n_logprobs: int, seed: int, row_global: int, max_logprobs: int) -> RowResult:
+               n_logprobs: int, seed: int, row_global: int, max_logprobs: int,
+               processed: bool = False) -> RowResult:
     """Sample one row; ``logits`` is the fp32 row, used as exact values.
     Parameters are taken as given (the callers pass the fp32 values the GPU
-    receives)."""
+    receives).  ``processed`` selects R11's log-probabilities of the
+    distribution sampled from instead of R5's raw ones."""
     t = float(temperature)
     p = float(top_p)
     k = int(top_k)
@@ -358,9 +364,19 @@ def sample_row(logits: np.ndarray, temperature: float, top_k: int, top_p: float,
     # R2: greedy.
     if t < GREEDY_EPS or k == 1:
         tok = int(order[0])
+        if processed:  # R11: a point mass on the chosen token
+            topn_lp[:n_listed] = np.where(topn_ids[:n_listed] == tok, 0.0, -np.inf)
+            return RowResult(STATUS_OK, tok, 0.0, topn_ids, topn_lp, kept=1)
         return RowResult(STATUS_OK, tok, float(logprob[tok]), topn_ids, topn_lp, kept=1)
 
     kept_ids, ambiguous = kept_set(l, t, k, p, order)
+    if processed:
+        # R11: log-probabilities of the temperature-scaled distribution
+        # renormalised over the kept set; -inf outside it.
+        z_kept = np.exp((l[kept_ids] - m) / t).sum()
+        logprob = np.full(vocab, -np.inf)
+        logprob[kept_ids] = (l[kept_ids] - m) / t - math.log(z_kept)
+        topn_lp[:n_listed] = logprob[order[:n_listed]]
 
     # R6: Gumbel-max over the kept set.
     keys = (l[kept_ids] - m) / t + gumbel_noise(seed, row_global, kept_ids)
@@ -405,23 +421,25 @@ class SampleResult:
 
 
 def _sample_rows(args):
-    logits, params, row_offset, max_logprobs, row_ids = args
+    logits, params, row_offset, max_logprobs, row_ids, processed = args
     out = []
     for i, r in enumerate(row_ids):
         pr = params[i]
         out.append(sample_row(logits[i], float(pr["temperature"]), int(pr["top_k"]),
                               float(pr["top_p"]), int(pr["n_logprobs"]), int(pr["seed"]),
-                              row_offset + int(r), max_logprobs))
+                              row_offset + int(r), max_logprobs, processed))
     return out
 
 
 def sample(logits: np.ndarray, params: np.ndarray, row_offset: int, max_logprobs: int,
-           rows: np.ndarray | None = None, workers: int = 1) -> SampleResult:
+           rows: np.ndarray | None = None, workers: int = 1,
+           processed: bool = False) -> SampleResult:
     """Sample every row (or the listed local ``rows``) of ``logits``.
 
     ``params`` is a record array with fields temperature, top_k, top_p,
     n_logprobs, seed (one entry per local row); ``row_offset`` is the global
-    index of local row 0 (the RNG is keyed on the global row).
+    index of local row 0 (the RNG is keyed on the global row); ``processed``
+    selects R11's log-probabilities.
     """
     logits = np.asarray(logits)
     row_ids = np.arange(logits.shape[0]) if rows is None else np.asarray(rows)
@@ -429,11 +447,13 @@ def sample(logits: np.ndarray, params: np.ndarray, row_offset: int, max_logprobs
         import multiprocessing as mp
 
         parts = np.array_split(row_ids, min(workers, row_ids.shape[0]))
-        jobs = [(logits[pr], params[pr], row_offset, max_logprobs, pr) for pr in parts if len(pr)]
+        jobs = [(logits[pr], params[pr], row_offset, max_logprobs, pr, processed)
+                for pr in parts if len(pr)]
         with mp.get_context("fork").Pool(len(jobs)) as pool:
             res = [r for part in pool.map(_sample_rows, jobs) for r in part]
     else:
-        res = _sample_rows((logits[row_ids], params[row_ids], row_offset, max_logprobs, row_ids))
+        res = _sample_rows((logits[row_ids], params[row_ids], row_offset, max_logprobs, row_ids,
+                            processed))
     return SampleResult(
         token_ids=np.array([r.token for r in res], dtype=np.int64),
         token_logprobs=np.array([r.token_logprob for r in res]),

@@ -459,3 +459,53 @@ def test_e4m3_projection_exact_on_integer_codes():
                                     vocab_chunk=16)
     want = (xi @ wi.T).astype(np.float64) * xs[:, None] * ws[None, :]
     assert np.array_equal(got, want)
+
+
+# --------------------------------------------------- processed log-probs (R11)
+def _row(l, t, k, p, n, seed=3):
+    return oracle.sample_row(np.asarray(l, dtype=np.float32), t, k, p, n, seed, 0, n,
+                             processed=True)
+
+
+def test_processed_logprobs_without_filters_are_log_softmax_of_scaled_logits():
+    from scipy.special import log_softmax
+
+    rng = np.random.default_rng(21)
+    l = rng.normal(0, 2, 500).astype(np.float32)
+    r = _row(l, 0.7, 0, 1.0, 8)
+    ref = log_softmax(l.astype(np.float64) / 0.7)
+    assert abs(r.token_logprob - ref[r.token]) < 1e-12
+    np.testing.assert_allclose(r.topn_logprobs, ref[r.topn_ids], rtol=0, atol=1e-12)
+
+
+def test_processed_logprobs_top_k_brute_force():
+    rng = np.random.default_rng(22)
+    l = rng.integers(-5, 6, 300).astype(np.float32)   # many ties at the k-th value
+    k = 17
+    r = _row(l, 1.0, k, 1.0, 40)
+    kth = sorted(l.tolist(), reverse=True)[k - 1]
+    kept = [i for i in range(l.shape[0]) if l[i] >= kth]
+    z = sum(math.exp(float(l[i])) for i in kept)
+    for i, lp in zip(r.topn_ids, r.topn_logprobs):
+        want = float(l[i]) - math.log(z) if i in kept else -math.inf
+        assert (lp == want) or abs(lp - want) < 1e-12, (i, lp, want)
+    assert r.token in kept
+
+
+def test_processed_logprobs_greedy_is_a_point_mass():
+    l = np.array([1.0, 3.0, 3.0, 2.0], dtype=np.float32)
+    r = _row(l, 0.0, 0, 1.0, 4)
+    assert r.token == 1 and r.token_logprob == 0.0
+    assert r.topn_ids.tolist() == [1, 2, 3, 0]
+    assert r.topn_logprobs.tolist() == [0.0, -math.inf, -math.inf, -math.inf]
+
+
+def test_processed_logprobs_top_p_sum_to_one_over_the_kept_set():
+    rng = np.random.default_rng(23)
+    l = rng.normal(0, 1.5, 2000).astype(np.float32)
+    r = _row(l, 0.9, 0, 0.6, 2000)
+    fin = np.isfinite(r.topn_logprobs)
+    assert fin.sum() == r.kept and 0 < r.kept < 2000
+    assert abs(np.exp(r.topn_logprobs[fin]).sum() - 1.0) < 1e-12
+    # the listed ids are the raw top-N: the kept ones form its prefix
+    assert fin[:r.kept].all() and not fin[r.kept:].any()
