@@ -63,6 +63,8 @@ enum {
 #define TS_MAX_LOGPROBS 1024   /* largest accepted max_logprobs              */
 #define TS_MAX_SLICES 64       /* largest accepted n_slices                  */
 #define TS_GREEDY_EPS 1e-6f    /* temperatures below this sample greedily    */
+/* sampler_sample_ex flags */
+#define TS_LOGPROBS_PROCESSED 1 /* log-probabilities of the sampled distribution */
 
 /*
  * Sampling parameters of one row (24 bytes, 8-byte aligned; an array of
@@ -220,6 +222,29 @@ int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
                           int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
                           float* topn_logprobs, int32_t* row_status, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * sampler_sample_ex: sampler_sample_slices with a flags word (0 gives
+ * sampler_sample_slices exactly; sampler_sample is the one-slice case).
+ *   TS_LOGPROBS_PROCESSED  token_logprobs and topn_logprobs describe the
+ *       distribution the token is drawn from instead of the raw
+ *       log_softmax(logits): (l - m)/T - ln(sum over the kept set of
+ *       exp((l - m)/T)) for tokens the filters keep, -inf for the others; a
+ *       greedy row is a point mass (0 for the chosen token, -inf for the
+ *       rest).  top-N lists the same ids as the raw mode (the N largest
+ *       logits).  The pages ask only for a non-negative max_logprobs
+ *       (section "What batch-sharded sampling is, in one paragraph"); this
+ *       is the processed variant of the same output.  Top-p-only rows whose
+ *       nucleus reaches below the listed candidates take the exact per-row
+ *       kernel in this mode.
+ * Other flag bits: TS_EINVAL.  Workspace: sampler_workspace_bytes_slices.
+ */
+int sampler_sample_ex(const float* const* slices, const int64_t* slice_cols,
+                      const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                      const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                      int32_t flags, int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                      float* topn_logprobs, int32_t* row_status, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /*
  * sampler_assemble_vocab_slices: out[r, off_s + c] = slice_s[r, c] with

@@ -33,7 +33,8 @@ def test_header_symbols_exported():
 
 def test_header_constants_match_binding():
     text = open(HEADER).read()
-    for name, val in [("TS_MAX_LOGPROBS", ts.TS_MAX_LOGPROBS), ("TS_MAX_SLICES", ts.TS_MAX_SLICES)]:
+    for name, val in [("TS_MAX_LOGPROBS", ts.TS_MAX_LOGPROBS), ("TS_MAX_SLICES", ts.TS_MAX_SLICES),
+                      ("TS_LOGPROBS_PROCESSED", ts.TS_LOGPROBS_PROCESSED)]:
         assert re.search(rf"#define {name} {val}\b", text)
     assert workloads.PARAMS_DTYPE.itemsize == ts.PARAMS_BYTES
 
@@ -261,3 +262,15 @@ def test_quantize_e4m3_validation():
     assert q(FAKE, 4, 8, 8, FAKE, 8, None, None) == ts.TS_EINVAL
     assert q(FAKE + 1, 4, 8, 8, FAKE, 8, FAKE, None) == ts.TS_EUNSUPPORTED
     assert q(None, 0, 8, 8, None, 8, None, None) == ts.TS_OK
+
+
+def test_sampler_ex_validation():
+    P = (ctypes.c_void_p * 2)(FAKE, FAKE * 2)
+    C = (ctypes.c_int64 * 2)(40, 60)
+    L = (ctypes.c_int64 * 2)(40, 60)
+    ex = lambda flags, ws=None, nb=0: ts.lib.sampler_sample_ex(  # noqa: E731
+        P, C, L, 2, 8, FAKE, 0, 5, flags, FAKE, FAKE, FAKE, FAKE, FAKE, ws, nb, None)
+    assert ex(2) == ts.TS_EINVAL                       # unknown flag bit
+    assert ex(-1) == ts.TS_EINVAL
+    assert ex(0) == ts.TS_EWORKSPACE                   # valid up to the workspace
+    assert ex(ts.TS_LOGPROBS_PROCESSED) == ts.TS_EWORKSPACE

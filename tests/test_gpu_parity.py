@@ -189,7 +189,8 @@ def test_assemble_ragged(dev, ts, widths, ld_extra, rows):
 
 
 # ---------------------------------------------------------------- sampler
-def _run_sampler(ts, dev, logits_np, params, row_offset, max_logprobs, ld_extra=0):
+def _run_sampler(ts, dev, logits_np, params, row_offset, max_logprobs, ld_extra=0,
+                 processed=False):
     import torch
 
     rows, vocab = logits_np.shape
@@ -200,7 +201,8 @@ def _run_sampler(ts, dev, logits_np, params, row_offset, max_logprobs, ld_extra=
     else:
         logits = torch.from_numpy(np.ascontiguousarray(logits_np)).to(dev)
     p = ts.params_to_device(params, dev)
-    out = ts.sampler_sample(logits, p, row_offset=row_offset, max_logprobs=max_logprobs)
+    out = ts.sampler_sample(logits, p, row_offset=row_offset, max_logprobs=max_logprobs,
+                            processed=processed)
     torch.cuda.synchronize()
     return {k: getattr(out, k).cpu().numpy() for k in
             ("token_ids", "token_logprobs", "topn_ids", "topn_logprobs", "row_status")}
@@ -438,7 +440,8 @@ def test_gumbel_noise_on_flat_rows(dev, ts, route):
 
 
 # ------------------------------------------------ sampler over vocab slices
-def _run_sampler_slices(ts, dev, logits_np, widths, params, row_offset, max_logprobs, ld_extra=0):
+def _run_sampler_slices(ts, dev, logits_np, widths, params, row_offset, max_logprobs, ld_extra=0,
+                        processed=False):
     """sampler_sample_slices over ``logits_np`` cut column-wise into ``widths``
     (each slice its own buffer; with ld_extra, a NaN-padded wider buffer)."""
     import torch
@@ -457,7 +460,8 @@ def _run_sampler_slices(ts, dev, logits_np, widths, params, row_offset, max_logp
             slices.append(full[:, a:b].contiguous())
     del full
     p = ts.params_to_device(params, dev)
-    out = ts.sampler_sample_slices(slices, p, row_offset=row_offset, max_logprobs=max_logprobs)
+    out = ts.sampler_sample_slices(slices, p, row_offset=row_offset, max_logprobs=max_logprobs,
+                                   processed=processed)
     torch.cuda.synchronize()
     return {k: getattr(out, k).cpu().numpy() for k in
             ("token_ids", "token_logprobs", "topn_ids", "topn_logprobs", "row_status")}
@@ -598,3 +602,71 @@ def test_sampler_draft_share(dev, ts, in_place, route):
     _compare(got, exp["token_ids"][sl], exp["token_logprobs"][sl], exp["topn_ids"][sl],
              exp["topn_logprobs"][sl], exp["row_status"][sl], flagged, exp["lse"][sl], logits,
              max_frac=1.0, label="draft_share")
+
+
+# ------------------------------------------ processed log-probabilities (R11)
+def _compare_processed(got, res, label=""):
+    """Ids and status exact; -inf pattern exact and finite values within
+    1e-4 of the oracle's, except on rows whose top-p boundary or best keys the
+    oracle flags (there the kept set, and so the values, may differ)."""
+    np.testing.assert_array_equal(got["row_status"], res.row_status)
+    ok = res.row_status == 0
+    firm = ok & ~res.flagged
+    mism = (got["token_ids"] != res.token_ids) & ok
+    assert not np.any(mism & firm), (label, np.nonzero(mism & firm)[0][:10])
+    np.testing.assert_array_equal(got["topn_ids"][ok], res.topn_ids[ok])
+    g, w = got["topn_logprobs"][firm], res.topn_logprobs[firm]
+    assert np.array_equal(np.isfinite(g), np.isfinite(w)), label
+    fin = np.isfinite(w)
+    assert np.abs(g[fin] - w[fin]).max(initial=0) <= LOGPROB_TOL, label
+    gt, wt = got["token_logprobs"][firm], res.token_logprobs[firm]
+    assert np.all(np.isfinite(gt)) and np.abs(gt - wt).max(initial=0) <= LOGPROB_TOL, label
+    assert np.all(got["token_logprobs"][ok] <= LOGPROB_TOL)   # probabilities, not above 1
+
+
+@pytest.mark.parametrize("name,slices", [("spec_decode", 1), ("spec_decode", 8),
+                                         ("rank_share", 1), ("draft", 1)])
+def test_sampler_processed_workloads(dev, ts, name, slices, route):
+    w = workloads.get(name)
+    logits = workloads.make_logits(w)
+    params = workloads.make_params(w)
+    say("sampler processed", name, slices, route)
+    if slices > 1:
+        got = _run_sampler_slices(ts, dev, logits, _even_widths(w.vocab, slices), params, 0,
+                                  w.max_logprobs, processed=True)
+    else:
+        got = _run_sampler(ts, dev, logits, params, 0, w.max_logprobs, processed=True)
+    res = oracle.sample(logits, params, 0, w.max_logprobs, processed=True)
+    assert res.flagged.sum() <= 1e-3 * w.rows
+    _compare_processed(got, res, label=name)
+
+
+@pytest.mark.parametrize("V", [1, 7, 1000, 20000, 70001])
+@pytest.mark.parametrize("kind", ["normal", "ints", "neginf", "wide"])
+def test_sampler_processed_edge_cases(dev, ts, V, kind, route):
+    rng = np.random.default_rng(V * 7 + len(kind))
+    rows, max_lp = 24, 9
+    logits = _edge_case(rng, V, rows, kind)
+    params = workloads.random_params(rng, rows, V, max_lp)
+    say("sampler processed edge", V, kind, route)
+    got = _run_sampler(ts, dev, logits, params, 2, max_lp, ld_extra=3, processed=True)
+    res = oracle.sample(logits, params, 2, max_lp, processed=True)
+    _compare_processed(got, res, label=f"{V}/{kind}")
+
+
+def test_sampler_processed_large_targets(dev, ts, route):
+    rng = np.random.default_rng(41)
+    rows, V, max_lp = 8, 70000, 300
+    logits = rng.standard_normal((rows, V)).astype(np.float32)
+    for r in range(0, rows, 2):
+        s0 = int(rng.integers(0, V - 3000))
+        logits[r, s0:s0 + 3000] += 6.0
+    params = workloads.random_params(rng, rows, V, max_lp)
+    params["top_k"] = np.array([1000, 300, 65, 1024, 0, 1000, 200, 700], dtype=np.int32)
+    params["top_p"] = np.array([1.0, 0.9, 0.5, 1.0, 0.7, 0.95, 1.0, 0.3], dtype=np.float32)
+    params["n_logprobs"] = np.array([300, 0, 300, 5, 300, 100, 65, 299], dtype=np.int32)
+    params["temperature"][:] = 0.9
+    say("sampler processed large targets", route)
+    got = _run_sampler(ts, dev, logits, params, 0, max_lp, processed=True)
+    res = oracle.sample(logits, params, 0, max_lp, processed=True)
+    _compare_processed(got, res, label="large targets")

@@ -14,6 +14,7 @@ Calls mirror the C entry points:
                                  logprobs / Gumbel-max sampling
   sampler_sample_slices          the same, reading the received vocabulary
                                  slices in place (no stitched buffer)
+  sampler_sample_ex              slices plus flags (processed log-probabilities)
   sampler_workspace_bytes(_slices)  workspace size queries
 and ``compute_logits_local`` returns the rank's own ``[rows, V_local]`` slice,
 the local-logits hook of batch-sharded sampling (page "Qwen4Exp batch-sharded
@@ -35,6 +36,7 @@ TS_OK, TS_EINVAL, TS_EUNSUPPORTED, TS_EWORKSPACE, TS_EHIP = 0, -1, -2, -3, -4
 TS_ROW_OK, TS_ROW_BAD_PARAMS, TS_ROW_BAD_LOGITS = 0, 1, 2
 TS_MAX_LOGPROBS = 1024
 TS_MAX_SLICES = 64
+TS_LOGPROBS_PROCESSED = 1
 PARAMS_BYTES = 24
 
 # (name, restype, argtypes) of every symbol the header declares.
@@ -50,6 +52,8 @@ SYMBOLS = {
     "sampler_workspace_bytes_slices": (_SZ, [_I64, _VP, _I32, _I32]),
     "sampler_sample_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _I32, _VP, _VP,
                                              _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "sampler_sample_ex": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _I32, _I32, _VP,
+                                         _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sampler_assemble_vocab_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _VP]),
     "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ts_last_error": (ctypes.c_char_p, []),
@@ -236,10 +240,15 @@ def allocate_workspace(rows: int, vocab: int, max_logprobs: int, device):
 
 
 def sampler_sample(logits, params, row_offset: int = 0, max_logprobs: int = 0, out=None,
-                   workspace=None, stream=None) -> SampleOutput:
+                   workspace=None, stream=None, processed: bool = False) -> SampleOutput:
     """Sample one token per row of fp32 ``logits [rows, V]`` (row stride = its
     leading dimension).  ``params`` is a device uint8 tensor of 24-byte
-    ``ts_row_params`` records (see ``params_to_device``)."""
+    ``ts_row_params`` records (see ``params_to_device``).  ``processed``
+    returns log-probabilities of the sampled distribution (sampler_sample_ex
+    with TS_LOGPROBS_PROCESSED) instead of the raw log_softmax."""
+    if processed:
+        return sampler_sample_slices([logits], params, row_offset, max_logprobs, out=out,
+                                     workspace=workspace, stream=stream, processed=True)
     torch = _torch()
     rows, vocab = logits.shape
     if logits.dtype != torch.float32 or logits.stride(1) != 1:
@@ -281,7 +290,7 @@ def sampler_workspace_bytes_slices(rows: int, slice_cols, max_logprobs: int) -> 
 
 
 def sampler_sample_slices(slices, params, row_offset: int = 0, max_logprobs: int = 0, out=None,
-                          workspace=None, stream=None) -> SampleOutput:
+                          workspace=None, stream=None, processed: bool = False) -> SampleOutput:
     """``sampler_sample`` over the column-wise concatenation of ``slices``
     (fp32 ``[rows, cols_s]`` each), read in place.  Token ids are global
     columns of that concatenation."""
@@ -295,8 +304,10 @@ def sampler_sample_slices(slices, params, row_offset: int = 0, max_logprobs: int
     if workspace is None:
         nb = max(256, sampler_workspace_bytes_slices(rows, list(cols), max_logprobs))
         workspace = torch.empty(nb, dtype=torch.uint8, device=device)
-    _check(lib.sampler_sample_slices(
-        ptrs, cols, lds, n, rows, _ptr(params), row_offset, max_logprobs,
+    head = (ptrs, cols, lds, n, rows, _ptr(params), row_offset, max_logprobs)
+    call = (lambda *t: lib.sampler_sample_ex(*head, TS_LOGPROBS_PROCESSED, *t)) if processed \
+        else (lambda *t: lib.sampler_sample_slices(*head, *t))
+    _check(call(
         _ptr(out.token_ids), _ptr(out.token_logprobs),
         _ptr(out.topn_ids) if max_logprobs > 0 else None,
         _ptr(out.topn_logprobs) if max_logprobs > 0 else None,

@@ -205,12 +205,13 @@ int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_
                        workspace_bytes, stream);
 }
 
-int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
-                          const int64_t* slice_ld, int32_t n_slices, int64_t rows,
-                          const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
-                          int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
-                          float* topn_logprobs, int32_t* row_status, void* workspace,
-                          size_t workspace_bytes, void* stream) {
+int sampler_sample_ex(const float* const* slices, const int64_t* slice_cols,
+                      const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                      const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                      int32_t flags, int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                      float* topn_logprobs, int32_t* row_status, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (flags & ~TS_LOGPROBS_PROCESSED) return fail(TS_EINVAL, "unknown flag bits 0x%x", flags);
   if (n_slices < 1 || n_slices > TS_MAX_SLICES)
     return fail(n_slices < 1 ? TS_EINVAL : TS_EUNSUPPORTED, "n_slices %d not in [1, %d]",
                 n_slices, TS_MAX_SLICES);
@@ -218,6 +219,7 @@ int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
   if (!slices || !slice_cols || !slice_ld) return fail(TS_EINVAL, "NULL slice arrays");
   ts::SamplerArgs a{};
   a.lv.n = n_slices;
+  a.flags = flags;
   int64_t total = 0;
   for (int i = 0; i < n_slices; ++i) {
     const int64_t c = slice_cols[i];
@@ -235,6 +237,17 @@ int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
   return sample_common(a, slice_cols, rows, total, params, row_offset, max_logprobs, token_ids,
                        token_logprobs, topn_ids, topn_logprobs, row_status, workspace,
                        workspace_bytes, stream);
+}
+
+int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
+                          const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                          const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                          int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                          float* topn_logprobs, int32_t* row_status, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return sampler_sample_ex(slices, slice_cols, slice_ld, n_slices, rows, params, row_offset,
+                           max_logprobs, 0, token_ids, token_logprobs, topn_ids, topn_logprobs,
+                           row_status, workspace, workspace_bytes, stream);
 }
 
 int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* slice_cols,

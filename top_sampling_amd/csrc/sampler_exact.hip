@@ -206,6 +206,86 @@ __device__ __forceinline__ void exact_row(const SamplerArgs& a, int r, FallbackS
   s = block_sum<XT, float>(s, sh.rf_);
   const float lse = m + logf(s);
 
+  // The sampled token first: the processed log-probabilities need the kept
+  // set it is drawn from.
+  int token;
+  const bool greedy = p.temperature < TS_GREEDY_EPS || p.top_k == 1;
+  float inv_t = 0.0f;
+  uint32_t thr = 0u;  // the kept set's smallest key
+  if (greedy) {
+    token = argmax_id;
+  } else {
+    inv_t = 1.0f / p.temperature;
+    // Top-k threshold key (0 keeps every non-NaN key).
+    uint32_t kk = 0u;
+    if (p.top_k > 0 && p.top_k < V) {
+      uint32_t gt, eq;
+      radix_kth(lv, r, static_cast<uint32_t>(p.top_k), sh, kk, gt, eq);
+    }
+    // Top-p threshold key on the temperature-scaled top-k distribution.
+    uint32_t kp = 0u;
+    if (p.top_p < 1.0f) {
+      unsigned long long z = 0ull;
+      for_row(lv, r, [&](int, float l) {
+        if (order_key(l) >= kk) z += fixed_mass(expf((l - m) * inv_t));
+      });
+      z = block_sum<XT, unsigned long long>(z, sh.rq);
+      const double tgt = ceil(static_cast<double>(p.top_p) * static_cast<double>(z));
+      unsigned long long target = static_cast<unsigned long long>(tgt);
+      if (target < 1ull) target = 1ull;
+      if (target > z) target = z;
+      kp = radix_mass(lv, r, kk, m, inv_t, target, sh);
+    }
+    thr = kk > kp ? kk : kp;
+    // Gumbel-max over the kept set, four consecutive tokens per Philox call.
+    const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
+    float gk = -INFINITY;
+    int gi = 0x7fffffff;
+    const int nq = (V + 3) >> 2;
+    for (int q = tid; q < nq; q += XT) {
+      float l4[4];
+      bool in[4];
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int v = 4 * q + j;
+        l4[j] = v < V ? logit_at(lv, r, v) : -INFINITY;
+        in[j] = v < V && order_key(l4[j]) >= thr;
+        any |= in[j];
+      }
+      if (!any) continue;
+      const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(q));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (!in[j]) continue;
+        const float key = (l4[j] - m) * inv_t + gumbel_from_word(w.v[j]);
+        if (better(key, 4 * q + j, gk, gi)) {
+          gk = key;
+          gi = 4 * q + j;
+        }
+      }
+    }
+    block_best<XT>(gk, gi, sh.rf_, sh.ri);
+    token = gi;
+  }
+  // Processed log-probabilities: (l - m) / T - ln(kept mass) inside the kept
+  // set, -inf outside it; a greedy row is a point mass on its token.
+  const bool proc = (a.flags & TS_LOGPROBS_PROCESSED) != 0;
+  float lzk = 0.0f;
+  if (proc && !greedy) {
+    float z = 0.0f;
+    for_row(lv, r, [&](int, float l) {
+      if (order_key(l) >= thr) z += expf((l - m) * inv_t);
+    });
+    lzk = logf(block_sum<XT, float>(z, sh.rf_));
+  }
+  auto out_lp = [&](uint32_t key, int id) -> float {
+    const float l = key_to_float(key);
+    if (!proc) return l - lse;
+    if (greedy) return id == token ? 0.0f : -INFINITY;
+    return key >= thr ? (l - m) * inv_t - lzk : -INFINITY;
+  };
+
   // Top-N log-probabilities.
   const int n = p.n_logprobs < V ? p.n_logprobs : V;
   const int64_t obase = static_cast<int64_t>(r) * a.max_logprobs;
@@ -250,70 +330,13 @@ __device__ __forceinline__ void exact_row(const SamplerArgs& a, int r, FallbackS
       for (int j = 0; j < n; ++j)
         rank += better_u(sh.ex.list_key[j], sh.ex.list_id[j], kt, it) ? 1 : 0;
       a.topn_ids[obase + rank] = it;
-      a.topn_logprobs[obase + rank] = key_to_float(kt) - lse;
+      a.topn_logprobs[obase + rank] = out_lp(kt, it);
     }
   }
 
-  int token;
-  if (p.temperature < TS_GREEDY_EPS || p.top_k == 1) {
-    token = argmax_id;
-  } else {
-    const float inv_t = 1.0f / p.temperature;
-    // Top-k threshold key (0 keeps every non-NaN key).
-    uint32_t kk = 0u;
-    if (p.top_k > 0 && p.top_k < V) {
-      uint32_t gt, eq;
-      radix_kth(lv, r, static_cast<uint32_t>(p.top_k), sh, kk, gt, eq);
-    }
-    // Top-p threshold key on the temperature-scaled top-k distribution.
-    uint32_t kp = 0u;
-    if (p.top_p < 1.0f) {
-      unsigned long long z = 0ull;
-      for_row(lv, r, [&](int, float l) {
-        if (order_key(l) >= kk) z += fixed_mass(expf((l - m) * inv_t));
-      });
-      z = block_sum<XT, unsigned long long>(z, sh.rq);
-      const double tgt = ceil(static_cast<double>(p.top_p) * static_cast<double>(z));
-      unsigned long long target = static_cast<unsigned long long>(tgt);
-      if (target < 1ull) target = 1ull;
-      if (target > z) target = z;
-      kp = radix_mass(lv, r, kk, m, inv_t, target, sh);
-    }
-    const uint32_t thr = kk > kp ? kk : kp;
-    // Gumbel-max over the kept set, four consecutive tokens per Philox call.
-    const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
-    float gk = -INFINITY;
-    int gi = 0x7fffffff;
-    const int nq = (V + 3) >> 2;
-    for (int q = tid; q < nq; q += XT) {
-      float l4[4];
-      bool in[4];
-      bool any = false;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int v = 4 * q + j;
-        l4[j] = v < V ? logit_at(lv, r, v) : -INFINITY;
-        in[j] = v < V && order_key(l4[j]) >= thr;
-        any |= in[j];
-      }
-      if (!any) continue;
-      const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(q));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (!in[j]) continue;
-        const float key = (l4[j] - m) * inv_t + gumbel_from_word(w.v[j]);
-        if (better(key, 4 * q + j, gk, gi)) {
-          gk = key;
-          gi = 4 * q + j;
-        }
-      }
-    }
-    block_best<XT>(gk, gi, sh.rf_, sh.ri);
-    token = gi;
-  }
   if (tid == 0) {
     a.token_ids[r] = token;
-    if (a.token_logprobs) a.token_logprobs[r] = logit_at(lv, r, token) - lse;
+    if (a.token_logprobs) a.token_logprobs[r] = out_lp(order_key(logit_at(lv, r, token)), token);
     if (a.row_status) a.row_status[r] = TS_ROW_OK;
   }
 }

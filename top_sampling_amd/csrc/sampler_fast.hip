@@ -256,7 +256,10 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
   const int c0 = geo.gofs;  // global column of the chunk's first logit
   const int n = geo.n;
-  const bool topp = kind == KIND_TOPP;
+  // The temperature-scaled mass: top-p-only rows, and unfiltered rows when
+  // the log-probabilities describe the sampled distribution.
+  const bool topp = kind == KIND_TOPP ||
+                    ((a.flags & TS_LOGPROBS_PROCESSED) && kind == KIND_FULL);
   const float inv_t = uniform_f32(kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature);
 
   float4 v[AV];
@@ -296,21 +299,24 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     }
   }
   if (lm > -INFINITY) {
-    // exp(l - m) as 2^(l log2 e - m log2 e): one fused multiply-add per logit.
-    const float nl = -lm * kLog2e;
+    // Differences from the maximum first, then the scale: the exponent's
+    // rounding error stays proportional to l - m, small where the terms are
+    // large (a fused l * c - m * c would round m * c, an error that grows with
+    // |m| / T).  The scaled sum forms its difference as (m - l) * -c, the same
+    // value but not the same instruction, so the compiler does not keep the
+    // first loop's 64 differences alive for the second.
 #pragma unroll
     for (int j = 0; j < AV; ++j) {
       const float4 f = v[j];
-      ls += __builtin_amdgcn_exp2f(fmaf(f.x, kLog2e, nl)) + __builtin_amdgcn_exp2f(fmaf(f.y, kLog2e, nl)) +
-            __builtin_amdgcn_exp2f(fmaf(f.z, kLog2e, nl)) + __builtin_amdgcn_exp2f(fmaf(f.w, kLog2e, nl));
+      ls += fast_exp(f.x - lm) + fast_exp(f.y - lm) + fast_exp(f.z - lm) + fast_exp(f.w - lm);
     }
     if (topp) {
-      const float nt = -lm * sc;
+      const float nsc = -sc;
 #pragma unroll
       for (int j = 0; j < AV; ++j) {
         const float4 f = v[j];
-        lt += __builtin_amdgcn_exp2f(fmaf(f.x, sc, nt)) + __builtin_amdgcn_exp2f(fmaf(f.y, sc, nt)) +
-              __builtin_amdgcn_exp2f(fmaf(f.z, sc, nt)) + __builtin_amdgcn_exp2f(fmaf(f.w, sc, nt));
+        lt += __builtin_amdgcn_exp2f((lm - f.x) * nsc) + __builtin_amdgcn_exp2f((lm - f.y) * nsc) +
+              __builtin_amdgcn_exp2f((lm - f.z) * nsc) + __builtin_amdgcn_exp2f((lm - f.w) * nsc);
       }
     }
   }
@@ -804,6 +810,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   const int r = blockIdx.x, tid = threadIdx.x, S = lay.S, V = a.vocab;
   const ts_row_params p = a.params[r];
   const int kind = row_kind(p, V, a.max_logprobs);
+  const bool proc = (a.flags & TS_LOGPROBS_PROCESSED) != 0;
   int* ctr = reinterpret_cast<int*>(ws + lay.off_ctr);
   int* exact_list = reinterpret_cast<int*>(ws + lay.off_exact);
   int* probe_list = reinterpret_cast<int*>(ws + lay.off_probe);
@@ -849,11 +856,11 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       for (int c = 0; c < S; ++c) {
         if (!(sh.recs[c].cmax > -INFINITY)) continue;
         se += sh.recs[c].sumexp * fast_exp(sh.recs[c].cmax - m);
-        if (kind == KIND_TOPP) {
+        if (kind == KIND_TOPP || (proc && kind == KIND_FULL)) {
           const float shift = (sh.recs[c].cmax - m) * inv_t;
           z += static_cast<double>(sh.recs[c].tmass) *
                static_cast<double>(__builtin_amdgcn_exp2f(shift * kLog2e));
-          kmin = fmaxf(kmin, sh.recs[c].kfloor + shift);
+          if (kind == KIND_TOPP) kmin = fmaxf(kmin, sh.recs[c].kfloor + shift);
         }
       }
     }
@@ -976,7 +983,12 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   }
   int token = -1;
   bool probe = false;
+  // The kept set's smallest key and its temperature-scaled mass (for the
+  // processed log-probabilities).
+  uint32_t kept_key = 0u;
+  double zk = 0.0;
   if (kind == KIND_FULL) {
+    zk = sh.z;
     const int* keys = reinterpret_cast<const int*>(ws + lay.off_key) +
                       static_cast<size_t>(r) * S * kKeyCap;
     float gk = -INFINITY;
@@ -997,7 +1009,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     const uint32_t kmin = kind == KIND_TOPK ? cand_key(sh.list[p.top_k - 1]) : 0u;
     uint32_t kept = kmin;
     const unsigned long long mine = tid < U ? sh.list[tid] : 0ull;
-    if (p.top_p < 1.0f) {
+    if (p.top_p < 1.0f || proc) {
       const double w = (tid < U && cand_key(mine) >= kmin)
                            ? static_cast<double>(fast_exp((key_to_float(cand_key(mine)) - m) * inv_t))
                            : 0.0;
@@ -1011,7 +1023,9 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
         sh.sel_found = 1;
       }
       __syncthreads();
-      if (!sh.sel_found || (kind == KIND_TOPP && (force & 1))) {
+      if (p.top_p >= 1.0f) {
+        // top-k alone: every listed entry at or above the k-th key is kept
+      } else if (!sh.sel_found || (kind == KIND_TOPP && (force & 1))) {
         if (kind == KIND_TOPK && !sh.sel_found) {  // cannot happen: the top-k set is all listed
           if (tid == 0) push_row(&ctr[0], exact_list, r);
           return;
@@ -1020,7 +1034,12 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       } else {
         kept = sh.sel_d > kmin ? sh.sel_d : kmin;
       }
+      if (proc && !probe) {
+        const double wk = (tid < U && cand_key(mine) >= kept) ? w : 0.0;
+        zk = block_sum<BT, double>(wk, sh.dscan);
+      }
     }
+    kept_key = kept;
     if (!probe) {
       float gk = -INFINITY;
       int gi = 0x7fffffff;
@@ -1063,6 +1082,15 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
         }
       }
     }
+    kept_key = kept;
+    if (proc && !probe) {
+      unsigned long long mk = 0ull;
+      for (int i = tid; i < U; i += BT) {
+        const uint32_t key = cand_key(sh.list[i]);
+        if (key >= kept) mk += list_mass(key, m, inv_t);
+      }
+      zk = static_cast<double>(block_sum<BT, unsigned long long>(mk, sh.uscan)) * kMassUnit;
+    }
     if (!probe) {
       float gk = -INFINITY;
       int gi = 0x7fffffff;
@@ -1086,18 +1114,30 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     const int nt = n_eff > 1 ? n_eff : 1;
     trim_and_sort(sh, U, nt < U ? nt : U, floor_key);
   }
+  if (kind == KIND_GREEDY) token = cand_id(sh.list[0]);  // largest logit, lowest id
+  if (proc && probe) {  // the kept mass lies beyond the listed logits
+    if (tid == 0) push_row(&ctr[0], exact_list, r);
+    return;
+  }
+  // Processed log-probabilities: (l - m) / T - ln(kept mass) inside the kept
+  // set, -inf outside it; a greedy row is a point mass on its token.
+  const float lzk = (proc && kind != KIND_GREEDY) ? static_cast<float>(log(zk)) : 0.0f;
   const int64_t obase = static_cast<int64_t>(r) * a.max_logprobs;
   for (int j = tid; j < a.max_logprobs; j += BT) {
     if (j < n_eff) {
       const unsigned long long e = sh.list[j];
+      const float l = key_to_float(cand_key(e));
+      float lp = l - lse;
+      if (proc)
+        lp = kind == KIND_GREEDY ? (cand_id(e) == token ? 0.0f : -INFINITY)
+             : cand_key(e) >= kept_key ? (l - m) * inv_t - lzk : -INFINITY;
       a.topn_ids[obase + j] = cand_id(e);
-      a.topn_logprobs[obase + j] = key_to_float(cand_key(e)) - lse;
+      a.topn_logprobs[obase + j] = lp;
     } else {
       a.topn_ids[obase + j] = -1;
       a.topn_logprobs[obase + j] = -INFINITY;
     }
   }
-  if (kind == KIND_GREEDY) token = cand_id(sh.list[0]);  // largest logit, lowest id
 
   if (probe) {
     // Top-p-only row whose boundary lies below the listed logits: the
@@ -1146,7 +1186,10 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   }
   if (tid == 0) {
     a.token_ids[r] = token;
-    if (a.token_logprobs) a.token_logprobs[r] = logit_at(a.lv, r, token) - lse;
+    if (a.token_logprobs) {
+      const float l = logit_at(a.lv, r, token);
+      a.token_logprobs[r] = !proc ? l - lse : kind == KIND_GREEDY ? 0.0f : (l - m) * inv_t - lzk;
+    }
     if (a.row_status) a.row_status[r] = TS_ROW_OK;
   }
 }

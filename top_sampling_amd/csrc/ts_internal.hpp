@@ -48,6 +48,7 @@ struct SamplerArgs {
   int32_t* topn_ids;      // may be null iff max_logprobs == 0
   float* topn_logprobs;
   int32_t* row_status;    // may be null
+  int flags;              // TS_LOGPROBS_PROCESSED
 };
 
 size_t sampler_workspace_size(int64_t rows, const int64_t* slice_cols, int n_slices,
