@@ -18,7 +18,12 @@ model shape (H = 2560, V = 248,320 in 8 slices) with an FP8 lm_head: each
 step quantizes the hidden states per row and projects with the E4M3 kernel.
 
 Prints one JSON line.  Per-kernel times come from HIP events recorded on the
-stream the kernels are launched on, over the timed region.
+stream the kernels are launched on, over the timed region.  After the timed
+steps each kernel is also timed alone, cold: 5 warm-up runs, then 50 runs,
+each preceded by a 512 MiB scratch write so that no logit is served from the
+256 MB Infinity Cache; the median with p10 / p90 is reported.  A measured
+copy bandwidth, and the shader clock and bf16 matrix-core rate under a dense
+MFMA load, are reported as context for the roofline fractions.
 """
 from __future__ import annotations
 
@@ -49,15 +54,33 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=640,
                     help="rows of the workload the CPU oracle is timed on")
+    ap.add_argument("--iso-runs", type=int, default=50,
+                    help="runs of each kernel timed alone (cold); 0 skips them")
     return ap.parse_args()
 
 
-def cpu_baseline(x, wt, wq, wsc, logits_sample, params, max_logprobs, rows: int):
+def oracle_workers() -> int:
+    """Host cores the oracle may use: the process's CPU affinity, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _oracle_sample_part(job):
+    """One process's share of the oracle sampler: rows [a, b) of the sample,
+    keyed on their global rows."""
+    import oracle
+
+    logits, params, row_offset, max_logprobs = job
+    oracle.sample(logits, params, row_offset, max_logprobs)
+    return logits.shape[0]
+
+
+def cpu_baseline(x, wt, wq, wsc, logits_sample, params, max_logprobs, rows: int, pool, workers):
     """The CPU oracle as it stands, timed on a bounded sample of the workload:
     the float64 projection of `rows` rows against the whole lm_head (for the
     FP8 workload: the oracle's per-row quantization of those rows, then its
-    projection from the same lm_head codes the GPU uses), then the full-sort
-    sampler on those rows.  Scaled to rows/s."""
+    projection from the same lm_head codes the GPU uses), with as many BLAS
+    threads as host cores, then the full-sort sampler on those rows, split by
+    rows over a process pool of the same size.  Scaled to rows/s."""
     import numpy as np
     import threadpoolctl
 
@@ -81,23 +104,104 @@ def cpu_baseline(x, wt, wq, wsc, logits_sample, params, max_logprobs, rows: int)
         what = "float64 projection"
     else:
         project = None
-    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
-        if threadpoolctl.threadpool_info() else 1
-    t0 = time.perf_counter()
-    if project is not None:
-        project()
-    t1 = time.perf_counter()
-    oracle.sample(logits_sample[:rows], params[:rows], 0, max_logprobs)
+    with threadpoolctl.threadpool_limits(limits=workers, user_api="blas"):
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        t0 = time.perf_counter()
+        if project is not None:
+            project()
+        t1 = time.perf_counter()
+    cuts = np.linspace(0, rows, workers + 1).astype(int)
+    jobs = [(logits_sample[a:b], params[a:b], int(a), max_logprobs)
+            for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
+    done = sum(pool.map(_oracle_sample_part, jobs)) if pool is not None else \
+        sum(map(_oracle_sample_part, jobs))
     t2 = time.perf_counter()
+    assert done == rows
+    procs = len(jobs) if pool is not None else 1
     proj = (f"{what} against the full lm_head ({t1 - t0:.1f}s, BLAS threads {threads}) + "
             if project is not None else "")
     return {
         "value": rows / (t2 - t0),
         "unit": "rows/s",
-        "cores": int(threads) if project is not None else 1,
+        "cores": int(max(threads if project is not None else 1, procs)),
         "kind": "oracle",
-        "sample": f"{rows} rows: {proj}full-sort sampler ({t2 - t1:.1f}s, 1 thread)",
+        "sample": f"{rows} rows: {proj}full-sort sampler ({t2 - t1:.1f}s, "
+                  f"{procs} processes)",
     }
+
+
+def time_alone(fn, stream, scratch, runs: int, warmup: int = 5) -> dict:
+    """fn timed alone with HIP events on `stream`: `warmup` untimed runs, then
+    `runs` runs each preceded by a write of the whole scratch buffer (outside
+    the events), so that what fn reads comes from HBM, not the Infinity Cache.
+    Median, p10 and p90 in milliseconds."""
+    import numpy as np
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(runs)]
+    for i, (a, b) in enumerate(evs):
+        scratch.fill_(i & 0xFF)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"median_ms": round(float(np.median(t)), 4),
+            "p10_ms": round(float(np.percentile(t, 10)), 4),
+            "p90_ms": round(float(np.percentile(t, 90)), 4)}
+
+
+def measured_copy_gbs(dev, stream, nbytes: int = 1 << 30, runs: int = 20) -> float:
+    """Achievable copy bandwidth (bytes read + bytes written per second, GB/s):
+    the median of device-to-device copies of a 1 GiB buffer."""
+    import numpy as np
+    import torch
+
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(runs)]
+    for a, b in evs:
+        a.record(stream)
+        dst.copy_(src)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+    del src, dst
+    return round(2.0 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def measured_mfma_clock(ts, dev, stream, iters: int = 1 << 18, launches: int = 3) -> dict:
+    """The shader clock and the bf16 matrix-core rate under a dense MFMA load
+    on every compute unit (the library's clock probe: per workgroup, the
+    shader-clock counter against the 100 MHz real-time counter), from the
+    last of `launches` back-to-back launches, after the clock has settled."""
+    import numpy as np
+    import torch
+
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    wgs = 2 * n_cu
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b in ev:
+        a.record(stream)
+        ticks = ts.mfma_clock_probe(wgs, iters, dev, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = ticks.cpu().numpy().astype(np.float64)
+    mhz = (t[:, 1] - t[:, 0]) / (t[:, 3] - t[:, 2]) * 100.0
+    ms = ev[-1][0].elapsed_time(ev[-1][1])
+    flops = wgs * 8.0 * iters * 4 * 32768
+    return {"mhz_median": round(float(np.median(mhz)), 0),
+            "mhz_p10": round(float(np.percentile(mhz, 10)), 0),
+            "mhz_p90": round(float(np.percentile(mhz, 90)), 0),
+            "bf16_mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "load": f"{wgs} workgroups x 8 waves x {iters} rounds of 4 bf16 32x32x16 MFMA"}
 
 
 def recorded_traffic(workload: str):
@@ -130,6 +234,15 @@ def main():
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
         sys.exit(2)
+
+    # The oracle's process pool is forked before anything touches the GPU; its
+    # workers run numpy only.
+    pool = None
+    workers = oracle_workers()
+    if not args.no_cpu_baseline and workers > 1:
+        import multiprocessing as mp
+
+        pool = mp.get_context("fork").Pool(workers)
 
     import numpy as np
     import torch
@@ -231,6 +344,34 @@ def main():
     sl_ms = sum(a.elapsed_time(b) for a, b in ev_sl) / args.steps
     n_diff = int((out_sl.token_ids != out.token_ids).sum())
 
+    # Each kernel alone, cold (a 512 MiB scratch write before every run).
+    iso = {}
+    if args.iso_runs > 0:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        if x is not None and w.fp8:
+            iso["quantize_hidden"] = time_alone(
+                lambda: ts.quantize_rows_e4m3(x, out=xq, scales=xsc, stream=stream),
+                stream, scratch, args.iso_runs)
+            iso["lmhead_e4m3"] = time_alone(
+                lambda: ts.lmhead_logits_local_e4m3(xq, xsc, wq, wsc, out=local, stream=stream),
+                stream, scratch, args.iso_runs)
+        elif x is not None:
+            iso["lmhead_gemm"] = time_alone(
+                lambda: ts.lmhead_logits_local(x, wt, out=local, stream=stream),
+                stream, scratch, args.iso_runs)
+        iso["assemble"] = time_alone(
+            lambda: ts.sampler_assemble_vocab_slices(slices, out=batch, stream=stream),
+            stream, scratch, args.iso_runs)
+        iso["sampler"] = time_alone(
+            lambda: ts.sampler_sample(batch, params, w.row_offset, w.max_logprobs, out=out,
+                                      workspace=ws, stream=stream),
+            stream, scratch, args.iso_runs)
+        iso["sampler_slices"] = time_alone(sample_slices, stream, scratch, args.iso_runs)
+        iso["step"] = time_alone(step, stream, scratch, args.iso_runs)
+        del scratch
+    copy_gbs = measured_copy_gbs(dev, stream)
+    clock = measured_mfma_clock(ts, dev, stream)
+
     flops = 2.0 * rows * vocab * w.hidden if w.hidden else 0.0
     sampler_bytes = 4.0 * rows * vocab + rows * (24 + 12 + 8 * w.max_logprobs)
     asm_bytes = 2 * 4.0 * rows * vocab
@@ -296,11 +437,27 @@ def main():
     }
     if quant_ms is not None:
         line["kernels"]["quantize_hidden"] = {"ms": round(quant_ms, 4)}
+    if iso:
+        algo = {"lmhead_gemm": gemm_bytes, "lmhead_e4m3": gemm_bytes, "assemble": asm_bytes,
+                "sampler": sampler_bytes, "sampler_slices": sampler_bytes}
+        for k, st in iso.items():
+            if k in algo and algo[k]:
+                st["gbs_median"] = round(algo[k] / (st["median_ms"] * 1e-3) / 1e9, 1)
+            if k in ("lmhead_gemm", "lmhead_e4m3") and flops:
+                st["tflops_median"] = round(flops / (st["median_ms"] * 1e-3) / 1e12, 1)
+            if k == "step":
+                st["rows_per_s_median"] = round(rows / (st["median_ms"] * 1e-3), 1)
+        line["isolated_cold"] = {"runs": args.iso_runs, "warmup": 5,
+                                 "scratch_write_bytes": 512 << 20, "kernels": iso}
+    line["context"] = {"copy_gbs": copy_gbs, "mfma_load": clock}
     if not args.no_cpu_baseline:
         sample_rows = min(args.cpu_rows, rows)
         logits_sample = batch[:sample_rows].cpu().numpy()
         line["cpu_baseline"] = cpu_baseline(x, wt, wq, wsc, logits_sample, params_np, w.max_logprobs,
-                                            sample_rows)
+                                            sample_rows, pool, workers)
+    if pool is not None:
+        pool.close()
+        pool.join()
     print(json.dumps(line), flush=True)
 
 

@@ -260,6 +260,23 @@ int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* sli
                                   const int64_t* slice_ld, int32_t n_slices, int64_t rows,
                                   float* out, int64_t ld_out, void* stream);
 
+/*
+ * ts_mfma_clock_probe: a measurement aid, not a step of the path.  Every
+ * workgroup (eight waves, two per SIMD) runs `iters` rounds of four
+ * independent bf16 32x32x16 matrix-core accumulations per wave and records
+ * the shader-clock counter and the constant 100 MHz real-time counter before
+ * the first round and after the last:
+ *   ticks       DEVICE uint64 [workgroups, 4]: clock start, clock end,
+ *               real-time start, real-time end (caller-owned)
+ *   workgroups  1 .. 65536 (one or more per compute unit loads every unit)
+ *   iters       1 .. 2^24
+ * The shader clock under this load is (clock end - clock start) /
+ * (real-time end - real-time start) x 100 MHz; the matrix-core rate is
+ * workgroups x 8 x iters x 4 x 32768 flop over the launch's duration.
+ * TS_EINVAL for a NULL ticks, a misaligned ticks or a size out of range.
+ */
+int ts_mfma_clock_probe(uint64_t* ticks, int32_t workgroups, int64_t iters, void* stream);
+
 /* Name of a TS_* return code (static string). */
 const char* ts_status_string(int status);
 

@@ -274,3 +274,13 @@ def test_sampler_ex_validation():
     assert ex(-1) == ts.TS_EINVAL
     assert ex(0) == ts.TS_EWORKSPACE                   # valid up to the workspace
     assert ex(ts.TS_LOGPROBS_PROCESSED) == ts.TS_EWORKSPACE
+
+
+def test_mfma_clock_probe_validation():
+    probe = ts.lib.ts_mfma_clock_probe
+    assert probe(None, 4, 16, None) == ts.TS_EINVAL
+    assert probe(FAKE + 4, 4, 16, None) == ts.TS_EINVAL        # misaligned
+    assert probe(FAKE, 0, 16, None) == ts.TS_EINVAL
+    assert probe(FAKE, 65537, 16, None) == ts.TS_EINVAL
+    assert probe(FAKE, 4, 0, None) == ts.TS_EINVAL
+    assert probe(FAKE, 4, (1 << 24) + 1, None) == ts.TS_EINVAL

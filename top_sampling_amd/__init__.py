@@ -55,6 +55,7 @@ SYMBOLS = {
     "sampler_sample_ex": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _I32, _I32, _VP,
                                          _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sampler_assemble_vocab_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _VP]),
+    "ts_mfma_clock_probe": (ctypes.c_int, [_VP, _I32, _I64, _VP]),
     "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ts_last_error": (ctypes.c_char_p, []),
 }
@@ -313,3 +314,13 @@ def sampler_sample_slices(slices, params, row_offset: int = 0, max_logprobs: int
         _ptr(out.topn_logprobs) if max_logprobs > 0 else None,
         _ptr(out.row_status), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
     return out
+
+
+def mfma_clock_probe(workgroups: int, iters: int, device, stream=None):
+    """Launch the matrix-core clock probe (a measurement aid) and return the
+    device tensor of per-workgroup ticks [workgroups, 4] (uint64 stored as
+    int64): shader clock start / end, 100 MHz real time start / end."""
+    torch = _torch()
+    ticks = torch.zeros(workgroups, 4, dtype=torch.int64, device=device)
+    _check(lib.ts_mfma_clock_probe(_ptr(ticks), workgroups, iters, _stream_ptr(stream)))
+    return ticks

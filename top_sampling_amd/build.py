@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtopsampling.so")
 SOURCES = ["api.hip", "lmhead_gemm.hip", "lmhead_fp8.hip", "sampler_fast.hip", "sampler_exact.hip",
-           "assemble.hip"]
+           "assemble.hip", "clock_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

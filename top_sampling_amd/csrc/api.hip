@@ -47,6 +47,18 @@ const char* ts_status_string(int status) {
 
 const char* ts_last_error(void) { return g_last_error; }
 
+int ts_mfma_clock_probe(uint64_t* ticks, int32_t workgroups, int64_t iters, void* stream) {
+  if (!ticks) return fail(TS_EINVAL, "NULL ticks");
+  if (!aligned(ticks, 8)) return fail(TS_EINVAL, "ticks must be 8-byte aligned");
+  if (workgroups < 1 || workgroups > 65536)
+    return fail(TS_EINVAL, "workgroups=%d outside 1..65536", workgroups);
+  if (iters < 1 || iters > (int64_t{1} << 24))
+    return fail(TS_EINVAL, "iters=%lld outside 1..2^24", static_cast<long long>(iters));
+  return hip_status(
+      ts::launch_mfma_clock_probe(ticks, workgroups, iters, static_cast<hipStream_t>(stream)),
+      "ts_mfma_clock_probe");
+}
+
 int lmhead_logits_local(const void* hidden, int64_t rows, int64_t hidden_dim, int64_t ld_hidden,
                         const void* lm_head, int64_t vocab_local, int64_t ld_lm_head,
                         float* logits, int64_t ld_logits, void* stream) {

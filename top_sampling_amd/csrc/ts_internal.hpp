@@ -70,4 +70,8 @@ struct AssembleSlices {
 hipError_t launch_assemble(const AssembleSlices& s, int64_t rows, float* out, int64_t ld_out,
                            hipStream_t stream);
 
+// ------------------------------------------------------------- measurement
+hipError_t launch_mfma_clock_probe(uint64_t* ticks, int workgroups, int64_t iters,
+                                   hipStream_t stream);
+
 }  // namespace ts
