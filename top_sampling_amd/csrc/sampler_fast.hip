@@ -205,6 +205,69 @@ __device__ __forceinline__ float wave_qth4(const float (&t)[4], int q) {
   return key_to_float(K);
 }
 
+// Chunk-pass thresholds, built on the top 16 key bits only (sign, exponent
+// and 7 mantissa bits): the largest K with zero low 16 bits and at least q
+// lanes (or, for the top-4 form, q of the wave's per-thread top-4 values) at
+// or above it.  K is at most the exact q-th largest key, so every logit the
+// exact threshold admits is admitted too; the extra ones lie within 2^-7
+// relative of it.  Half the ballots of the exact search.
+__device__ __forceinline__ float wave_qth_hi16(float x, int q) {
+  const uint32_t k = order_key(x);
+  uint32_t K = 0u;
+#pragma unroll
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t cand = K | (1u << b);
+    if (__popcll(__ballot(k >= cand)) >= q) K = cand;
+  }
+  return key_floor_value(K);
+}
+
+__device__ __forceinline__ float wave_qth4_hi16(const float (&t)[4], int q) {
+  const uint32_t k0 = order_key(t[0]), k1 = order_key(t[1]), k2 = order_key(t[2]),
+                 k3 = order_key(t[3]);
+  uint32_t K = 0u;
+#pragma unroll
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t cand = K | (1u << b);
+    const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand)) +
+                    __popcll(__ballot(k2 >= cand)) + __popcll(__ballot(k3 >= cand));
+    if (cnt >= q) K = cand;
+  }
+  return key_floor_value(K);
+}
+
+// (m & a) | (~m & b) in one v_bfi_b32.  Written as an opaque instruction so
+// that a tree of them over a register array is not turned back into an
+// indexed access (which would move the array to scratch memory).
+__device__ __forceinline__ float bit_blend(uint32_t m, float a, float b) {
+  float r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+__device__ __forceinline__ float4 blend4(uint32_t m, const float4& a, const float4& b) {
+  return make_float4(bit_blend(m, a.x, b.x), bit_blend(m, a.y, b.y), bit_blend(m, a.z, b.z),
+                     bit_blend(m, a.w, b.w));
+}
+
+// Element b (= 4 j + q) of the thread's chunk registers, for a per-lane b: a
+// blend tree over j, then over q.
+__device__ __forceinline__ float pick_logit(const float4 (&v)[AV], int b) {
+  static_assert(AV == 16, "the blend tree is written for 16 float4 per thread");
+  const uint32_t m0 = 0u - ((b >> 2) & 1u), m1 = 0u - ((b >> 3) & 1u),
+                 m2 = 0u - ((b >> 4) & 1u), m3 = 0u - ((b >> 5) & 1u);
+  float4 l1[8], l2[4], l3[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) l1[i] = blend4(m0, v[2 * i + 1], v[2 * i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) l2[i] = blend4(m1, l1[2 * i + 1], l1[2 * i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) l3[i] = blend4(m2, l2[2 * i + 1], l2[2 * i]);
+  const float4 f = blend4(m3, l3[1], l3[0]);
+  const uint32_t q0 = 0u - (b & 1u), q1 = 0u - ((b >> 1) & 1u);
+  return bit_blend(q1, bit_blend(q0, f.w, f.z), bit_blend(q0, f.y, f.x));
+}
+
 // Smallest 23-bit uniform index m = x >> 9 a token needs so that its key
 // x_tok + g(u) can exceed `bar`, given x_tok <= xm: g(u) > bar - x_tok needs
 // u > exp(-exp(xm - bar)).  The bound is lowered by a relative 2^-10 and one
@@ -246,6 +309,13 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   const int r = bid / S, c = bid - r * S;
   const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
   if (bid == 0 && tid < 2) reinterpret_cast<int*>(ws + lay.off_ctr)[tid] = 0;
+  // The chunk's loads go out first, so the parameter read and the row-kind
+  // decision overlap them (rows the chunk pass skips waste one chunk read).
+  const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
+  const int c0 = geo.gofs;  // global column of the chunk's first logit
+  const int n = geo.n;
+  float4 v[AV];
+  load_chunk<VEC>(v, geo.src, n, tid);
   const ts_row_params p = a.params[r];
   const int V = a.vocab;
   // Row-uniform values in scalar registers, so the per-kind paths below are
@@ -253,17 +323,11 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   const int kind = __builtin_amdgcn_readfirstlane(row_kind(p, V, a.max_logprobs));
   if (kind == KIND_BAD || kind == KIND_EXACT) return;
   ChunkRec* rec = reinterpret_cast<ChunkRec*>(ws + lay.off_chunk) + bid;
-  const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
-  const int c0 = geo.gofs;  // global column of the chunk's first logit
-  const int n = geo.n;
   // The temperature-scaled mass: top-p-only rows, and unfiltered rows when
   // the log-probabilities describe the sampled distribution.
   const bool topp = kind == KIND_TOPP ||
                     ((a.flags & TS_LOGPROBS_PROCESSED) && kind == KIND_FULL);
   const float inv_t = uniform_f32(kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature);
-
-  float4 v[AV];
-  load_chunk<VEC>(v, geo.src, n, tid);
 
   // The thread maximum, each float4 taken as soon as it lands (with the
   // thread's four largest values when M > 64); then sum exp(l - max) and, for
@@ -351,7 +415,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   // block's 4 * 256 top-4 values, by radix selection in LDS.
   if (M < n && M <= 256) {
     const int q = (M + AW - 1) / AW;
-    const float tw = four ? wave_qth4(t, q) : wave_qth(t[0], q);
+    const float tw = four ? wave_qth4_hi16(t, q) : wave_qth_hi16(t[0], q);
     if (lane_id == 0) sh.wthr[wave] = tw;
   } else if (M < n) {
 #pragma unroll
@@ -410,19 +474,14 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   }
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws + lay.off_cand) +
                              static_cast<size_t>(bid) * kCandCap;
-  if (cm != 0ull) {
-#pragma unroll
-    for (int j = 0; j < AV; ++j) {
-      if (((cm >> (4 * j)) & 0xFull) == 0ull) continue;
-      const int e = 4 * (j * AT + tid);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if ((cm >> (4 * j + q)) & 1ull) {
-          if (slot < kCandCap) cand[slot] = pack_cand(order_key(lane(v[j], q)), c0 + e + q);
-          ++slot;
-        }
-      }
-    }
+  // One pass per set bit of the thread's mask: the wave loops only as often
+  // as its busiest lane has candidates (candidates are sparse).
+  while (cm != 0ull) {
+    const int b = __builtin_ctzll(cm);
+    cm &= cm - 1ull;
+    const int e = 4 * ((b >> 2) * AT + tid) + (b & 3);
+    if (slot < kCandCap) cand[slot] = pack_cand(order_key(pick_logit(v, b)), c0 + e);
+    ++slot;
   }
 
   if (tid == 0) {
