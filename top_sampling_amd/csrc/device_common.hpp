@@ -135,6 +135,40 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// One DPP move of a float (ctrl and row_mask are compile-time constants);
+// lanes of rows outside row_mask keep `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                    CTRL, ROW_MASK, 0xF, false));
+}
+
+// Maximum over the wave, returned uniform (in a scalar register), by DPP:
+// a butterfly within each 16-lane row, then the rows folded with row
+// broadcasts into the last row, read from lane 63.  Every lane must be active.
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = fmaxf(v, dpp_f32<0xB1, 0xF>(v, v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E, 0xF>(v, v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x124, 0xF>(v, v));  // row_ror:4
+  v = fmaxf(v, dpp_f32<0x128, 0xF>(v, v));  // row_ror:8
+  v = fmaxf(v, dpp_f32<0x142, 0xA>(v, v));  // row_bcast:15 into rows 1 and 3
+  v = fmaxf(v, dpp_f32<0x143, 0xC>(v, v));  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// A value that at least eight lanes of the wave reach or exceed: the
+// smallest of the eight 8-lane group maxima (half rows), returned uniform.
+// It is at most the wave's eighth-largest value.  Every lane must be active.
+__device__ __forceinline__ float wave_8th_floor_uniform(float v) {
+  v = fmaxf(v, dpp_f32<0xB1, 0xF>(v, v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E, 0xF>(v, v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141, 0xF>(v, v));  // row_half_mirror: 8-lane group maximum
+  v = fminf(v, dpp_f32<0x128, 0xF>(v, v));  // row_ror:8: smaller of the row's two groups
+  v = fminf(v, dpp_f32<0x142, 0xA>(v, v));  // row_bcast:15 into rows 1 and 3
+  v = fminf(v, dpp_f32<0x143, 0xC>(v, v));  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ void wave_best(float& k, int& i) {
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) {

@@ -5,9 +5,9 @@
 // batch-sharded sampling: inside vLLM PR #61018", section "What
 // batch-sharded sampling is, in one paragraph").  The logits are read where
 // they lie: one buffer, or the vocabulary slices the exchange delivered
-// (LogitsView; chunks never straddle two slices).  It is HBM-bound: every
-// logit is read from HBM once by the chunk pass; the noise and probe passes
-// re-read only the rows that need them.
+// (LogitsView; chunks never straddle two slices).  Every logit is read from
+// HBM once by the chunk pass; the probe pass re-reads only the rows that need
+// it.
 //
 // A  chunk pass   one 256-thread workgroup per (row, chunk of <= 16384
 //                 logits), the chunk held in registers (16 float4 per
@@ -17,14 +17,14 @@
 //                     NaN or +inf shows up as a NaN sum;
 //                   - a logit candidate list holding at least the chunk's
 //                     share of the row's M largest, M = max(n_logprobs,
-//                     top_k) (64 for top-p-only rows): the threshold is the
-//                     q-th largest per-thread maximum (or top-4 value) of
-//                     each wave, found with one ballot per key bit, or an
-//                     LDS radix selection for large M.
-// N  noise        one workgroup per chunk of a full-vocabulary or top-p-only
-//                 row: Philox4x32-10 Gumbel keys, skipped for tokens whose
-//                 uniform cannot lift them over the running bar; every key
-//                 above the chunk's floor goes to a short key list.
+//                     top_k) (64 for top-p-only rows): the threshold is
+//                     bounded by the q-th largest per-thread maximum (or
+//                     top-4 value) of each wave, found with one ballot per
+//                     key bit, or an LDS radix selection for large M;
+//                   - for full-vocabulary and top-p-only rows, Philox4x32-10
+//                     Gumbel keys, skipped for tokens whose uniform cannot
+//                     lift them over the running bar; every key above the
+//                     chunk's floor goes to a short key list.
 // B  merge        one 256-thread workgroup per row: log-sum-exp; the union of
 //                 logit candidates above the highest chunk threshold is
 //                 exactly the row's logits above it.  Short prefixes (top N,
@@ -114,6 +114,7 @@ struct ChunkSmem {
   uint32_t keys4[4 * AT];  // per-thread top-4 keys (block-level selection)
   int klist[kKeyCap];
   float wthr[AW];
+  float wbar[AW];
   float rm[AW], rs[AW], rt[AW];
   int rb[AW];
   float rf[AW];
@@ -300,6 +301,105 @@ __device__ __forceinline__ void insert3(float key, int id, float (&k)[3], int (&
   }
 }
 
+// ------------------------------------------------------------- Gumbel keys
+// Gumbel keys of one chunk of a full-vocabulary or top-p-only row, drawn by
+// the chunk pass from the logits in its registers, relative to the chunk
+// maximum: x = (l - cmax) / T, key = x + g.  Full rows list the chunk's best
+// key (floor: that key); top-p-only rows list every key at or above the
+// floor.  Every thread of the workgroup calls it, with sh.nkey zero.  Returns
+// the number of keys (above kKeyCap: overflow, the list is not written).
+__device__ __forceinline__ int chunk_keys(const float4 (&v)[AV], float cmax, float inv_t, bool topp,
+                                          uint64_t seed, uint64_t grow, int c0,
+                                          int* __restrict__ klist_out, ChunkSmem& sh,
+                                          float& kfloor) {
+  const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
+  kfloor = INFINITY;
+  {
+    // Full rows keep each thread's best key; the chunk maximum's key is at
+    // least the smallest Gumbel value, so no token below that bar needs its
+    // noise.  Top-p-only rows keep each thread's best three.  The bar a token
+    // must clear is the larger of the thread's own (its best, or its third
+    // best) and the wave's, refreshed after every float4: for full rows the
+    // wave's largest best key (a token under it cannot be the chunk's best),
+    // for top-p rows a value eight of the wave's best keys reach (the
+    // smallest of the eight 8-lane group maxima).  The top-p key floor below
+    // is raised to every wave's bar, so a token skipped under a bar is under
+    // the floor and the key list above the floor stays complete; whole waves
+    // skip the Gumbel draw once a few good keys are known.
+    float kb[3] = {-INFINITY, -INFINITY, -INFINITY};
+    int ib[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
+    float wbar = topp ? -INFINITY : kMinGumbel;
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const int e = 4 * (j * AT + tid);
+      float x[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x[q] = (lane(v[j], q) - cmax) * inv_t;
+      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      const float bar = fmaxf(wbar, topp ? kb[2] : kb[0]);
+      if (xm + kGumbelMax >= bar) {  // else no key here can clear the bar (or all padding)
+        const uint32_t th = u_floor_bits(xm, bar);
+        const U32x4 w = token_words(seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if ((w.v[q] >> 9) < th || x[q] == -INFINITY) continue;
+          const float key = x[q] + gumbel_from_word(w.v[q]);
+          const int id = c0 + e + q;
+          if (topp) {
+            insert3(key, id, kb, ib);
+          } else if (better(key, id, kb[0], ib[0])) {
+            kb[0] = key;
+            ib[0] = id;
+          }
+        }
+      }
+      wbar = fmaxf(wbar, topp ? wave_8th_floor_uniform(kb[0]) : wave_max_uniform(kb[0]));
+    }
+    if (!topp) {
+      float k1 = kb[0];
+      int i1 = ib[0];
+      block_best<AT>(k1, i1, sh.rf, sh.ri);
+      if (tid == 0 && i1 != 0x7fffffff) {
+        klist_out[0] = i1;
+        sh.nkey = 1;
+      }
+      kfloor = k1;
+    } else {
+      // Floor F >= every thread's third-best key, so the tokens with key >=
+      // F all sit in the threads' top-three lists, and F >= every wave's
+      // final bar, so no skipped token lies at or above it.  F is also raised
+      // to the smallest of the four waves' third-largest best keys to keep
+      // the list short (at least twelve entries when that raises it, eight
+      // when a wave's bar does).
+      const float f0 = block_max<AT>(kb[2], sh.rf);
+      const float tw = wave_qth(kb[0], 3);
+      if (lane_id == 0) {
+        sh.wthr[wave] = tw;
+        sh.wbar[wave] = wbar;
+      }
+      __syncthreads();
+      float g = sh.wthr[0], wb = sh.wbar[0];
+#pragma unroll
+      for (int w = 1; w < AW; ++w) {
+        g = fminf(g, sh.wthr[w]);
+        wb = fmaxf(wb, sh.wbar[w]);
+      }
+      kfloor = fmaxf(fmaxf(f0, g), wb);
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        if (ib[i] != 0x7fffffff && kb[i] >= kfloor) {
+          const int slot = atomicAdd(&sh.nkey, 1);
+          if (slot < kKeyCap) sh.klist[slot] = ib[i];
+        }
+      }
+      __syncthreads();
+      if (sh.nkey <= kKeyCap && tid < sh.nkey) klist_out[tid] = sh.klist[tid];
+    }
+  }
+  __syncthreads();
+  return sh.nkey;
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLayout lay,
                                                         uint8_t* __restrict__ ws) {
@@ -484,133 +584,30 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     ++slot;
   }
 
+  // Gumbel keys for the rows that draw them over the whole vocabulary
+  // (full-vocabulary rows) or over an unknown nucleus (top-p-only rows).
+  const bool ovf = total > kCandCap;
+  int nkey = 0;
+  float kfloor = INFINITY;
+  if ((kind == KIND_FULL || kind == KIND_TOPP) && !ovf) {
+    int* klist_out = reinterpret_cast<int*>(ws + lay.off_key) + static_cast<size_t>(bid) * kKeyCap;
+    nkey = chunk_keys(v, cmax, inv_t, kind == KIND_TOPP, p.seed,
+                      static_cast<uint64_t>(a.row_offset + r), c0, klist_out, sh, kfloor);
+  }
   if (tid == 0) {
-    const bool ovf = total > kCandCap;
+    const bool key_ovf = nkey > kKeyCap;
     ChunkRec o;
     o.cmax = cmax;
     o.sumexp = s;
     o.tmass = tmass;
     o.kt = order_key(tf);
     o.ncand = ovf ? 0 : total;
-    o.status = ovf ? 2 : 0;
-    o.nkey = 0;  // the noise pass fills the Gumbel-key list
-    o.kfloor = INFINITY;
+    o.status = (ovf || key_ovf) ? 2 : 0;
+    o.nkey = key_ovf ? 0 : nkey;
+    o.kfloor = kfloor;
 #pragma unroll
     for (int i = 0; i < 8; ++i) o.pad[i] = 0;
     *rec = o;
-  }
-}
-
-// ------------------------------------------------------------------- N: noise
-// Gumbel keys of full-vocabulary and top-p-only rows, one workgroup per
-// chunk of such a row (the others exit at once); keys are taken relative to
-// the chunk maximum the chunk pass recorded: x = (l - cmax) / T, key = x + g.
-struct NoiseSmem {
-  int klist[kKeyCap];
-  float wthr[AW];
-  float rf[AW];
-  int ri[AW];
-  int nkey;
-};
-
-template <bool VEC>
-__global__ __launch_bounds__(AT) void noise_kernel(SamplerArgs a, FastLayout lay,
-                                                   uint8_t* __restrict__ ws) {
-  __shared__ NoiseSmem sh;
-  const int S = lay.S;
-  const int bid = blockIdx.x;
-  const int r = bid / S, c = bid - r * S;
-  const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
-  const ts_row_params p = a.params[r];
-  const int V = a.vocab;
-  const int kind = row_kind(p, V, a.max_logprobs);
-  if (kind != KIND_FULL && kind != KIND_TOPP) return;
-  ChunkRec* rec = reinterpret_cast<ChunkRec*>(ws + lay.off_chunk) + bid;
-  if (rec->status != 0) return;  // NaN / +inf or candidate overflow: the row goes elsewhere
-  const float cmax = rec->cmax;
-  const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
-  const int c0 = geo.gofs;  // global column of the chunk's first logit (a multiple of 4)
-  const int n = geo.n;
-  const bool topp = kind == KIND_TOPP;
-  const float inv_t = 1.0f / p.temperature;
-  if (tid == 0) sh.nkey = 0;
-  float4 v[AV];
-  load_chunk<VEC>(v, geo.src, n, tid);
-  __syncthreads();
-  // Gumbel keys relative to the chunk maximum: x = (l - cmax) / T, key = x + g.
-  float kfloor = INFINITY;
-  {
-    const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
-    // Full rows keep each thread's best key; the chunk maximum's key is at
-    // least the smallest Gumbel value, so no token below that bar needs its
-    // noise.  Top-p-only rows keep each thread's best three.
-    float kb[3] = {-INFINITY, -INFINITY, -INFINITY};
-    int ib[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
-    const float bar0 = topp ? -INFINITY : kMinGumbel;
-#pragma unroll
-    for (int j = 0; j < AV; ++j) {
-      const int e = 4 * (j * AT + tid);
-      float x[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = (lane(v[j], q) - cmax) * inv_t;
-      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      const float bar = fmaxf(bar0, topp ? kb[2] : kb[0]);
-      if (xm + kGumbelMax < bar) continue;  // also skips all-padding slots
-      const uint32_t th = u_floor_bits(xm, bar);
-      const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if ((w.v[q] >> 9) < th || x[q] == -INFINITY) continue;
-        const float key = x[q] + gumbel_from_word(w.v[q]);
-        const int id = c0 + e + q;
-        if (topp) {
-          insert3(key, id, kb, ib);
-        } else if (better(key, id, kb[0], ib[0])) {
-          kb[0] = key;
-          ib[0] = id;
-        }
-      }
-    }
-    int* klist_out = reinterpret_cast<int*>(ws + lay.off_key) + static_cast<size_t>(bid) * kKeyCap;
-    if (!topp) {
-      float k1 = kb[0];
-      int i1 = ib[0];
-      block_best<AT>(k1, i1, sh.rf, sh.ri);
-      if (tid == 0 && i1 != 0x7fffffff) {
-        klist_out[0] = i1;
-        sh.nkey = 1;
-      }
-      kfloor = k1;
-    } else {
-      // Floor F >= every thread's third-best key, so the tokens with key >=
-      // F all sit in the threads' top-three lists; F is also raised to the
-      // smallest of the four waves' third-largest best keys to keep the
-      // list short (at least twelve entries when it is raised).
-      const float f0 = block_max<AT>(kb[2], sh.rf);
-      const float tw = wave_qth(kb[0], 3);
-      if (lane_id == 0) sh.wthr[wave] = tw;
-      __syncthreads();
-      float g = sh.wthr[0];
-#pragma unroll
-      for (int w = 1; w < AW; ++w) g = fminf(g, sh.wthr[w]);
-      kfloor = fmaxf(f0, g);
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        if (ib[i] != 0x7fffffff && kb[i] >= kfloor) {
-          const int slot = atomicAdd(&sh.nkey, 1);
-          if (slot < kKeyCap) sh.klist[slot] = ib[i];
-        }
-      }
-      __syncthreads();
-      if (sh.nkey <= kKeyCap && tid < sh.nkey) klist_out[tid] = sh.klist[tid];
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const bool key_ovf = sh.nkey > kKeyCap;
-    rec->nkey = key_ovf ? 0 : sh.nkey;
-    rec->kfloor = kfloor;
-    if (key_ovf) rec->status = 2;
   }
 }
 
@@ -1346,12 +1343,6 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
   else
     hipLaunchKernelGGL(chunk_pass_kernel<false>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (vec)
-    hipLaunchKernelGGL(noise_kernel<true>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
-  else
-    hipLaunchKernelGGL(noise_kernel<false>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int force = env_flag("TS_SAMPLER_FORCE_PROBE") ? 1 : 0;
   hipLaunchKernelGGL(merge_kernel, dim3(a.rows), dim3(BT), 0, stream, a, lay, ws, force);
