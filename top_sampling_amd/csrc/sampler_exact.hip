@@ -41,6 +41,7 @@ struct FallbackSmem {
   uint32_t sel_above;
   unsigned long long sel_above_q;
   int list_n;
+  double pabove[kProbes];  // probe rows: mass above each probe
   LogitsView lv;  // the slice table, read with per-thread indices from here
 };
 
@@ -349,13 +350,22 @@ __device__ __forceinline__ void finish_probe_row(const SamplerArgs& a, const Fas
   const ts_row_params p = a.params[r];
   const double* part = reinterpret_cast<const double*>(ws + lay.off_part) +
                        static_cast<size_t>(li) * lay.S * kProbes;
+  // Thread i sums probe i's mass over the chunks (chunk order).
+  const int np = pr.npts;
+  if (static_cast<int>(threadIdx.x) < np) {
+    double above = 0.0;
+    for (int c = 0; c < lay.S; ++c) above += part[static_cast<size_t>(c) * kProbes + threadIdx.x];
+    sh.pabove[threadIdx.x] = above;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     const double target = static_cast<double>(p.top_p) * pr.z;
     int win = -1;
-    for (int i = 0; i < pr.npts && win < 0; ++i) {
-      double above = 0.0;
-      for (int c = 0; c < lay.S; ++c) above += part[static_cast<size_t>(c) * kProbes + i];
-      if (above < target) win = pr.id[i];
+    for (int i = 0; i < np; ++i) {
+      if (sh.pabove[i] < target) {
+        win = i;
+        break;
+      }
     }
     sh.list_n = win;
   }
@@ -367,8 +377,8 @@ __device__ __forceinline__ void finish_probe_row(const SamplerArgs& a, const Fas
     return;
   }
   if (threadIdx.x == 0) {
-    a.token_ids[r] = win;
-    if (a.token_logprobs) a.token_logprobs[r] = logit_at(sh.lv, r, win) - pr.lse;
+    a.token_ids[r] = pr.id[win];
+    if (a.token_logprobs) a.token_logprobs[r] = pr.pt[win] - pr.lse;  // pt: the probe's logit
     if (a.row_status) a.row_status[r] = TS_ROW_OK;
   }
 }
@@ -379,16 +389,15 @@ __global__ __launch_bounds__(XT) void sampler_finish_kernel(SamplerArgs a, FastL
                                                             uint8_t* ws, int all_rows) {
   __shared__ FallbackSmem sh;
   const int b = blockIdx.x;
+  const int* ctr = reinterpret_cast<const int*>(ws + lay.off_ctr);
+  const int n_exact = all_rows ? 0 : ctr[0], n_probe = all_rows ? 0 : ctr[1];
+  if (!all_rows && b >= n_probe + n_exact) return;  // nothing left for this workgroup
   stage_view(a.lv, sh.lv);
   if (all_rows) {
     exact_row(a, b, sh);
-    return;
-  }
-  const int* ctr = reinterpret_cast<const int*>(ws + lay.off_ctr);
-  const int n_exact = ctr[0], n_probe = ctr[1];
-  if (b < n_probe) {
+  } else if (b < n_probe) {
     finish_probe_row(a, lay, ws, b, reinterpret_cast<const int*>(ws + lay.off_probe)[b], sh);
-  } else if (b - n_probe < n_exact) {
+  } else {
     exact_row(a, reinterpret_cast<const int*>(ws + lay.off_exact)[b - n_probe], sh);
   }
 }

@@ -1270,22 +1270,33 @@ __global__ __launch_bounds__(PT) void probe_kernel(SamplerArgs a, FastLayout lay
     float acc[kProbes];
 #pragma unroll
     for (int i = 0; i < kProbes; ++i) acc[i] = 0.0f;
-    for (int e = 4 * tid; e < n; e += 4 * PT) {
-      float4 f;
-      if (vec && e + 3 < n) {
-        f = load_stream4(src + e);
-      } else {
-        f.x = e + 0 < n ? load_stream(src + e + 0) : -INFINITY;
-        f.y = e + 1 < n ? load_stream(src + e + 1) : -INFINITY;
-        f.z = e + 2 < n ? load_stream(src + e + 2) : -INFINITY;
-        f.w = e + 3 < n ? load_stream(src + e + 3) : -INFINITY;
+    // Four float4 per thread in flight per step (a fourth of the round trips
+    // of one at a time); each thread still takes its elements in the order
+    // e = 4 tid + 4 PT j, j = 0, 1, ...
+    constexpr int U = 4;
+    for (int e0 = 4 * tid; e0 < n; e0 += 4 * PT * U) {
+      float4 f[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + 4 * PT * u;
+        if (vec && e + 3 < n) {
+          f[u] = load_stream4(src + e);
+        } else {
+          f[u].x = e + 0 < n ? load_stream(src + e + 0) : -INFINITY;
+          f[u].y = e + 1 < n ? load_stream(src + e + 1) : -INFINITY;
+          f[u].z = e + 2 < n ? load_stream(src + e + 2) : -INFINITY;
+          f[u].w = e + 3 < n ? load_stream(src + e + 3) : -INFINITY;
+        }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float l = lane(f, q);
-        const float wt = __builtin_amdgcn_exp2f((l - pr.m) * sc);
+      for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int i = 0; i < kProbes; ++i) acc[i] += l > pr.pt[i] ? wt : 0.0f;
+        for (int q = 0; q < 4; ++q) {
+          const float l = lane(f[u], q);
+          const float wt = __builtin_amdgcn_exp2f((l - pr.m) * sc);
+#pragma unroll
+          for (int i = 0; i < kProbes; ++i) acc[i] += l > pr.pt[i] ? wt : 0.0f;
+        }
       }
     }
 #pragma unroll
