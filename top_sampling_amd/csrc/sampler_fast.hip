@@ -630,8 +630,10 @@ struct MergeSmem {
   float rf[BW];
   int ri[BW];
   uint32_t ru[BW];
-  uint32_t sel_d, sel_above, rmax;
-  int nlist, status, total;
+  uint32_t sel_d, sel_above, rmax, sel_cnt;
+  int nlist, status, total, nsmall;
+  uint32_t skey[BT];             // one radix bin's entries, ranked directly
+  unsigned long long smass[BT];
   float m, lse, kmin;
   uint32_t floor_key;
   double z;
@@ -675,32 +677,83 @@ __device__ void lds_bitonic_desc(unsigned long long* s, int n) {
   }
 }
 
-__device__ __forceinline__ int digit_shift(int rd) { return rd == 0 ? 21 : (rd == 1 ? 10 : 0); }
-__device__ __forceinline__ int digit_width(int rd) { return rd == 2 ? 10 : 11; }
 
-// Order key of the k-th largest entry of sh.list[0, U) (1 <= k <= U): radix
-// selection over the 32-bit key, 11/11/10-bit digits.
-__device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k) {
+// Largest key offset (key - base) over the entries of sh.list[0, U) with
+// key >= base, as a bit count: offsets fit in span_bits bits.
+__device__ int list_span_bits(MergeSmem& sh, int U, uint32_t base) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0u, pmask = 0u, rem = static_cast<uint32_t>(k);
-  for (int rd = 0; rd < 3; ++rd) {
-    const int shift = digit_shift(rd), width = digit_width(rd);
+  uint32_t mx = 0u;
+  for (int i = tid; i < U; i += BT) {
+    const uint32_t key = cand_key(sh.list[i]);
+    if (key >= base) mx = max(mx, key - base);
+  }
+  if (tid == 0) sh.rmax = 0u;
+  __syncthreads();
+  atomicMax(&sh.rmax, mx);
+  __syncthreads();
+  const uint32_t r = sh.rmax;
+  __syncthreads();
+  return r == 0u ? 0 : 32 - __builtin_clz(r);
+}
+
+// High bits (offset >> lowbit) of a key offset; no bits are left above bit 31.
+__device__ __forceinline__ uint32_t high_bits(uint32_t off, int lowbit) {
+  return lowbit >= 32 ? 0u : (off >> lowbit);
+}
+
+// Order key of the k-th largest entry of sh.list[0, U) (1 <= k <= U), every
+// key >= base.  Radix selection over the offset key - base with 11-bit digits
+// from its top bit down; as soon as the selected bin holds at most BT
+// entries, they are gathered and the k-th is found by ranking them directly
+// (ties: the key x with #{> x} < k' <= #{>= x} within the bin).
+__device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k, uint32_t base) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u, rem = static_cast<uint32_t>(k), hd = static_cast<uint32_t>(U);
+  int lowbit = list_span_bits(sh, U, base);
+  while (lowbit > 0 && hd > static_cast<uint32_t>(BT)) {
+    const int width = lowbit < 11 ? lowbit : 11;
+    const int shift = lowbit - width;
     const uint32_t dmask = (1u << width) - 1u;
+    const uint32_t hi = high_bits(prefix, lowbit);
     for (int b = tid; b < RB; b += BT) sh.hist[b] = 0u;
     __syncthreads();
     for (int i = tid; i < U; i += BT) {
-      const uint32_t key = cand_key(sh.list[i]);
-      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+      const uint32_t off = cand_key(sh.list[i]) - base;
+      if (high_bits(off, lowbit) == hi) atomicAdd(&sh.hist[(off >> shift) & dmask], 1u);
     }
     __syncthreads();
     select_digit_top<BT, RB / BT>(sh.hist, 1 << width, rem, sh.ru, &sh.sel_d, &sh.sel_above);
-    const uint32_t d = sh.sel_d, ab = sh.sel_above;
+    const uint32_t d = sh.sel_d;
+    rem -= sh.sel_above;
+    hd = sh.hist[d];
     __syncthreads();
-    rem -= ab;
     prefix |= d << shift;
-    pmask |= dmask << shift;
+    lowbit = shift;
   }
-  return prefix;
+  if (lowbit == 0) return base + prefix;
+  const uint32_t hi = high_bits(prefix, lowbit);
+  if (tid == 0) sh.nsmall = 0;
+  __syncthreads();
+  for (int i = tid; i < U; i += BT) {
+    const uint32_t key = cand_key(sh.list[i]);
+    if (high_bits(key - base, lowbit) == hi) sh.skey[atomicAdd(&sh.nsmall, 1)] = key;
+  }
+  __syncthreads();
+  const int ns = sh.nsmall;
+  if (tid < ns) {
+    const uint32_t x = sh.skey[tid];
+    uint32_t gt = 0u, ge = 0u;
+    for (int j = 0; j < ns; ++j) {
+      const uint32_t y = sh.skey[j];
+      gt += y > x ? 1u : 0u;
+      ge += y >= x ? 1u : 0u;
+    }
+    if (gt < rem && rem <= ge) sh.sel_d = x;  // equal keys write the same value
+  }
+  __syncthreads();
+  const uint32_t res = sh.sel_d;
+  __syncthreads();
+  return res;
 }
 
 // Fixed-point (2^-40) temperature-scaled weight exp((l - m) / T) of a listed
@@ -712,26 +765,37 @@ __device__ __forceinline__ unsigned long long list_mass(uint32_t key, float m, f
 // Top-p boundary among the entries of sh.list[0, U) with key >= kmin: the
 // largest key t whose entries at or above it carry mass >= target (fixed
 // point), i.e. the key of the first sorted position where the cumulative
-// mass reaches the target.  Radix selection with mass-weighted bins, from
-// the top digit down.  *found = 0 if the eligible entries' whole mass stays
-// below the target.
+// mass reaches the target.  Radix selection with mass-weighted bins over the
+// offset key - kmin, from its top bit down (each bin also counts its
+// entries, packed above the mass: a bin's mass stays below 2^52); once the
+// selected bin holds at most BT entries they are gathered and the boundary
+// is found among them directly.  Fixed-point sums are exact, so the result
+// does not depend on the order of the additions.  *found = 0 if the
+// eligible entries' whole mass stays below the target.
 __device__ uint32_t list_mass_key(MergeSmem& sh, int U, uint32_t kmin, float m, float inv_t,
                                   double target, int* found) {
   constexpr int BPT = RB / BT;
+  constexpr unsigned long long kCountOne = 1ull << 52;
+  constexpr unsigned long long kMassBits = kCountOne - 1ull;
   const int tid = threadIdx.x;
-  uint32_t prefix = 0u, pmask = 0u;
+  uint32_t prefix = 0u, hd = static_cast<uint32_t>(U);
   double rem = target;
-  for (int rd = 0; rd < 3; ++rd) {
-    const int shift = digit_shift(rd), width = digit_width(rd);
+  int lowbit = list_span_bits(sh, U, kmin);
+  bool rounds = false;
+  while (lowbit > 0 && hd > static_cast<uint32_t>(BT)) {
+    const int width = lowbit < 11 ? lowbit : 11;
+    const int shift = lowbit - width;
     const uint32_t dmask = (1u << width) - 1u;
     const int nb = 1 << width;
+    const uint32_t hi = high_bits(prefix, lowbit);
     for (int b = tid; b < RB; b += BT) sh.mhist[b] = 0ull;
     if (tid == 0) sh.sel_found = 0;
     __syncthreads();
     for (int i = tid; i < U; i += BT) {
       const uint32_t key = cand_key(sh.list[i]);
-      if (key >= kmin && (key & pmask) == prefix)
-        atomicAdd(&sh.mhist[(key >> shift) & dmask], list_mass(key, m, inv_t));
+      if (key >= kmin && high_bits(key - kmin, lowbit) == hi)
+        atomicAdd(&sh.mhist[((key - kmin) >> shift) & dmask],
+                  kCountOne + list_mass(key, m, inv_t));
     }
     __syncthreads();
     // Bins from the top digit down, BPT per thread: find d with
@@ -742,19 +806,21 @@ __device__ uint32_t list_mass_key(MergeSmem& sh, int U, uint32_t kmin, float m, 
     for (int j = 0; j < BPT; ++j) {
       const int b = nb - 1 - (tid * BPT + j);
       h[j] = b >= 0 ? sh.mhist[b] : 0ull;
-      mine += h[j];
+      mine += h[j] & kMassBits;
     }
     unsigned long long tot;
     unsigned long long ex = block_exclusive_scan<BT, unsigned long long>(mine, sh.uscan, tot);
 #pragma unroll
     for (int j = 0; j < BPT; ++j) {
       const int b = nb - 1 - (tid * BPT + j);
-      if (b >= 0 && static_cast<double>(ex) < rem && rem <= static_cast<double>(ex + h[j])) {
+      const unsigned long long hm = h[j] & kMassBits;
+      if (b >= 0 && static_cast<double>(ex) < rem && rem <= static_cast<double>(ex + hm)) {
         sh.sel_d = static_cast<uint32_t>(b);
         sh.sel_above64 = ex;
+        sh.sel_cnt = static_cast<uint32_t>(h[j] >> 52);
         sh.sel_found = 1;
       }
-      ex += h[j];
+      ex += hm;
     }
     __syncthreads();
     if (!sh.sel_found) {
@@ -763,13 +829,55 @@ __device__ uint32_t list_mass_key(MergeSmem& sh, int U, uint32_t kmin, float m, 
     }
     const uint32_t d = sh.sel_d;
     rem -= static_cast<double>(sh.sel_above64);
+    hd = sh.sel_cnt;
     __syncthreads();
     prefix |= d << shift;
-    pmask |= dmask << shift;
+    lowbit = shift;
+    rounds = true;
   }
-  *found = 1;
-  return prefix;
+  if (lowbit == 0 && rounds) {
+    *found = 1;
+    return kmin + prefix;
+  }
+  // Direct search among the (at most BT) eligible entries sharing the
+  // selected high bits.
+  const uint32_t hi = high_bits(prefix, lowbit);
+  if (tid == 0) {
+    sh.nsmall = 0;
+    sh.sel_found = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < U; i += BT) {
+    const uint32_t key = cand_key(sh.list[i]);
+    if (key >= kmin && high_bits(key - kmin, lowbit) == hi) {
+      const int slot = atomicAdd(&sh.nsmall, 1);
+      sh.skey[slot] = key;
+      sh.smass[slot] = list_mass(key, m, inv_t);
+    }
+  }
+  __syncthreads();
+  const int ns = sh.nsmall;
+  if (tid < ns) {
+    const uint32_t x = sh.skey[tid];
+    unsigned long long above = 0ull, eq = 0ull;
+    for (int j = 0; j < ns; ++j) {
+      const uint32_t y = sh.skey[j];
+      const unsigned long long w = sh.smass[j];
+      above += y > x ? w : 0ull;
+      eq += y == x ? w : 0ull;
+    }
+    if (static_cast<double>(above) < rem && rem <= static_cast<double>(above + eq)) {
+      sh.sel_d = x;  // equal keys write the same value
+      sh.sel_found = 1;
+    }
+  }
+  __syncthreads();
+  const uint32_t res = sh.sel_d;
+  *found = sh.sel_found;
+  __syncthreads();
+  return res;
 }
+
 
 // Keeps the entries of sh.list[0, U) (all with key >= floor_key) that are at
 // least the need-th largest, plus whatever shares its radix bin when the list
@@ -1107,7 +1215,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       token = gi;
     }
   } else if (kind == KIND_TOPK || kind == KIND_TOPP) {
-    const uint32_t kmin = kind == KIND_TOPK ? list_kth_key(sh, U, p.top_k) : 0u;
+    const uint32_t kmin = kind == KIND_TOPK ? list_kth_key(sh, U, p.top_k, floor_key) : 0u;
     uint32_t kept = kmin;
     if (p.top_p < 1.0f) {
       double target;
