@@ -56,6 +56,8 @@ def parse():
                     help="rows of the workload the CPU oracle is timed on")
     ap.add_argument("--iso-runs", type=int, default=50,
                     help="runs of each kernel timed alone (cold); 0 skips them")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the copy-bandwidth and clock-probe context figures")
     return ap.parse_args()
 
 
@@ -369,8 +371,8 @@ def main():
         iso["sampler_slices"] = time_alone(sample_slices, stream, scratch, args.iso_runs)
         iso["step"] = time_alone(step, stream, scratch, args.iso_runs)
         del scratch
-    copy_gbs = measured_copy_gbs(dev, stream)
-    clock = measured_mfma_clock(ts, dev, stream)
+    copy_gbs = None if args.no_context else measured_copy_gbs(dev, stream)
+    clock = None if args.no_context else measured_mfma_clock(ts, dev, stream)
 
     flops = 2.0 * rows * vocab * w.hidden if w.hidden else 0.0
     sampler_bytes = 4.0 * rows * vocab + rows * (24 + 12 + 8 * w.max_logprobs)
