@@ -437,6 +437,8 @@ def main():
         },
         "roofline": roof,
     }
+    if not flops:  # sampler-only workload: there is no projection to report
+        del line["kernels"][gemm_kernel]
     if quant_ms is not None:
         line["kernels"]["quantize_hidden"] = {"ms": round(quant_ms, 4)}
     if iso:
