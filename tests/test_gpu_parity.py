@@ -392,6 +392,31 @@ def test_sampler_logprob_widths(dev, ts, max_lp, n, route):
              res.row_status, res.flagged, lse, logits, max_frac=1.0)
 
 
+def test_sampler_long_topk_tie_runs(dev, ts, route):
+    """Top-k sets longer than 192 (settled by selection, not sorting) whose
+    top-k boundary or top-p boundary falls inside a long run of equal
+    logits: more tied entries than one per thread of the merge workgroup."""
+    rng = np.random.default_rng(23)
+    rows, V = 12, 3000
+    logits = (rng.standard_normal((rows, V)) - 3.0).astype(np.float32)
+    for r in range(rows):
+        run = [600, 300, 900][r % 3]
+        logits[r, rng.choice(V, run, replace=False)] = 2.0   # a tie run at the top
+    logits[6:, rng.choice(V, 50, replace=False)] = 2.5      # a few above the run
+    params = np.zeros(rows, dtype=workloads.PARAMS_DTYPE)
+    params["temperature"] = 0.9
+    params["top_k"] = np.array([500, 1000, 250, 700] * 3, dtype=np.int32)
+    params["top_p"] = np.array([0.5, 0.9, 1.0] * 4, dtype=np.float32)
+    params["n_logprobs"] = 5
+    params["seed"] = np.arange(rows, dtype=np.uint64) + np.uint64(77)
+    say("sampler long top-k tie runs", route)
+    got = _run_sampler(ts, dev, logits, params, 0, 5)
+    res, lse = _oracle_ref(logits, params, 0, 5)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label="tie runs")
+    assert np.all(got["row_status"] == 0)
+
+
 def test_sampler_row_offset_split_matches_single_call(dev, ts):
     """A rank's share of rows (row_offset) draws exactly what one call over all
     rows draws: the RNG is keyed on the global row."""

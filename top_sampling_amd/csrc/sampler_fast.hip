@@ -839,6 +839,18 @@ __device__ uint32_t list_mass_key(MergeSmem& sh, int U, uint32_t kmin, float m, 
     *found = 1;
     return kmin + prefix;
   }
+  if (lowbit == 0) {
+    // Every eligible entry has the key kmin (possibly more than BT of them):
+    // the boundary is kmin if their whole mass reaches the target.
+    unsigned long long mine = 0ull;
+    for (int i = tid; i < U; i += BT) {
+      const uint32_t key = cand_key(sh.list[i]);
+      if (key == kmin) mine += list_mass(key, m, inv_t);
+    }
+    const unsigned long long tot = block_sum<BT, unsigned long long>(mine, sh.uscan);
+    *found = (tot > 0ull && rem <= static_cast<double>(tot)) ? 1 : 0;
+    return kmin;
+  }
   // Direct search among the (at most BT) eligible entries sharing the
   // selected high bits.
   const uint32_t hi = high_bits(prefix, lowbit);
