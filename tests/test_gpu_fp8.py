@@ -137,6 +137,18 @@ def test_gemm_e4m3_into_wide_buffer(dev, ts):
     assert np.abs(got - oracle.lmhead_logits_e4m3(xc, xs, wc, ws)).max() <= LOGIT_TOL
 
 
+@pytest.mark.parametrize("vocab,ld", [(1001, 1028), (258, 264), (5, 8)])
+def test_gemm_e4m3_row_stores_ragged_tail(dev, ts, vocab, ld, gemm_tile):
+    """Rows that take 16-byte stores with a width that is not a multiple of 4:
+    the scaled tail is written element by element, the padding untouched."""
+    rng = np.random.default_rng(vocab + 1)
+    xc, xs = _codes(rng, 333, 256, 1.0)
+    wc, ws = _codes(rng, vocab, 256, 0.05)
+    say("gemm e4m3 row stores", vocab, ld)
+    got = _run_gemm(ts, dev, xc, xs, wc, ws, ld_extra=ld - vocab)
+    assert np.abs(got - oracle.lmhead_logits_e4m3(xc, xs, wc, ws)).max() <= LOGIT_TOL
+
+
 def test_gemm_e4m3_special_codes(dev, ts):
     """Saturated codes, subnormal codes and zero scales' neighbours: codes
     drawn uniformly over every finite E4M3 value."""

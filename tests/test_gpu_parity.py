@@ -117,6 +117,29 @@ def test_gemm_slices_into_wide_buffer(dev, ts, gemm_tile):
     assert torch.all(wide[:, vocab:] == 7.0)
 
 
+@pytest.mark.parametrize("vocab,ld", [(1001, 1028), (1023, 1024), (258, 264), (5, 8)])
+def test_gemm_row_stores_ragged_tail(dev, ts, vocab, ld, gemm_tile):
+    """An output whose rows take 16-byte stores (aligned base, leading
+    dimension a multiple of 4) but whose width is not a multiple of 4: the
+    row tail is written element by element and the padding stays untouched."""
+    import torch
+
+    rng = np.random.default_rng(vocab)
+    rows, hidden = 333, 256
+    xb = workloads.bf16_bits_from_f32(rng.standard_normal((rows, hidden)).astype(np.float32))
+    wb = workloads.bf16_bits_from_f32(
+        (rng.standard_normal((vocab, hidden)) / np.sqrt(hidden)).astype(np.float32))
+    say("gemm row stores", vocab, ld)
+    wide = torch.full((rows, ld), float("nan"), device=dev)
+    ts.lmhead_logits_local(_bf16_to_device(xb, dev), _bf16_to_device(wb, dev),
+                           out=wide[:, :vocab])
+    torch.cuda.synchronize()
+    full = wide.cpu().numpy()
+    assert np.all(np.isnan(full[:, vocab:]))
+    err = np.abs(full[:, :vocab].astype(np.float64) - oracle.lmhead_logits(xb, wb)).max()
+    assert err <= LOGIT_TOL, err
+
+
 @pytest.mark.parametrize("name,tile", [("decode", ""), ("spec_decode", ""), ("large", ""),
                                        ("draft", ""), ("spec_decode", "3"), ("large", "4")])
 def test_gemm_full_size_sampled(dev, ts, name, tile, monkeypatch):

@@ -25,10 +25,12 @@
 // lm_head fragments of a 64-wide slice stay in registers while the hidden
 // fragments stream one ahead of their MFMAs, which keeps the wave within 256
 // registers at a 160 x 64 wave tile.  Both scales are applied when the
-// accumulators are stored.
+// accumulators are stored, which goes through LDS as in the bf16 kernel:
+// row segments, 16-byte non-temporal stores.
 #include <stdlib.h>
 
 #include "ts_internal.hpp"
+#include "tile_store.hpp"
 
 namespace ts {
 namespace {
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void lmhead_e4m3_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ xs, int64_t ldx,
     const uint8_t* __restrict__ W, const float* __restrict__ wsc, int64_t ldw,
     float* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_total,
-    int tiles_per_xcd) {
+    int tiles_per_xcd, int vec_out) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -211,8 +213,28 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void lmhead_e4m3_kernel(
                                                                        0, 0, 0, 0);
       }
     }
+    // Schedule per 64-wide slice: the B fragments and the first A fragment
+    // (two 16-byte LDS reads each), then for every row block the next A
+    // fragment's reads ahead of this block's MFMAs, so each LDS read has a
+    // block of MFMAs to hide behind.
+#pragma unroll
+    for (int kk = 0; kk < kFbk / 64; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * TN + 2, 0);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if (i + 1 < TM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, TN, 0);
+      }
+    }
   }
 
+  if (vec_out) {
+    static_assert(NW * kTileStoreFloats * 4 <= 2 * STAGE, "tile-store scratch fits the stages");
+    __syncthreads();  // every wave is done reading the stage buffers
+    store_tile_rows<true>(acc, reinterpret_cast<float*>(lds), wave, lane, C, ldc, m0 + wm0,
+                          n0 + wn0, M, N, xs, wsc);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int col = n0 + wn0 + j * 32 + frow;
@@ -239,9 +261,10 @@ hipError_t launch_e4m3(const uint8_t* X, const float* xs, int64_t ldx, const uin
   const int tiles_n = (N + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
   const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int vec_out = rows_take_vector_stores(C, ldc);
   hipLaunchKernelGGL((lmhead_e4m3_kernel<BM, BN, WAVES_M, WAVES_N, NTLOAD>), dim3(per_xcd * kXcds),
                      dim3(64 * WAVES_M * WAVES_N), 0, stream, X, xs, ldx, W, wsc, ldw, C, ldc, M,
-                     N, K, tiles_m, total, per_xcd);
+                     N, K, tiles_m, total, per_xcd, vec_out);
   return hipGetLastError();
 }
 

@@ -13,12 +13,17 @@
 // hidden sizes that are not a multiple of 64.  LDS rows are 128 bytes (64
 // bf16) with the 16-byte chunk index XOR-swizzled by the row pair, so the
 // fragment reads of 32 consecutive rows spread over all banks.  The fp32
-// logits are written with non-temporal stores.  Tiles are ordered so that the
+// logits leave through LDS: each wave turns its accumulator blocks into row
+// segments and writes them with 16-byte non-temporal stores, a quarter of the
+// store instructions of writing them from the MFMA layout (that epilogue cost
+// about a fifth of the kernel at 640 x 151,936 x 4,096; outputs whose rows
+// cannot take 16-byte stores keep the direct 4-byte path).  Tiles are ordered so that the
 // workgroups sharing one lm_head strip run on the same XCD back to back (the
 // strip is then read from HBM once and reused from that XCD's L2).
 #include <stdlib.h>
 
 #include "ts_internal.hpp"
+#include "tile_store.hpp"
 
 namespace ts {
 namespace {
@@ -188,7 +193,7 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, int NTLOAD>
 __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void lmhead_gemm_dl_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W, int64_t ldw,
     float* __restrict__ C, int64_t ldc, int M, int N, int K, int tiles_m, int tiles_total,
-    int tiles_per_xcd) {
+    int tiles_per_xcd, int vec_out) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
@@ -299,6 +304,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void lmhead_gemm_dl_kern
     }
   }
 
+  if (vec_out) {
+    __syncthreads();  // every wave is done reading the stage buffers
+    static_assert(NW * kTileStoreFloats * 4 <= 2 * STAGE, "tile-store scratch fits the stages");
+    store_tile_rows<false>(acc, reinterpret_cast<float*>(lds), wave, lane, C, ldc, m0 + wm0,
+                           n0 + wn0, M, N, nullptr, nullptr);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -322,9 +334,10 @@ hipError_t launch_dl(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t 
   const int tiles_n = (N + BN - 1) / BN;
   const int total = tiles_m * tiles_n;
   const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int vec_out = rows_take_vector_stores(C, ldc);
   hipLaunchKernelGGL((lmhead_gemm_dl_kernel<BM, BN, WAVES_M, WAVES_N, NTLOAD>),
                      dim3(per_xcd * kXcds), dim3(64 * WAVES_M * WAVES_N), 0, stream, X, ldx, W, ldw,
-                     C, ldc, M, N, K, tiles_m, total, per_xcd);
+                     C, ldc, M, N, K, tiles_m, total, per_xcd, vec_out);
   return hipGetLastError();
 }
 
