@@ -178,11 +178,14 @@ def measured_copy_gbs(dev, stream, nbytes: int = 1 << 30, runs: int = 20) -> flo
     return round(2.0 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def measured_mfma_clock(ts, dev, stream, iters: int = 1 << 18, launches: int = 3) -> dict:
+def measured_mfma_clock(ts, dev, stream, iters: int = 1 << 18, launches: int = 3,
+                        random: bool = False) -> dict:
     """The shader clock and the bf16 matrix-core rate under a dense MFMA load
     on every compute unit (the library's clock probe: per workgroup, the
     shader-clock counter against the 100 MHz real-time counter), from the
-    last of `launches` back-to-back launches, after the clock has settled."""
+    last of `launches` back-to-back launches, after the clock has settled.
+    `random` gives the MFMAs random operand bits (as real data has) instead
+    of a few small values."""
     import numpy as np
     import torch
 
@@ -192,7 +195,7 @@ def measured_mfma_clock(ts, dev, stream, iters: int = 1 << 18, launches: int = 3
           for _ in range(launches)]
     for a, b in ev:
         a.record(stream)
-        ticks = ts.mfma_clock_probe(wgs, iters, dev, stream=stream)
+        ticks = ts.mfma_clock_probe(wgs, iters, dev, stream=stream, random=random)
         b.record(stream)
     torch.cuda.synchronize()
     t = ticks.cpu().numpy().astype(np.float64)
@@ -203,28 +206,41 @@ def measured_mfma_clock(ts, dev, stream, iters: int = 1 << 18, launches: int = 3
             "mhz_p10": round(float(np.percentile(mhz, 10)), 0),
             "mhz_p90": round(float(np.percentile(mhz, 90)), 0),
             "bf16_mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
-            "load": f"{wgs} workgroups x 8 waves x {iters} rounds of 4 bf16 32x32x16 MFMA"}
+            "load": f"{wgs} workgroups x 8 waves x {iters} rounds of 4 bf16 32x32x16 MFMA, "
+                    f"{'random' if random else 'small'} operands"}
+
+
+# Workloads with a committed counter summary: (summary file, projection
+# kernel, kernel sources the summary's hash covers, in order).
+TRAFFIC_RECORDS = {
+    "spec_decode": ("spec_decode_step_hbm_traffic.txt", "lmhead_gemm",
+                    ["lmhead_gemm.hip", "tile_store.hpp"]),
+    "fp8": ("fp8_step_hbm_traffic.txt", "lmhead_e4m3", ["lmhead_fp8.hip", "tile_store.hpp"]),
+}
 
 
 def recorded_traffic(workload: str):
     """HBM bytes per projection launch from the committed counter summary
     (FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or None when
-    the summary is for another workload or the kernel source has changed
+    there is no summary for the workload or the kernel sources have changed
     since the counters were taken."""
     import hashlib
 
-    if workload != "spec_decode":
+    if workload not in TRAFFIC_RECORDS:
         return None
-    path = os.path.join(ROOT, "profiles", "spec_decode_step_hbm_traffic.txt")
-    src = os.path.join(ROOT, "top_sampling_amd", "csrc", "lmhead_gemm.hip")
+    fname, kernel, sources = TRAFFIC_RECORDS[workload]
+    path = os.path.join(ROOT, "profiles", fname)
     try:
         text = open(path).read()
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for src in sources:
+            h.update(open(os.path.join(ROOT, "top_sampling_amd", "csrc", src), "rb").read())
+        digest = h.hexdigest()[:16]
     except OSError:
         return None
     for ln in text.splitlines():
         f = ln.split()
-        if len(f) == 3 and f[0] == "lmhead_gemm" and f[1].startswith("traffic_bytes_per_launch="):
+        if len(f) == 3 and f[0] == kernel and f[1].startswith("traffic_bytes_per_launch="):
             if f[2] == f"source_sha256_16={digest}":
                 return int(f[1].split("=", 1)[1])
     return None
@@ -373,6 +389,7 @@ def main():
         del scratch
     copy_gbs = None if args.no_context else measured_copy_gbs(dev, stream)
     clock = None if args.no_context else measured_mfma_clock(ts, dev, stream)
+    clock_rnd = None if args.no_context else measured_mfma_clock(ts, dev, stream, random=True)
 
     flops = 2.0 * rows * vocab * w.hidden if w.hidden else 0.0
     sampler_bytes = 4.0 * rows * vocab + rows * (24 + 12 + 8 * w.max_logprobs)
@@ -453,7 +470,7 @@ def main():
                 st["rows_per_s_median"] = round(rows / (st["median_ms"] * 1e-3), 1)
         line["isolated_cold"] = {"runs": args.iso_runs, "warmup": 5,
                                  "scratch_write_bytes": 512 << 20, "kernels": iso}
-    line["context"] = {"copy_gbs": copy_gbs, "mfma_load": clock}
+    line["context"] = {"copy_gbs": copy_gbs, "mfma_load": clock, "mfma_load_random": clock_rnd}
     if not args.no_cpu_baseline:
         sample_rows = min(args.cpu_rows, rows)
         logits_sample = batch[:sample_rows].cpu().numpy()

@@ -270,12 +270,19 @@ int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* sli
  *               real-time start, real-time end (caller-owned)
  *   workgroups  1 .. 65536 (one or more per compute unit loads every unit)
  *   iters       1 .. 2^24
+ *   operands    TS_PROBE_SMALL_OPERANDS (a few small values: little bit
+ *               switching) or TS_PROBE_RANDOM_OPERANDS (random bit patterns
+ *               per lane, finite): the sustained rate depends on the data
  * The shader clock under this load is (clock end - clock start) /
  * (real-time end - real-time start) x 100 MHz; the matrix-core rate is
  * workgroups x 8 x iters x 4 x 32768 flop over the launch's duration.
- * TS_EINVAL for a NULL ticks, a misaligned ticks or a size out of range.
+ * TS_EINVAL for a NULL ticks, a misaligned ticks, a size out of range or an
+ * unknown operands value.
  */
-int ts_mfma_clock_probe(uint64_t* ticks, int32_t workgroups, int64_t iters, void* stream);
+#define TS_PROBE_SMALL_OPERANDS 0
+#define TS_PROBE_RANDOM_OPERANDS 1
+int ts_mfma_clock_probe(uint64_t* ticks, int32_t workgroups, int64_t iters, int32_t operands,
+                        void* stream);
 
 /* Name of a TS_* return code (static string). */
 const char* ts_status_string(int status);

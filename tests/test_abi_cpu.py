@@ -34,7 +34,9 @@ def test_header_symbols_exported():
 def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name, val in [("TS_MAX_LOGPROBS", ts.TS_MAX_LOGPROBS), ("TS_MAX_SLICES", ts.TS_MAX_SLICES),
-                      ("TS_LOGPROBS_PROCESSED", ts.TS_LOGPROBS_PROCESSED)]:
+                      ("TS_LOGPROBS_PROCESSED", ts.TS_LOGPROBS_PROCESSED),
+                      ("TS_PROBE_SMALL_OPERANDS", ts.TS_PROBE_SMALL_OPERANDS),
+                      ("TS_PROBE_RANDOM_OPERANDS", ts.TS_PROBE_RANDOM_OPERANDS)]:
         assert re.search(rf"#define {name} {val}\b", text)
     assert workloads.PARAMS_DTYPE.itemsize == ts.PARAMS_BYTES
 
@@ -278,9 +280,11 @@ def test_sampler_ex_validation():
 
 def test_mfma_clock_probe_validation():
     probe = ts.lib.ts_mfma_clock_probe
-    assert probe(None, 4, 16, None) == ts.TS_EINVAL
-    assert probe(FAKE + 4, 4, 16, None) == ts.TS_EINVAL        # misaligned
-    assert probe(FAKE, 0, 16, None) == ts.TS_EINVAL
-    assert probe(FAKE, 65537, 16, None) == ts.TS_EINVAL
-    assert probe(FAKE, 4, 0, None) == ts.TS_EINVAL
-    assert probe(FAKE, 4, (1 << 24) + 1, None) == ts.TS_EINVAL
+    rnd = ts.TS_PROBE_RANDOM_OPERANDS
+    assert probe(None, 4, 16, rnd, None) == ts.TS_EINVAL
+    assert probe(FAKE + 4, 4, 16, rnd, None) == ts.TS_EINVAL        # misaligned
+    assert probe(FAKE, 0, 16, rnd, None) == ts.TS_EINVAL
+    assert probe(FAKE, 65537, 16, rnd, None) == ts.TS_EINVAL
+    assert probe(FAKE, 4, 0, rnd, None) == ts.TS_EINVAL
+    assert probe(FAKE, 4, (1 << 24) + 1, rnd, None) == ts.TS_EINVAL
+    assert probe(FAKE, 4, 16, 2, None) == ts.TS_EINVAL              # unknown operand mode

@@ -14,10 +14,11 @@ def test_mfma_clock_probe_ticks():
 
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     dev = torch.device("cuda:0")
-    print("mfma clock probe 64 x 4096", flush=True)
-    ticks = ts.mfma_clock_probe(64, 4096, dev)
-    torch.cuda.synchronize()
-    t = ticks.cpu().numpy().astype(np.float64)
-    assert np.all(t[:, 1] > t[:, 0]) and np.all(t[:, 3] > t[:, 2])
-    mhz = (t[:, 1] - t[:, 0]) / (t[:, 3] - t[:, 2]) * 100.0
-    assert np.all((mhz > 300) & (mhz < 3500)), mhz
+    for random in (False, True):
+        print("mfma clock probe 64 x 4096, random operands:", random, flush=True)
+        ticks = ts.mfma_clock_probe(64, 4096, dev, random=random)
+        torch.cuda.synchronize()
+        t = ticks.cpu().numpy().astype(np.float64)
+        assert np.all(t[:, 1] > t[:, 0]) and np.all(t[:, 3] > t[:, 2])
+        mhz = (t[:, 1] - t[:, 0]) / (t[:, 3] - t[:, 2]) * 100.0
+        assert np.all((mhz > 300) & (mhz < 3500)), mhz

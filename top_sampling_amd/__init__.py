@@ -37,6 +37,7 @@ TS_ROW_OK, TS_ROW_BAD_PARAMS, TS_ROW_BAD_LOGITS = 0, 1, 2
 TS_MAX_LOGPROBS = 1024
 TS_MAX_SLICES = 64
 TS_LOGPROBS_PROCESSED = 1
+TS_PROBE_SMALL_OPERANDS, TS_PROBE_RANDOM_OPERANDS = 0, 1
 PARAMS_BYTES = 24
 
 # (name, restype, argtypes) of every symbol the header declares.
@@ -55,7 +56,7 @@ SYMBOLS = {
     "sampler_sample_ex": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _I32, _I32, _VP,
                                          _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sampler_assemble_vocab_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _VP]),
-    "ts_mfma_clock_probe": (ctypes.c_int, [_VP, _I32, _I64, _VP]),
+    "ts_mfma_clock_probe": (ctypes.c_int, [_VP, _I32, _I64, _I32, _VP]),
     "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ts_last_error": (ctypes.c_char_p, []),
 }
@@ -316,11 +317,13 @@ def sampler_sample_slices(slices, params, row_offset: int = 0, max_logprobs: int
     return out
 
 
-def mfma_clock_probe(workgroups: int, iters: int, device, stream=None):
+def mfma_clock_probe(workgroups: int, iters: int, device, stream=None, random: bool = False):
     """Launch the matrix-core clock probe (a measurement aid) and return the
     device tensor of per-workgroup ticks [workgroups, 4] (uint64 stored as
-    int64): shader clock start / end, 100 MHz real time start / end."""
+    int64): shader clock start / end, 100 MHz real time start / end.
+    ``random`` selects random operand bits instead of a few small values."""
     torch = _torch()
     ticks = torch.zeros(workgroups, 4, dtype=torch.int64, device=device)
-    _check(lib.ts_mfma_clock_probe(_ptr(ticks), workgroups, iters, _stream_ptr(stream)))
+    mode = TS_PROBE_RANDOM_OPERANDS if random else TS_PROBE_SMALL_OPERANDS
+    _check(lib.ts_mfma_clock_probe(_ptr(ticks), workgroups, iters, mode, _stream_ptr(stream)))
     return ticks

@@ -47,16 +47,21 @@ const char* ts_status_string(int status) {
 
 const char* ts_last_error(void) { return g_last_error; }
 
-int ts_mfma_clock_probe(uint64_t* ticks, int32_t workgroups, int64_t iters, void* stream) {
+int ts_mfma_clock_probe(uint64_t* ticks, int32_t workgroups, int64_t iters, int32_t operands,
+                        void* stream) {
   if (!ticks) return fail(TS_EINVAL, "NULL ticks");
   if (!aligned(ticks, 8)) return fail(TS_EINVAL, "ticks must be 8-byte aligned");
   if (workgroups < 1 || workgroups > 65536)
     return fail(TS_EINVAL, "workgroups=%d outside 1..65536", workgroups);
   if (iters < 1 || iters > (int64_t{1} << 24))
     return fail(TS_EINVAL, "iters=%lld outside 1..2^24", static_cast<long long>(iters));
-  return hip_status(
-      ts::launch_mfma_clock_probe(ticks, workgroups, iters, static_cast<hipStream_t>(stream)),
-      "ts_mfma_clock_probe");
+  if (operands != TS_PROBE_SMALL_OPERANDS && operands != TS_PROBE_RANDOM_OPERANDS)
+    return fail(TS_EINVAL, "operands=%d is neither TS_PROBE_SMALL_OPERANDS nor "
+                "TS_PROBE_RANDOM_OPERANDS", operands);
+  return hip_status(ts::launch_mfma_clock_probe(ticks, workgroups, iters,
+                                                operands == TS_PROBE_RANDOM_OPERANDS ? 1 : 0,
+                                                static_cast<hipStream_t>(stream)),
+                    "ts_mfma_clock_probe");
 }
 
 int lmhead_logits_local(const void* hidden, int64_t rows, int64_t hidden_dim, int64_t ld_hidden,

@@ -6,7 +6,11 @@
 // accumulations (enough independent work to keep the matrix pipe issuing back
 // to back), eight waves per workgroup (two per SIMD).  Lane 0 of wave 0 reads
 // the shader-clock counter (s_memtime) and the constant 100 MHz real-time
-// counter (s_memrealtime) before the first round and after the last.
+// counter (s_memrealtime) before the first round and after the last.  The
+// operands are either a few small values (little bit switching) or random
+// bit patterns per lane: on this part the matrix cores' sustained rate
+// depends on the data, and random operands (like real weights and
+// activations) draw more power.
 #include "ts_internal.hpp"
 
 namespace ts {
@@ -17,14 +21,31 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kProbeThreads = 512;
 
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
 __global__ __launch_bounds__(kProbeThreads) void mfma_clock_kernel(uint64_t* __restrict__ ticks,
-                                                                   int64_t iters) {
+                                                                   int64_t iters, int random) {
   const int tid = threadIdx.x;
   bf16x8 a, b;
+  if (random) {
+    // xorshift32 per lane; exponent bit 14 cleared so no value is Inf or NaN
+    uint32_t h = (blockIdx.x * static_cast<uint32_t>(kProbeThreads) + tid) * 2654435761u + 12345u;
+    s16x8 ra, rb;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = static_cast<__bf16>(0.001f * static_cast<float>((tid + i) & 7));
-    b[i] = static_cast<__bf16>(0.002f * static_cast<float>((tid * 3 + i) & 7));
+    for (int i = 0; i < 8; ++i) {
+      h ^= h << 13; h ^= h >> 17; h ^= h << 5;
+      ra[i] = static_cast<short>(h & 0xbfffu);
+      h ^= h << 13; h ^= h >> 17; h ^= h << 5;
+      rb[i] = static_cast<short>(h & 0xbfffu);
+    }
+    a = __builtin_bit_cast(bf16x8, ra);
+    b = __builtin_bit_cast(bf16x8, rb);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = static_cast<__bf16>(0.001f * static_cast<float>((tid + i) & 7));
+      b[i] = static_cast<__bf16>(0.002f * static_cast<float>((tid * 3 + i) & 7));
+    }
   }
   f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
   __syncthreads();
@@ -54,10 +75,10 @@ __global__ __launch_bounds__(kProbeThreads) void mfma_clock_kernel(uint64_t* __r
 
 }  // namespace
 
-hipError_t launch_mfma_clock_probe(uint64_t* ticks, int workgroups, int64_t iters,
+hipError_t launch_mfma_clock_probe(uint64_t* ticks, int workgroups, int64_t iters, int random,
                                    hipStream_t stream) {
   hipLaunchKernelGGL(mfma_clock_kernel, dim3(static_cast<unsigned>(workgroups)),
-                     dim3(kProbeThreads), 0, stream, ticks, iters);
+                     dim3(kProbeThreads), 0, stream, ticks, iters, random);
   return hipGetLastError();
 }
 

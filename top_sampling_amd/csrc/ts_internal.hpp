@@ -71,7 +71,7 @@ hipError_t launch_assemble(const AssembleSlices& s, int64_t rows, float* out, in
                            hipStream_t stream);
 
 // ------------------------------------------------------------- measurement
-hipError_t launch_mfma_clock_probe(uint64_t* ticks, int workgroups, int64_t iters,
+hipError_t launch_mfma_clock_probe(uint64_t* ticks, int workgroups, int64_t iters, int random,
                                    hipStream_t stream);
 
 }  // namespace ts
