@@ -191,21 +191,6 @@ __device__ __forceinline__ float wave_qth(float x, int q) {
   return key_to_float(K);
 }
 
-// The same over the wave's per-thread top-4 values (q <= 256).
-__device__ __forceinline__ float wave_qth4(const float (&t)[4], int q) {
-  const uint32_t k0 = order_key(t[0]), k1 = order_key(t[1]), k2 = order_key(t[2]),
-                 k3 = order_key(t[3]);
-  uint32_t K = 0u;
-#pragma unroll
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = K | (1u << b);
-    const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand)) +
-                    __popcll(__ballot(k2 >= cand)) + __popcll(__ballot(k3 >= cand));
-    if (cnt >= q) K = cand;
-  }
-  return key_to_float(K);
-}
-
 // Chunk-pass thresholds, built on the top 16 key bits only (sign, exponent
 // and 7 mantissa bits): the largest K with zero low 16 bits and at least q
 // lanes (or, for the top-4 form, q of the wave's per-thread top-4 values) at
