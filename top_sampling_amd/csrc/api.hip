@@ -292,7 +292,7 @@ int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* sli
     s.col_off[i] = total;
     vec4 = vec4 && aligned(slices[i], 16) && (slice_ld[i] % 4 == 0) && (c % 4 == 0) &&
            (total % 4 == 0);
-    s.chunk_start[i + 1] = s.chunk_start[i] + (c + 4095) / 4096;
+    s.chunk_start[i + 1] = s.chunk_start[i] + (c + ts::kAssembleChunk - 1) / ts::kAssembleChunk;
     total += c;
   }
   if (ld_out < total) return fail(TS_EINVAL, "ld_out %lld below total width %lld",

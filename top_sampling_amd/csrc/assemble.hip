@@ -5,8 +5,8 @@
 // with an all-to-all).
 //
 // HBM-bound copy: every byte is read once and written once.  One workgroup
-// copies one 4096-float column chunk of one slice for a stride of rows;
-// 16-byte loads and stores when every slice allows them.
+// copies one kAssembleChunk-float column chunk of one slice for a stride of
+// rows; 16-byte loads and stores when every slice allows them.
 #include "device_common.hpp"
 #include "ts_internal.hpp"
 
@@ -14,7 +14,8 @@ namespace ts {
 namespace {
 
 constexpr int kAsmThreads = 256;
-constexpr int kAsmChunk = 4096;  // floats per workgroup per row (16 per thread)
+constexpr int kAsmChunk = static_cast<int>(kAssembleChunk);
+static_assert(kAsmChunk % (4 * kAsmThreads) == 0, "whole float4s per thread");
 
 __global__ __launch_bounds__(kAsmThreads) void assemble_kernel(AssembleSlices s, int64_t rows,
                                                                float* __restrict__ out,
