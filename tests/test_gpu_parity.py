@@ -6,6 +6,7 @@ except token ids on rows the oracle flags (top-p boundary mass within 1e-5 of
 p, or two best Gumbel keys within 1e-4), which must stay below 0.1% of rows;
 slice assembly bit-exact.
 """
+import math
 import os
 import sys
 
@@ -438,6 +439,51 @@ def test_sampler_long_topk_tie_runs(dev, ts, route):
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
              res.row_status, res.flagged, lse, logits, max_frac=1.0, label="tie runs")
     assert np.all(got["row_status"] == 0)
+
+
+def _kept_by_definition(l, t, k, p):
+    """The kept set written out from its definition, by brute force on a
+    short row: v is in the top-k set iff fewer than k logits are strictly
+    larger (k = 0: every token), and kept iff the temperature-scaled mass of
+    the top-k tokens with a strictly larger logit is below p times the set's
+    mass."""
+    n = len(l)
+    top = [v for v in range(n) if k == 0 or sum(l[u] > l[v] for u in range(n)) < k]
+    if p >= 1.0:
+        return top
+    m = max(l)
+    w = {u: math.exp((l[u] - m) / t) for u in top}
+    z = math.fsum(w.values())
+    return [v for v in top if math.fsum(w[u] for u in top if l[u] > l[v]) < p * z]
+
+
+@pytest.mark.parametrize("t,k,p", [(1.0, 0, 1.0), (0.6, 0, 0.8), (1.4, 4, 1.0), (0.9, 5, 0.7)])
+def test_gumbel_max_frequencies_chi_square(dev, ts, t, k, p, route):
+    """The sampled tokens follow the filtered softmax (the Gumbel-max
+    theorem): one row repeated over 200,000 rows, each drawing its own noise
+    (the generator is keyed on the row), token frequencies against
+    softmax(l / T) over the kept set under a chi-square test; no token outside
+    the kept set is ever drawn."""
+    import scipy.stats
+
+    l = np.array([1.2, 0.3, -0.4, 0.9, 0.0, -1.0, 0.5], dtype=np.float32)
+    kept = _kept_by_definition([float(x) for x in l], t, k, p)
+    z = np.exp((l[kept].astype(np.float64) - l.max()) / t)
+    probs = z / z.sum()
+    draws = 200_000
+    logits = np.ascontiguousarray(np.broadcast_to(l, (draws, l.size)))
+    params = np.zeros(draws, dtype=workloads.PARAMS_DTYPE)
+    params["temperature"], params["top_k"], params["top_p"] = t, k, p
+    params["seed"] = 1234
+    say("gumbel chi-square", t, k, p, route)
+    got = _run_sampler(ts, dev, logits, params, 0, 0)
+    assert np.all(got["row_status"] == 0)
+    counts = np.bincount(got["token_ids"], minlength=l.size)
+    assert counts[[v for v in range(l.size) if v not in kept]].sum() == 0
+    if len(kept) > 1:
+        assert scipy.stats.chisquare(counts[kept], probs * draws).pvalue > 1e-3
+    else:
+        assert counts[kept[0]] == draws
 
 
 def test_sampler_row_offset_split_matches_single_call(dev, ts):

@@ -133,6 +133,7 @@ struct ProbeRec {  // a top-p-only row whose boundary lies below the listed logi
 struct FastLayout {
   int S;  // chunks per row
   int L;  // logits per chunk (multiple of 4; a slice's last chunk may be shorter)
+  int cc;  // candidate slots per chunk: min(kCandCap, L) (a chunk lists at most L)
   int nsl;                      // column slices
   int cbase[TS_MAX_SLICES + 1];  // first chunk of each slice (chunks never straddle slices)
   size_t off_ctr, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part, total;
@@ -168,6 +169,7 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n) {
   L = (L + 3) / 4 * 4;
   if (L < 4) L = 4;
   l.L = static_cast<int>(L);
+  l.cc = l.L < kCandCap ? l.L : kCandCap;
   l.nsl = n;
   int64_t total = 0;
   l.cbase[0] = 0;
@@ -190,7 +192,7 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n) {
   l.off_chunk = off;
   off = align_up(off + RS * sizeof(ChunkRec), 256);
   l.off_cand = off;
-  off = align_up(off + RS * kCandCap * sizeof(unsigned long long), 256);
+  off = align_up(off + RS * static_cast<size_t>(l.cc) * sizeof(unsigned long long), 256);
   l.off_key = off;
   off = align_up(off + RS * kKeyCap * sizeof(int), 256);
   l.off_prec = off;

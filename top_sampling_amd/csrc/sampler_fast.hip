@@ -558,20 +558,20 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     total += c;
   }
   unsigned long long* cand = reinterpret_cast<unsigned long long*>(ws + lay.off_cand) +
-                             static_cast<size_t>(bid) * kCandCap;
+                             static_cast<size_t>(bid) * lay.cc;
   // One pass per set bit of the thread's mask: the wave loops only as often
   // as its busiest lane has candidates (candidates are sparse).
   while (cm != 0ull) {
     const int b = __builtin_ctzll(cm);
     cm &= cm - 1ull;
     const int e = 4 * ((b >> 2) * AT + tid) + (b & 3);
-    if (slot < kCandCap) cand[slot] = pack_cand(order_key(pick_logit(v, b)), c0 + e);
+    if (slot < lay.cc) cand[slot] = pack_cand(order_key(pick_logit(v, b)), c0 + e);
     ++slot;
   }
 
   // Gumbel keys for the rows that draw them over the whole vocabulary
   // (full-vocabulary rows) or over an unknown nucleus (top-p-only rows).
-  const bool ovf = total > kCandCap;
+  const bool ovf = total > lay.cc;
   int nkey = 0;
   float kfloor = INFINITY;
   if ((kind == KIND_FULL || kind == KIND_TOPP) && !ovf) {
@@ -1053,14 +1053,14 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   // over it read global memory (L2-resident), four entries in flight per
   // thread.
   const unsigned long long* cand = reinterpret_cast<const unsigned long long*>(ws + lay.off_cand) +
-                                   static_cast<size_t>(r) * S * kCandCap;
+                                   static_cast<size_t>(r) * S * lay.cc;
   auto cand_at = [&](int g) -> unsigned long long {
     int lo = 0, hi = S - 1;  // chunk c with pos[c] <= g < pos[c + 1]
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (sh.pos[mid] <= g) lo = mid; else hi = mid - 1;
     }
-    return cand[static_cast<size_t>(lo) * kCandCap + (g - sh.pos[lo])];
+    return cand[static_cast<size_t>(lo) * lay.cc + (g - sh.pos[lo])];
   };
   if (total > kListMax) {
     // Raise the floor to the row's M-th largest candidate: radix selection
