@@ -304,13 +304,14 @@ __device__ __forceinline__ int chunk_keys(const float4 (&v)[AV], float cmax, flo
     // least the smallest Gumbel value, so no token below that bar needs its
     // noise.  Top-p-only rows keep each thread's best three.  The bar a token
     // must clear is the larger of the thread's own (its best, or its third
-    // best) and the wave's, refreshed after every float4: for full rows the
-    // wave's largest best key (a token under it cannot be the chunk's best),
-    // for top-p rows a value eight of the wave's best keys reach (the
-    // smallest of the eight 8-lane group maxima).  The top-p key floor below
-    // is raised to every wave's bar, so a token skipped under a bar is under
-    // the floor and the key list above the floor stays complete; whole waves
-    // skip the Gumbel draw once a few good keys are known.
+    // best) and the wave's, refreshed after five of the sixteen float4s: for
+    // full rows the wave's largest best key (a token under it cannot be the
+    // chunk's best), for top-p rows a value eight of the wave's best keys
+    // reach (the smallest of the eight 8-lane group maxima).  The top-p key
+    // floor below is raised to every wave's bar, so a token skipped under a
+    // bar is under the floor and the key list above the floor stays
+    // complete; whole waves skip the Gumbel draw once a few good keys are
+    // known.
     float kb[3] = {-INFINITY, -INFINITY, -INFINITY};
     int ib[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
     float wbar = topp ? -INFINITY : kMinGumbel;
@@ -338,7 +339,9 @@ __device__ __forceinline__ int chunk_keys(const float4 (&v)[AV], float cmax, flo
           }
         }
       }
-      wbar = fmaxf(wbar, topp ? wave_8th_floor_uniform(kb[0]) : wave_max_uniform(kb[0]));
+      // Refreshed early and then less often: the bar rises fastest at first.
+      if (j == 0 || j == 1 || j == 3 || j == 7 || j == 11)
+        wbar = fmaxf(wbar, topp ? wave_8th_floor_uniform(kb[0]) : wave_max_uniform(kb[0]));
     }
     if (!topp) {
       float k1 = kb[0];
