@@ -1115,12 +1115,40 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       floor_key += prefix;
     }
   }
-#pragma unroll 4
-  for (int g = tid; g < total; g += BT) {
-    const unsigned long long x = cand_at(g);
-    if (cand_key(x) >= floor_key) {
-      const int slot = atomicAdd(&sh.nlist, 1);
-      if (slot < kListMax) sh.list[slot] = x;
+  {
+    // Thread t takes g = t, t + BT, ... four at a time (four loads in
+    // flight); its chunk index only moves forward, so it walks the chunk
+    // offsets instead of searching them.  Slots come one atomic per wave:
+    // the wave's count from a ballot, each lane's offset from mbcnt.  The
+    // list's order is immaterial (every later step sorts, selects or takes a
+    // maximum with id tie-breaks).
+    const int lane_id = tid & (kWave - 1);
+    int c = 0;
+    for (int g0 = tid; g0 < total; g0 += 4 * BT) {
+      unsigned long long x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = g0 + u * BT;
+        x[u] = 0ull;
+        if (g < total) {
+          while (sh.pos[c + 1] <= g) ++c;
+          x[u] = cand[static_cast<size_t>(c) * lay.cc + (g - sh.pos[c])];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool keep = g0 + u * BT < total && cand_key(x[u]) >= floor_key;
+        const unsigned long long bal = __ballot(keep);
+        if (bal == 0ull) continue;
+        // lane 0 holds the wave's smallest g, so it is active whenever any lane is
+        int base = 0;
+        if (lane_id == 0) base = atomicAdd(&sh.nlist, __popcll(bal));
+        base = __builtin_amdgcn_readfirstlane(base);
+        const int slot = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                    static_cast<uint32_t>(bal >> 32),
+                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
+        if (keep && slot < kListMax) sh.list[slot] = x[u];
+      }
     }
   }
   __syncthreads();
