@@ -156,17 +156,31 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// A value that at least eight lanes of the wave reach or exceed: the
-// smallest of the eight 8-lane group maxima (half rows), returned uniform.
-// It is at most the wave's eighth-largest value.  Every lane must be active.
-__device__ __forceinline__ float wave_8th_floor_uniform(float v) {
+// The eight 8-lane group maxima of v, two order statistics of them, both
+// uniform: the return value is the smallest (eight lanes, one per group,
+// reach it) and `second` the second largest (two lanes of different groups
+// reach it).  The largest and second largest travel as a pair, combined over
+// disjoint groups only: lanes of rows outside a broadcast's row mask take
+// (-inf, -inf), the pair's identity.  Every lane must be active.
+__device__ __forceinline__ float wave_group_floors(float v, float& second) {
   v = fmaxf(v, dpp_f32<0xB1, 0xF>(v, v));   // quad_perm [1,0,3,2]
   v = fmaxf(v, dpp_f32<0x4E, 0xF>(v, v));   // quad_perm [2,3,0,1]
   v = fmaxf(v, dpp_f32<0x141, 0xF>(v, v));  // row_half_mirror: 8-lane group maximum
-  v = fminf(v, dpp_f32<0x128, 0xF>(v, v));  // row_ror:8: smaller of the row's two groups
-  v = fminf(v, dpp_f32<0x142, 0xA>(v, v));  // row_bcast:15 into rows 1 and 3
-  v = fminf(v, dpp_f32<0x143, 0xC>(v, v));  // row_bcast:31 into rows 2 and 3
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  const float o = dpp_f32<0x128, 0xF>(v, v);  // row_ror:8: the row's other group
+  float lo = fminf(v, o), hi = fmaxf(v, o), nd = lo;
+  {
+    lo = fminf(lo, dpp_f32<0x142, 0xA>(lo, lo));  // row_bcast:15 into rows 1 and 3
+    const float h2 = dpp_f32<0x142, 0xA>(-INFINITY, hi), n2 = dpp_f32<0x142, 0xA>(-INFINITY, nd);
+    nd = fmaxf(fminf(hi, h2), fmaxf(nd, n2));
+    hi = fmaxf(hi, h2);
+  }
+  {
+    lo = fminf(lo, dpp_f32<0x143, 0xC>(lo, lo));  // row_bcast:31 into rows 2 and 3
+    const float h2 = dpp_f32<0x143, 0xC>(-INFINITY, hi), n2 = dpp_f32<0x143, 0xC>(-INFINITY, nd);
+    nd = fmaxf(fminf(hi, h2), fmaxf(nd, n2));
+  }
+  second = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(nd), 63));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lo), 63));
 }
 
 __device__ __forceinline__ void wave_best(float& k, int& i) {

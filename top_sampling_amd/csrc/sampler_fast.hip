@@ -115,6 +115,7 @@ struct ChunkSmem {
   int klist[kKeyCap];
   float wthr[AW];
   float wbar[AW];
+  float wsec[AW];  // posted second-largest group maxima (top-p key bars)
   float rm[AW], rs[AW], rt[AW];
   int rb[AW];
   float rf[AW];
@@ -291,8 +292,9 @@ __device__ __forceinline__ void insert3(float key, int id, float (&k)[3], int (&
 // the chunk pass from the logits in its registers, relative to the chunk
 // maximum: x = (l - cmax) / T, key = x + g.  Full rows list the chunk's best
 // key (floor: that key); top-p-only rows list every key at or above the
-// floor.  Every thread of the workgroup calls it, with sh.nkey zero.  Returns
-// the number of keys (above kKeyCap: overflow, the list is not written).
+// floor.  Every thread of the workgroup calls it, with sh.nkey zero and
+// sh.wsec all -inf.  Returns the number of keys (above kKeyCap: overflow, the
+// list is not written).
 __device__ __forceinline__ int chunk_keys(const float4 (&v)[AV], float cmax, float inv_t, bool topp,
                                           uint64_t seed, uint64_t grow, int c0,
                                           int* __restrict__ klist_out, ChunkSmem& sh,
@@ -306,15 +308,18 @@ __device__ __forceinline__ int chunk_keys(const float4 (&v)[AV], float cmax, flo
     // must clear is the larger of the thread's own (its best, or its third
     // best) and the wave's, refreshed after five of the sixteen float4s: for
     // full rows the wave's largest best key (a token under it cannot be the
-    // chunk's best), for top-p rows a value eight of the wave's best keys
-    // reach (the smallest of the eight 8-lane group maxima).  The top-p key
-    // floor below is raised to every wave's bar, so a token skipped under a
-    // bar is under the floor and the key list above the floor stays
-    // complete; whole waves skip the Gumbel draw once a few good keys are
-    // known.
+    // chunk's best); for top-p rows a value eight keys of the chunk reach,
+    // the larger of two: the smallest of the wave's eight 8-lane group
+    // maxima of the best keys, and the smallest of the second-largest group
+    // maxima the four waves have posted in LDS (two keys per wave; a stale
+    // or missing post is lower, so it still holds).  The top-p key floor
+    // below is raised to every wave's bar, so a token skipped under a bar is
+    // under the floor and the key list above the floor stays complete; whole
+    // waves skip the Gumbel draw once a few good keys are known.
     float kb[3] = {-INFINITY, -INFINITY, -INFINITY};
     int ib[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
     float wbar = topp ? -INFINITY : kMinGumbel;
+    volatile float* posted = sh.wsec;
 #pragma unroll
     for (int j = 0; j < AV; ++j) {
       const int e = 4 * (j * AT + tid);
@@ -340,8 +345,19 @@ __device__ __forceinline__ int chunk_keys(const float4 (&v)[AV], float cmax, flo
         }
       }
       // Refreshed early and then less often: the bar rises fastest at first.
-      if (j == 0 || j == 1 || j == 3 || j == 7 || j == 11)
-        wbar = fmaxf(wbar, topp ? wave_8th_floor_uniform(kb[0]) : wave_max_uniform(kb[0]));
+      if (j == 0 || j == 1 || j == 3 || j == 7 || j == 11) {
+        if (topp) {
+          float second;
+          const float own = wave_group_floors(kb[0], second);
+          if (lane_id == 0) posted[wave] = second;
+          float b = posted[0];
+#pragma unroll
+          for (int w = 1; w < AW; ++w) b = fminf(b, posted[w]);
+          wbar = fmaxf(wbar, fmaxf(own, uniform_f32(b)));
+        } else {
+          wbar = fmaxf(wbar, wave_max_uniform(kb[0]));
+        }
+      }
     }
     if (!topp) {
       float k1 = kb[0];
@@ -496,6 +512,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     sh.ncand = 0;
     sh.nkey = 0;
   }
+  if (tid < AW) sh.wsec[tid] = -INFINITY;
   // Logit candidate threshold tf: at least M logits of the chunk are >= tf.
   // M <= 64: every wave holds ceil(M/4) per-thread maxima >= its own q-th
   // largest, so the smallest of the four wave values works.  64 < M <= 256:
