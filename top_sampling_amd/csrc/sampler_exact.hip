@@ -87,14 +87,25 @@ __device__ __forceinline__ void select_digit_mass(FallbackSmem& sh, int nb, unsi
 }
 
 // Calls f(i, l) for the logits of row r, each thread taking every XT-th
-// column of each slice.
+// column of each slice, in increasing column order.  The loads run kRowLoads
+// columns ahead of the calls (one wave's load covers 64 consecutive columns),
+// so a pass over a row is not one memory round trip per column step.
+constexpr int kRowLoads = 16;
 template <typename F>
 __device__ __forceinline__ void for_row(const LogitsView& lv, int r, F&& f) {
   for (int s = 0; s < lv.n; ++s) {
     const float* __restrict__ src = lv.ptr[s] + static_cast<int64_t>(r) * lv.ld[s];
     const int base = static_cast<int>(lv.off[s]);
     const int cols = static_cast<int>(lv.off[s + 1] - lv.off[s]);
-    for (int j = threadIdx.x; j < cols; j += XT) f(base + j, src[j]);
+    int j = threadIdx.x;
+    for (; j + (kRowLoads - 1) * XT < cols; j += kRowLoads * XT) {
+      float x[kRowLoads];
+#pragma unroll
+      for (int u = 0; u < kRowLoads; ++u) x[u] = src[j + u * XT];
+#pragma unroll
+      for (int u = 0; u < kRowLoads; ++u) f(base + j + u * XT, x[u]);
+    }
+    for (; j < cols; j += XT) f(base + j, src[j]);
   }
 }
 
@@ -242,27 +253,40 @@ __device__ __forceinline__ void exact_row(const SamplerArgs& a, int r, FallbackS
     const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
     float gk = -INFINITY;
     int gi = 0x7fffffff;
+    // Thread t takes the groups q = t, t + XT, ..., the logits of four
+    // groups loaded before any is used.
     const int nq = (V + 3) >> 2;
-    for (int q = tid; q < nq; q += XT) {
-      float l4[4];
-      bool in[4];
-      bool any = false;
+    constexpr int QG = 4;
+    for (int q0 = tid; q0 < nq; q0 += QG * XT) {
+      float l4[QG][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int v = 4 * q + j;
-        l4[j] = v < V ? logit_at(lv, r, v) : -INFINITY;
-        in[j] = v < V && order_key(l4[j]) >= thr;
-        any |= in[j];
+      for (int u = 0; u < QG; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int v = 4 * (q0 + u * XT) + j;
+          l4[u][j] = v < V ? logit_at(lv, r, v) : -INFINITY;
+        }
       }
-      if (!any) continue;
-      const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(q));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (!in[j]) continue;
-        const float key = (l4[j] - m) * inv_t + gumbel_from_word(w.v[j]);
-        if (better(key, 4 * q + j, gk, gi)) {
-          gk = key;
-          gi = 4 * q + j;
+      for (int u = 0; u < QG; ++u) {
+        const int q = q0 + u * XT;
+        bool in[4];
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          in[j] = 4 * q + j < V && order_key(l4[u][j]) >= thr;
+          any |= in[j];
+        }
+        if (!any) continue;
+        const U32x4 w = token_words(p.seed, grow, static_cast<uint32_t>(q));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!in[j]) continue;
+          const float key = (l4[u][j] - m) * inv_t + gumbel_from_word(w.v[j]);
+          if (better(key, 4 * q + j, gk, gi)) {
+            gk = key;
+            gi = 4 * q + j;
+          }
         }
       }
     }
