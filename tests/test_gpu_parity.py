@@ -376,6 +376,46 @@ def test_sampler_large_targets(dev, ts, layout, route):
              res.row_status, res.flagged, lse, logits, max_frac=1.0, label=layout)
 
 
+def test_sampler_topk_beyond_fast_route(dev, ts, route):
+    """top_k between 1,024 and V: the fast route hands these rows to the
+    exact per-row kernel (with and without top-p, with top-N)."""
+    rng = np.random.default_rng(21)
+    rows, V, max_lp = 10, 20000, 20
+    logits = (rng.standard_normal((rows, V)) * 1.5).astype(np.float32)
+    params = workloads.random_params(rng, rows, V, max_lp, greedy_frac=0.0)
+    params["top_k"] = np.array([1025, 1500, 2048, 5000, 19999, 1025, 3000, 1100, 8191, 1024],
+                               dtype=np.int32)
+    params["top_p"] = np.array([1.0, 0.9, 1.0, 0.7, 0.95, 0.5, 1.0, 0.8, 0.99, 0.9],
+                               dtype=np.float32)
+    say("sampler top_k beyond the fast route", route)
+    got = _run_sampler(ts, dev, logits, params, 2, max_lp)
+    res, lse = _oracle_ref(logits, params, 2, max_lp)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label="topk>1024")
+
+
+def test_sampler_probes_outside_nucleus(dev, ts, route):
+    """Top-p-only rows whose nucleus (about 120 of 200 raised logits) is past
+    the listed head but holds only a tenth of the mass: the best Gumbel keys
+    mostly fall outside it, so many rows keep none of their probes and go to
+    the exact kernel; every row must still match the oracle."""
+    rng = np.random.default_rng(22)
+    rows, V, max_lp = 16, 20000, 5
+    logits = (rng.standard_normal((rows, V)) * 0.1).astype(np.float32)
+    for r in range(rows):
+        hot = rng.choice(V, size=200, replace=False)
+        logits[r, hot] += 3.0
+    params = workloads.random_params(rng, rows, V, max_lp, greedy_frac=0.0)
+    params["temperature"][:] = 1.0
+    params["top_k"][:] = 0
+    params["top_p"][:] = 0.1
+    say("sampler probes outside the nucleus", route)
+    got = _run_sampler(ts, dev, logits, params, 9, max_lp)
+    res, lse = _oracle_ref(logits, params, 9, max_lp)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, max_frac=1.0, label="probe-fallback")
+
+
 def test_sampler_bad_rows(dev, ts, route):
     rng = np.random.default_rng(0)
     rows, V = 12, 500
