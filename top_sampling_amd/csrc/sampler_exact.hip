@@ -152,7 +152,7 @@ __device__ __forceinline__ uint32_t radix_mass(const LogitsView& lv, int r, uint
     for_row(lv, r, [&](int, float l) {
       const uint32_t key = order_key(l);
       if (key >= floor_key && (key & pmask) == prefix)
-        atomicAdd(&sh.ex.mass[(key >> shift) & dmask], fixed_mass(expf((l - m) * inv_t)));
+        atomicAdd(&sh.ex.mass[(key >> shift) & dmask], fixed_mass(fast_exp((l - m) * inv_t)));
     });
     __syncthreads();
     select_digit_mass(sh, 1 << width, rem);
@@ -191,16 +191,25 @@ __device__ __forceinline__ void exact_row(const SamplerArgs& a, int r, FallbackS
     return;
   }
 
-  // Pass 1: maximum key with its lowest id; screen NaN and +inf.
+  // Pass 1: maximum key with its lowest id; screen NaN and +inf; and each
+  // thread's sum of exp(l - its running maximum), rescaled as that maximum
+  // grows (fixed per-thread order, fixed tree), for the log-sum-exp.
   uint32_t bk = 0u;
   int bi = 0x7fffffff;
   int bad = 0;
+  float mt = -INFINITY, st = 0.0f;
   for_row(lv, r, [&](int i, float l) {
     bad |= (isnan(l) || (isinf(l) && l > 0.0f)) ? 1 : 0;
     const uint32_t key = order_key(l);
     if (better_u(key, i, bk, bi)) {
       bk = key;
       bi = i;
+    }
+    if (l > mt) {
+      st = st * fast_exp(mt - l) + 1.0f;
+      mt = l;
+    } else if (l > -INFINITY) {
+      st += fast_exp(l - mt);
     }
   });
   bad = block_sum<XT, int>(bad, sh.ri);
@@ -211,11 +220,7 @@ __device__ __forceinline__ void exact_row(const SamplerArgs& a, int r, FallbackS
     return;
   }
   const int argmax_id = bi;
-
-  // Pass 2: log-sum-exp of the raw logits (fixed per-thread order, fixed tree).
-  float s = 0.0f;
-  for_row(lv, r, [&](int, float l) { s += expf(l - m); });
-  s = block_sum<XT, float>(s, sh.rf_);
+  const float s = block_sum<XT, float>(mt > -INFINITY ? st * fast_exp(mt - m) : 0.0f, sh.rf_);
   const float lse = m + logf(s);
 
   // The sampled token first: the processed log-probabilities need the kept
@@ -239,7 +244,7 @@ __device__ __forceinline__ void exact_row(const SamplerArgs& a, int r, FallbackS
     if (p.top_p < 1.0f) {
       unsigned long long z = 0ull;
       for_row(lv, r, [&](int, float l) {
-        if (order_key(l) >= kk) z += fixed_mass(expf((l - m) * inv_t));
+        if (order_key(l) >= kk) z += fixed_mass(fast_exp((l - m) * inv_t));
       });
       z = block_sum<XT, unsigned long long>(z, sh.rq);
       const double tgt = ceil(static_cast<double>(p.top_p) * static_cast<double>(z));
@@ -300,7 +305,7 @@ __device__ __forceinline__ void exact_row(const SamplerArgs& a, int r, FallbackS
   if (proc && !greedy) {
     float z = 0.0f;
     for_row(lv, r, [&](int, float l) {
-      if (order_key(l) >= thr) z += expf((l - m) * inv_t);
+      if (order_key(l) >= thr) z += fast_exp((l - m) * inv_t);
     });
     lzk = logf(block_sum<XT, float>(z, sh.rf_));
   }
