@@ -358,8 +358,10 @@ hipError_t launch_cfg(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t
 
 // Tile shapes (rows x vocab per workgroup, waves): the default picks the
 // shape that pads the row count least; TS_GEMM_TILE=<n> forces shape n (the
-// tests run every shape).  1: 64x256/4 waves and 2: 128x256/8 waves stream
-// the lm_head past the caches (one row tile reads it once); 3: 256x256/8;
+// tests run every shape).  1: 64x128/4 waves and 2: 128x128/8 waves stream
+// the lm_head past the caches (one row tile reads it once; 128-wide strips
+// give twice the workgroups of 256-wide ones, so the last round over the
+// CUs is not left a third full at a 151,936-row lm_head); 3: 256x256/8;
 // 4: 320x256/8; 5: the register-staged kernel (also used when the hidden size
 // is not a multiple of 64).
 hipError_t launch_lmhead_gemm(const uint16_t* hidden, int64_t ld_hidden, const uint16_t* lm_head,
@@ -375,10 +377,10 @@ hipError_t launch_lmhead_gemm(const uint16_t* hidden, int64_t ld_hidden, const u
   }
   switch (sel) {
     case 1:
-      return launch_dl<64, 256, 1, 4, 1>(hidden, ld_hidden, lm_head, ld_lm_head, logits, ld_logits,
+      return launch_dl<64, 128, 1, 4, 1>(hidden, ld_hidden, lm_head, ld_lm_head, logits, ld_logits,
                                          rows, vocab, hidden_dim, stream);
     case 2:
-      return launch_dl<128, 256, 2, 4, 1>(hidden, ld_hidden, lm_head, ld_lm_head, logits, ld_logits,
+      return launch_dl<128, 128, 2, 4, 1>(hidden, ld_hidden, lm_head, ld_lm_head, logits, ld_logits,
                                           rows, vocab, hidden_dim, stream);
     case 3:
       return launch_dl<256, 256, 2, 4, 0>(hidden, ld_hidden, lm_head, ld_lm_head, logits, ld_logits,
