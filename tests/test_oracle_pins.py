@@ -61,6 +61,122 @@ def test_rng_rows_and_seeds_independent():
     assert len(set(a[:4].tolist())) == 4
 
 
+# RNG word layout (the contract of the sampler's noise): key = (seed low 32
+# bits, seed high 32 bits), counter = (v >> 2, row low 32 bits, row high 32
+# bits, 0), token v takes output word v & 3.  Each entry below spells the key
+# and counter words out by hand (hex), so a swapped key half, a swapped row
+# half, a counter word in the wrong slot or a wrong word index all change some
+# expected word.  Seeds and rows set both 32-bit halves; v covers all four
+# word slots and the counter's high bits.
+#   (seed, global row, token v, key0, key1, ctr1, ctr2)
+RNG_TABLE = [
+    (0x0000000000000000, 0x0000000000000000, 0, 0x00000000, 0x00000000, 0x00000000, 0x00000000),
+    (0x0000000000000000, 0x0000000000000000, 3, 0x00000000, 0x00000000, 0x00000000, 0x00000000),
+    (0x0123456789ABCDEF, 0x0000000500000007, 13, 0x89ABCDEF, 0x01234567, 0x00000007, 0x00000005),
+    (0x0123456789ABCDEF, 0x0000000500000007, 14, 0x89ABCDEF, 0x01234567, 0x00000007, 0x00000005),
+    (0x0123456789ABCDEF, 0x0000000700000005, 13, 0x89ABCDEF, 0x01234567, 0x00000005, 0x00000007),
+    (0x89ABCDEF01234567, 0x0000000500000007, 13, 0x01234567, 0x89ABCDEF, 0x00000007, 0x00000005),
+    (0xFFFFFFFF00000001, 0x0000000100000000, 151935, 0x00000001, 0xFFFFFFFF, 0x00000000, 0x00000001),
+    (0x00000001FFFFFFFF, 0x00000000FFFFFFFF, 151932, 0xFFFFFFFF, 0x00000001, 0xFFFFFFFF, 0x00000000),
+    (0x9E3779B97F4A7C15, 0x0000000200000280, 262143, 0x7F4A7C15, 0x9E3779B9, 0x00000280, 0x00000002),
+    (0x9E3779B97F4A7C15, 0x0000000200000280, 1, 0x7F4A7C15, 0x9E3779B9, 0x00000280, 0x00000002),
+    (0x00000000DEADBEEF, 0x000000000000027F, 2147483646, 0xDEADBEEF, 0x00000000, 0x0000027F, 0x00000000),
+    (0xCAFEF00D00000000, 0xFFFFFFFFFFFFFFFF, 7, 0x00000000, 0xCAFEF00D, 0xFFFFFFFF, 0xFFFFFFFF),
+    (0x0000000000000001, 0x0000000000000001, 4, 0x00000001, 0x00000000, 0x00000001, 0x00000000),
+    (0x0000000000000001, 0x0000000000000001, 5, 0x00000001, 0x00000000, 0x00000001, 0x00000000),
+]
+
+
+def _table_word(entry):
+    """The expected word of one table entry: the known-answer-pinned Philox
+    on the hand-written counter and key, output word v & 3."""
+    _, _, v, key0, key1, ctr1, ctr2 = entry
+    out = oracle.philox4x32_10(np.array([v >> 2]), np.array([ctr1]), np.array([ctr2]),
+                               np.array([0]), key0, key1)
+    return int(out[v & 3][0])
+
+
+def test_rng_word_table_layout():
+    slots = set()
+    for entry in RNG_TABLE:
+        seed, row, v, key0, key1, ctr1, ctr2 = entry
+        # the hand-split words are the halves of seed and row
+        assert (key1 << 32) | key0 == seed and (ctr2 << 32) | ctr1 == row, entry
+        got = int(oracle.random_words(seed, row, np.array([v]))[0])
+        assert got == _table_word(entry), entry
+        slots.add(v & 3)
+    assert slots == {0, 1, 2, 3}
+
+
+def test_rng_word_table_discriminates_layouts():
+    """The table is sensitive to the layout: the words a mis-wired generator
+    would produce (key halves swapped, row halves swapped, word slot
+    reversed) differ from the table on some entry."""
+    def wrong(entry, how):
+        seed, row, v, key0, key1, ctr1, ctr2 = entry
+        if how == "key":
+            key0, key1 = key1, key0
+        elif how == "row":
+            ctr1, ctr2 = ctr2, ctr1
+        out = oracle.philox4x32_10(np.array([v >> 2]), np.array([ctr1]), np.array([ctr2]),
+                                   np.array([0]), key0, key1)
+        return int(out[(3 - (v & 3)) if how == "slot" else (v & 3)][0])
+    for how in ("key", "row", "slot"):
+        assert any(wrong(e, how) != _table_word(e) for e in RNG_TABLE), how
+
+
+def test_uniform_endpoints_and_grid():
+    """u = ((x >> 9) + 1/2) * 2^-23: the nine low bits are dropped, the
+    smallest word gives 2^-24 and the largest 1 - 2^-24 (both exact)."""
+    x = np.array([0, 0x1FF, 0x200, 0x3FF, 0x80000000, 0xFFFFFE00, 0xFFFFFFFF], dtype=np.uint64)
+    u = oracle.uniform_from_words(x)
+    assert u[0] == 2.0 ** -24 and u[1] == 2.0 ** -24
+    assert u[2] == 3 * 2.0 ** -24 and u[3] == 3 * 2.0 ** -24
+    assert u[4] == 0.5 + 2.0 ** -24
+    assert u[5] == 1.0 - 2.0 ** -24 and u[6] == 1.0 - 2.0 ** -24
+    # the Gumbel range these give
+    g = -np.log(-np.log(u[[0, 6]]))
+    assert abs(g[0] - (-math.log(24 * math.log(2)))) < 1e-12
+    assert 16.63 < g[1] < 16.64
+
+
+def _two_token_row_with_key_gap(gap, t=1.0, seed=0x5EED, row=3):
+    """Logits of a two-token row whose Gumbel keys (l - m)/T + g differ by
+    `gap` (token 0 ahead), from the noise written out by hand: g = -ln(-ln u)
+    with u from the table-pinned word layout."""
+    words = [_table_word((seed, row, v, seed & 0xFFFFFFFF, seed >> 32, row & 0xFFFFFFFF,
+                          row >> 32)) for v in (0, 1)]
+    u = [((w >> 9) + 0.5) * 2.0 ** -23 for w in words]
+    g = [-math.log(-math.log(x)) for x in u]
+    l1 = 0.0
+    l0 = t * (gap + g[1] - g[0]) + l1
+    return np.array([l0, l1], dtype=np.float64), t, seed, row
+
+
+@pytest.mark.parametrize("scale,flag", [(0.5, True), (2.0, False), (-0.5, True), (-2.0, False)])
+def test_tie_flag_window(scale, flag):
+    """flag_tie marks a row exactly when its two best Gumbel keys lie closer
+    than KEY_TIE_WINDOW: half the window apart is flagged, twice the window
+    apart is not, whichever token leads."""
+    gap = scale * oracle.KEY_TIE_WINDOW
+    l, t, seed, row = _two_token_row_with_key_gap(gap)
+    r = oracle.sample_row(l, t, 0, 1.0, 0, seed, row, 0)
+    assert r.flag_tie == flag
+    assert r.token == (0 if gap > 0 else 1)
+    assert not r.flag_top_p
+
+
+def test_tie_flag_needs_two_kept_tokens():
+    """With top-k = 1 (greedy) or a one-token kept set there is no second key
+    and no flag, however close the two keys are."""
+    l, t, seed, row = _two_token_row_with_key_gap(0.1 * oracle.KEY_TIE_WINDOW)
+    assert not oracle.sample_row(l, t, 1, 1.0, 0, seed, row, 0).flag_tie
+    assert oracle.sample_row(l, t, 0, 1.0, 0, seed, row, 0).flag_tie
+    # top-p keeping only the larger logit: one kept token, no flag
+    big = np.array([8.0, 0.0])
+    assert not oracle.sample_row(big, 1.0, 0, 0.5, 0, seed, row, 0).flag_tie
+
+
 # ----------------------------------------------------------------- projection
 def _bf16_fraction(bits: int) -> Fraction:
     """Exact value of a bf16 bit pattern, from the IEEE binary32 layout."""
