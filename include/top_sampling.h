@@ -25,9 +25,19 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued asynchronously on it.
  *   - A nonzero return value means argument validation failed and NOTHING was
- *     enqueued (invalid configurations are rejected up front rather than
- *     degraded silently).  ts_last_error() then describes the failure for
+ *     enqueued: invalid configurations are rejected up front rather than
+ *     degraded silently.  This follows the fail-fast convention of the
+ *     sequence-parallel patch described on the page "Qwen 4 leak: SGLang
+ *     shards the Qwen4Exp prefill" (orcarouter.ai blog, ja edition), section
+ *     "The cost to you: constraints": unsupported configurations fail during
+ *     argument validation.  ts_last_error() then describes the failure for
  *     the calling thread.  TS_EHIP reports a failed kernel launch.
+ *   - The preconditions batch-sharded sampling states (page "Qwen4Exp
+ *     batch-sharded sampling: inside vLLM PR #61018", section "What
+ *     batch-sharded sampling is, in one paragraph") include a non-negative
+ *     max_logprobs: max_logprobs < 0 is TS_EINVAL in every sampler call.
+ *   - Measurement and check aids that are not steps of the path (clock
+ *     probe, noise readout) are declared in top_sampling_measure.h.
  *   - Sizes of zero are valid no-ops.
  *   - Matrices are row-major with an explicit leading dimension (elements).
  */
@@ -158,7 +168,15 @@ int lmhead_logits_local_e4m3(const void* hidden, const float* hidden_scales, int
 
 /*
  * sampler_workspace_bytes: device workspace sampler_sample needs for these
- * sizes (host-only computation; callable without a GPU).
+ * sizes (host-only computation; callable without a GPU).  The caller owns
+ * the workspace, as every other buffer: serving replays fixed graph buckets
+ * (page "Qwen 4 leak: SGLang shards the Qwen4Exp prefill", section "The
+ * layout bug they had to fix first": fixed physical CUDA-graph buckets), so
+ * the library allocates nothing per call and the caller sizes each bucket's
+ * workspace once from this query.  Returns 0 for negative sizes or
+ * max_logprobs < 0 (the non-negative max_logprobs precondition of page
+ * "Qwen4Exp batch-sharded sampling: inside vLLM PR #61018", section "What
+ * batch-sharded sampling is, in one paragraph").
  */
 size_t sampler_workspace_bytes(int64_t rows, int64_t vocab, int32_t max_logprobs);
 
@@ -261,33 +279,15 @@ int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* sli
                                   float* out, int64_t ld_out, void* stream);
 
 /*
- * ts_mfma_clock_probe: a measurement aid, not a step of the path.  Every
- * workgroup (eight waves, two per SIMD) runs `iters` rounds of four
- * independent bf16 32x32x16 matrix-core accumulations per wave and records
- * the shader-clock counter and the constant 100 MHz real-time counter before
- * the first round and after the last:
- *   ticks       DEVICE uint64 [workgroups, 4]: clock start, clock end,
- *               real-time start, real-time end (caller-owned)
- *   workgroups  1 .. 65536 (one or more per compute unit loads every unit)
- *   iters       1 .. 2^24
- *   operands    TS_PROBE_SMALL_OPERANDS (a few small values: little bit
- *               switching) or TS_PROBE_RANDOM_OPERANDS (random bit patterns
- *               per lane, finite): the sustained rate depends on the data
- * The shader clock under this load is (clock end - clock start) /
- * (real-time end - real-time start) x 100 MHz; the matrix-core rate is
- * workgroups x 8 x iters x 4 x 32768 flop over the launch's duration.
- * TS_EINVAL for a NULL ticks, a misaligned ticks, a size out of range or an
- * unknown operands value.
+ * ts_status_string: name of a TS_* return code (a static string; unknown
+ * codes give "TS_UNKNOWN").  ts_last_error: a description of the calling
+ * thread's last nonzero return (a per-thread static buffer, overwritten by
+ * that thread's next failure).  Both serve the fail-fast convention above:
+ * a rejected configuration says why it was rejected (page "Qwen 4 leak:
+ * SGLang shards the Qwen4Exp prefill", section "The cost to you:
+ * constraints").  Host-only; callable without a GPU.
  */
-#define TS_PROBE_SMALL_OPERANDS 0
-#define TS_PROBE_RANDOM_OPERANDS 1
-int ts_mfma_clock_probe(uint64_t* ticks, int32_t workgroups, int64_t iters, int32_t operands,
-                        void* stream);
-
-/* Name of a TS_* return code (static string). */
 const char* ts_status_string(int status);
-
-/* Detail of the calling thread's last nonzero return (static per thread). */
 const char* ts_last_error(void);
 
 #ifdef __cplusplus

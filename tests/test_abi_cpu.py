@@ -13,26 +13,32 @@ import workloads
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "top_sampling.h")
+MEASURE_HEADER = os.path.join(ROOT, "include", "top_sampling_measure.h")
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(path):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M))
 
 
 def test_header_symbols_exported():
-    names = _declared_functions()
+    product = _declared_functions(HEADER)
+    measure = _declared_functions(MEASURE_HEADER)
+    names = product | measure
     assert names == set(ts.SYMBOLS), names
+    # the measurement aids are not part of the product header
+    assert measure == {"ts_mfma_clock_probe", "ts_gumbel_keys"}
+    assert not (product & measure)
     lib = ctypes.CDLL(ts.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_header_constants_match_binding():
-    text = open(HEADER).read()
+    text = open(HEADER).read() + open(MEASURE_HEADER).read()
     for name, val in [("TS_MAX_LOGPROBS", ts.TS_MAX_LOGPROBS), ("TS_MAX_SLICES", ts.TS_MAX_SLICES),
                       ("TS_LOGPROBS_PROCESSED", ts.TS_LOGPROBS_PROCESSED),
                       ("TS_PROBE_SMALL_OPERANDS", ts.TS_PROBE_SMALL_OPERANDS),
@@ -288,3 +294,20 @@ def test_mfma_clock_probe_validation():
     assert probe(FAKE, 4, 0, rnd, None) == ts.TS_EINVAL
     assert probe(FAKE, 4, (1 << 24) + 1, rnd, None) == ts.TS_EINVAL
     assert probe(FAKE, 4, 16, 2, None) == ts.TS_EINVAL              # unknown operand mode
+
+
+def test_gumbel_keys_validation():
+    gk = ts.lib.ts_gumbel_keys
+    args = [FAKE] * 6
+    assert gk(*args, 0, None, None, None) == ts.TS_OK                 # empty: no-op
+    assert gk(*args, -1, FAKE, FAKE, None) == ts.TS_EINVAL
+    assert gk(*args, 1 << 31, FAKE, FAKE, None) == ts.TS_EINVAL
+    for i in range(6):
+        bad = list(args)
+        bad[i] = None
+        assert gk(*bad, 4, FAKE, FAKE, None) == ts.TS_EINVAL, i
+    bad = list(args)
+    bad[3] = FAKE + 4                                                  # seeds need 8 bytes
+    assert gk(*bad, 4, FAKE, FAKE, None) == ts.TS_EINVAL
+    assert gk(*args, 4, FAKE + 2, FAKE, None) == ts.TS_EINVAL          # keys misaligned
+    assert b"misaligned" in ts.lib.ts_last_error()

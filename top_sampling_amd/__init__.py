@@ -40,7 +40,8 @@ TS_LOGPROBS_PROCESSED = 1
 TS_PROBE_SMALL_OPERANDS, TS_PROBE_RANDOM_OPERANDS = 0, 1
 PARAMS_BYTES = 24
 
-# (name, restype, argtypes) of every symbol the header declares.
+# (name, restype, argtypes) of every symbol the headers declare
+# (include/top_sampling.h and the measurement aids of top_sampling_measure.h).
 _VP, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 SYMBOLS = {
     "lmhead_logits_local": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _I64, _VP, _I64, _VP]),
@@ -57,6 +58,7 @@ SYMBOLS = {
                                          _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sampler_assemble_vocab_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _VP]),
     "ts_mfma_clock_probe": (ctypes.c_int, [_VP, _I32, _I64, _I32, _VP]),
+    "ts_gumbel_keys": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP]),
     "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "ts_last_error": (ctypes.c_char_p, []),
 }
@@ -327,3 +329,18 @@ def mfma_clock_probe(workgroups: int, iters: int, device, stream=None, random: b
     mode = TS_PROBE_RANDOM_OPERANDS if random else TS_PROBE_SMALL_OPERANDS
     _check(lib.ts_mfma_clock_probe(_ptr(ticks), workgroups, iters, mode, _stream_ptr(stream)))
     return ticks
+
+
+def gumbel_keys(logits, row_max, temperature, seeds, rows, ids, stream=None):
+    """The sampler's own fp32 Gumbel-max keys and Philox noise words for listed
+    tokens (a check aid): all arguments are 1-D device tensors of one length
+    (fp32 logits / row_max / temperature, int64 seeds (uint64 bits) and rows,
+    int32 ids).  Returns (keys fp32, words int32 holding the uint32 bits)."""
+    torch = _torch()
+    n = int(ids.numel())
+    keys = torch.empty(n, dtype=torch.float32, device=ids.device)
+    words = torch.empty(n, dtype=torch.int32, device=ids.device)
+    _check(lib.ts_gumbel_keys(_ptr(logits), _ptr(row_max), _ptr(temperature), _ptr(seeds),
+                              _ptr(rows), _ptr(ids), n, _ptr(keys), _ptr(words),
+                              _stream_ptr(stream)))
+    return keys, words

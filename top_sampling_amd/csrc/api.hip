@@ -64,6 +64,24 @@ int ts_mfma_clock_probe(uint64_t* ticks, int32_t workgroups, int64_t iters, int3
                     "ts_mfma_clock_probe");
 }
 
+int ts_gumbel_keys(const float* logits, const float* row_max, const float* temperature,
+                   const uint64_t* seeds, const int64_t* rows, const int32_t* ids, int64_t n,
+                   float* keys, uint32_t* words, void* stream) {
+  if (n < 0) return fail(TS_EINVAL, "n < 0");
+  if (n > kMaxDim) return fail(TS_EINVAL, "n above 2^31-1");
+  if (n == 0) return TS_OK;
+  if (!logits || !row_max || !temperature || !seeds || !rows || !ids)
+    return fail(TS_EINVAL, "NULL input");
+  if (!aligned(logits, 4) || !aligned(row_max, 4) || !aligned(temperature, 4) ||
+      !aligned(seeds, 8) || !aligned(rows, 8) || !aligned(ids, 4) || !aligned(keys, 4) ||
+      !aligned(words, 4))
+    return fail(TS_EINVAL, "misaligned pointer");
+  return hip_status(ts::launch_gumbel_keys(logits, row_max, temperature, seeds, rows, ids,
+                                           static_cast<int>(n), keys, words,
+                                           static_cast<hipStream_t>(stream)),
+                    "ts_gumbel_keys launch");
+}
+
 int lmhead_logits_local(const void* hidden, int64_t rows, int64_t hidden_dim, int64_t ld_hidden,
                         const void* lm_head, int64_t vocab_local, int64_t ld_lm_head,
                         float* logits, int64_t ld_logits, void* stream) {

@@ -46,12 +46,16 @@ __device__ __forceinline__ void store_tile_rows(const Acc (&acc)[TM][TN], float*
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      // In by columns (the accumulator layout), out by rows.  A wave's LDS
-      // operations complete in issue order, so the reads see these writes and
-      // the next block's writes cannot overtake them.
+      // In by columns (the accumulator layout), out by rows.  Lanes read
+      // what other lanes wrote, so each exchange is fenced at wavefront
+      // scope: after the writes (the reads below see them) and after the
+      // reads (the next block's writes cannot overtake them).
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         scr[(8 * (e >> 2) + 4 * fhalf + (e & 3)) * SP + frow] = acc[i][j][e];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int col = col0 + j * 32 + c0;
       f32x4v cs = {1.0f, 1.0f, 1.0f, 1.0f};
       if (SCALED) {
@@ -78,6 +82,9 @@ __device__ __forceinline__ void store_tile_rows(const Acc (&acc)[TM][TN], float*
             if (col + t < N) __builtin_nontemporal_store(v[t], dst + t);
         }
       }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
 }

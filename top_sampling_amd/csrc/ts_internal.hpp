@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/top_sampling.h"
+#include "../../include/top_sampling_measure.h"
 
 namespace ts {
 
@@ -78,5 +79,8 @@ hipError_t launch_assemble(const AssembleSlices& s, int64_t rows, float* out, in
 // ------------------------------------------------------------- measurement
 hipError_t launch_mfma_clock_probe(uint64_t* ticks, int workgroups, int64_t iters, int random,
                                    hipStream_t stream);
+hipError_t launch_gumbel_keys(const float* logits, const float* row_max, const float* temperature,
+                              const uint64_t* seeds, const int64_t* rows, const int32_t* ids,
+                              int n, float* keys, uint32_t* words, hipStream_t stream);
 
 }  // namespace ts
