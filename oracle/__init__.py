@@ -63,7 +63,7 @@ import numpy as np
 
 GREEDY_EPS = 1e-6          # R2: temperatures below this sample greedily
 TOP_P_FLAG_WINDOW = 1e-5   # top-p boundaries whose mass lies this close to p are ambiguous
-KEY_TIE_WINDOW = 1e-4      # rows whose two best Gumbel keys lie this close are flagged
+KEY_TIE_WINDOW = 1e-5      # rows whose two best Gumbel keys lie this close are flagged
 
 STATUS_OK = 0
 STATUS_BAD_PARAMS = 1

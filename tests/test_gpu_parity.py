@@ -2,9 +2,10 @@
 
 Bars: logits within 2e-3 absolute (fp32 MFMA accumulation vs float64);
 log-probabilities within 1e-4; token ids, top-N ids and row status bit-exact,
-except token ids on rows the oracle flags (top-p boundary mass within 1e-5 of
-p, or two best Gumbel keys within 1e-4), which must stay below 0.1% of rows;
-slice assembly bit-exact.
+except token ids on rows the oracle flags (the token depends on where within
+1e-5 of p the top-p boundary falls, or the two best Gumbel keys lie within
+1e-5), which must stay below 0.1% of each test's rows (so none in a test of
+fewer than 1,000 rows); slice assembly bit-exact.
 """
 import math
 import os
@@ -350,7 +351,7 @@ def test_sampler_edge_cases(dev, ts, V, kind, route):
     got = _run_sampler(ts, dev, logits, params, 5, max_lp, ld_extra=3)
     res, lse = _oracle_ref(logits, params, 5, max_lp)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=f"{V}/{kind}")
+             res.row_status, res.flagged, lse, logits, label=f"{V}/{kind}")
 
 
 @pytest.mark.parametrize("layout", ["crowded", "spread"])
@@ -373,7 +374,7 @@ def test_sampler_large_targets(dev, ts, layout, route):
     got = _run_sampler(ts, dev, logits, params, 3, max_lp)
     res, lse = _oracle_ref(logits, params, 3, max_lp)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=layout)
+             res.row_status, res.flagged, lse, logits, label=layout)
 
 
 def test_sampler_topk_beyond_fast_route(dev, ts, route):
@@ -391,7 +392,7 @@ def test_sampler_topk_beyond_fast_route(dev, ts, route):
     got = _run_sampler(ts, dev, logits, params, 2, max_lp)
     res, lse = _oracle_ref(logits, params, 2, max_lp)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label="topk>1024")
+             res.row_status, res.flagged, lse, logits, label="topk>1024")
 
 
 def test_sampler_probes_outside_nucleus(dev, ts, route):
@@ -413,7 +414,7 @@ def test_sampler_probes_outside_nucleus(dev, ts, route):
     got = _run_sampler(ts, dev, logits, params, 9, max_lp)
     res, lse = _oracle_ref(logits, params, 9, max_lp)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label="probe-fallback")
+             res.row_status, res.flagged, lse, logits, label="probe-fallback")
 
 
 def test_sampler_bad_rows(dev, ts, route):
@@ -437,7 +438,7 @@ def test_sampler_bad_rows(dev, ts, route):
     res, lse = _oracle_ref(logits, params, 0, 4)
     assert got["row_status"].tolist() == [0, 2, 2, 2, 1, 1, 1, 1, 1, 1, 1, 1]
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0)
+             res.row_status, res.flagged, lse, logits)
     assert np.all(np.isnan(got["topn_logprobs"][1:]))
 
 
@@ -453,7 +454,7 @@ def test_sampler_logprob_widths(dev, ts, max_lp, n, route):
     got = _run_sampler(ts, dev, logits, params, 0, max_lp)
     res, lse = _oracle_ref(logits, params, 0, max_lp)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0)
+             res.row_status, res.flagged, lse, logits)
 
 
 def test_sampler_long_topk_tie_runs(dev, ts, route):
@@ -477,7 +478,7 @@ def test_sampler_long_topk_tie_runs(dev, ts, route):
     got = _run_sampler(ts, dev, logits, params, 0, 5)
     res, lse = _oracle_ref(logits, params, 0, 5)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label="tie runs")
+             res.row_status, res.flagged, lse, logits, label="tie runs")
     assert np.all(got["row_status"] == 0)
 
 
@@ -569,7 +570,7 @@ def test_gumbel_noise_on_flat_rows(dev, ts, route):
     got = _run_sampler(ts, dev, logits, params, 1 << 33, 3)
     res, lse = _oracle_ref(logits, params, 1 << 33, 3)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label="flat")
+             res.row_status, res.flagged, lse, logits, label="flat")
     assert res.flagged.sum() <= 1
 
 
@@ -652,7 +653,7 @@ def test_sampler_slices_layouts(dev, ts, layout, kind, route):
     got = _run_sampler_slices(ts, dev, logits, widths, params, 11, 9, ld_extra=ld_extra)
     res, lse = _oracle_ref(logits, params, 11, 9)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=f"{layout}/{kind}")
+             res.row_status, res.flagged, lse, logits, label=f"{layout}/{kind}")
 
 
 @pytest.mark.parametrize("V,widths", [(1, [1]), (3, [1, 1, 1]), (7, [0, 4, 3]), (9, [4, 4, 1]),
@@ -666,7 +667,7 @@ def test_sampler_slices_tiny(dev, ts, V, widths, route):
     got = _run_sampler_slices(ts, dev, logits, widths, params, 0, 3)
     res, lse = _oracle_ref(logits, params, 0, 3)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=f"tiny{V}")
+             res.row_status, res.flagged, lse, logits, label=f"tiny{V}")
 
 
 @pytest.mark.parametrize("layout", ["crowded", "spread"])
@@ -688,7 +689,7 @@ def test_sampler_slices_large_targets(dev, ts, layout, route):
     got = _run_sampler_slices(ts, dev, logits, [17500] * 4, params, 3, max_lp)
     res, lse = _oracle_ref(logits, params, 3, max_lp)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, max_frac=1.0, label=layout)
+             res.row_status, res.flagged, lse, logits, label=layout)
 
 
 def test_sampler_one_slice_matches_buffer_call(dev, ts):
@@ -735,7 +736,7 @@ def test_sampler_draft_share(dev, ts, in_place, route):
     flagged = exp["flag_top_p"][sl] | exp["flag_tie"][sl]
     _compare(got, exp["token_ids"][sl], exp["token_logprobs"][sl], exp["topn_ids"][sl],
              exp["topn_logprobs"][sl], exp["row_status"][sl], flagged, exp["lse"][sl], logits,
-             max_frac=1.0, label="draft_share")
+             label="draft_share")
 
 
 # ------------------------------------------ processed log-probabilities (R11)
@@ -785,6 +786,7 @@ def test_sampler_processed_edge_cases(dev, ts, V, kind, route):
     say("sampler processed edge", V, kind, route)
     got = _run_sampler(ts, dev, logits, params, 2, max_lp, ld_extra=3, processed=True)
     res = oracle.sample(logits, params, 2, max_lp, processed=True)
+    assert res.flagged.sum() <= 1e-3 * rows
     _compare_processed(got, res, label=f"{V}/{kind}")
 
 
@@ -803,4 +805,5 @@ def test_sampler_processed_large_targets(dev, ts, route):
     say("sampler processed large targets", route)
     got = _run_sampler(ts, dev, logits, params, 0, max_lp, processed=True)
     res = oracle.sample(logits, params, 0, max_lp, processed=True)
+    assert res.flagged.sum() <= 1e-3 * rows
     _compare_processed(got, res, label="large targets")
