@@ -221,7 +221,8 @@ def test_slices_workspace_query():
     V = 151936
     assert ts.sampler_workspace_bytes_slices(640, [V], 20) == ts.sampler_workspace_bytes(640, V, 20)
     four = ts.sampler_workspace_bytes_slices(640, [V // 4] * 4, 20)
-    assert four >= ts.sampler_workspace_bytes(640, V, 20)
+    # more, shorter chunks: more records, fewer candidate slots per chunk
+    assert 0 < four <= 2 * ts.sampler_workspace_bytes(640, V, 20)
     assert ts.sampler_workspace_bytes_slices(640, [V // 64] * 64, 20) > 0
     assert ts.sampler_workspace_bytes_slices(640, [], 20) == 0
     assert ts.sampler_workspace_bytes_slices(640, [10, -1], 20) == 0
@@ -311,3 +312,4 @@ def test_gumbel_keys_validation():
     assert gk(*bad, 4, FAKE, FAKE, None) == ts.TS_EINVAL
     assert gk(*args, 4, FAKE + 2, FAKE, None) == ts.TS_EINVAL          # keys misaligned
     assert b"misaligned" in ts.lib.ts_last_error()
+

@@ -378,8 +378,8 @@ def test_sampler_large_targets(dev, ts, layout, route):
 
 
 def test_sampler_topk_beyond_fast_route(dev, ts, route):
-    """top_k between 1,024 and V: the fast route hands these rows to the
-    exact per-row kernel (with and without top-p, with top-N)."""
+    """top_k between 1,024 and V: up to 2,048 on the fast route, beyond it
+    the exact per-row kernel (with and without top-p, with top-N)."""
     rng = np.random.default_rng(21)
     rows, V, max_lp = 10, 20000, 20
     logits = (rng.standard_normal((rows, V)) * 1.5).astype(np.float32)
@@ -393,6 +393,27 @@ def test_sampler_topk_beyond_fast_route(dev, ts, route):
     res, lse = _oracle_ref(logits, params, 2, max_lp)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
              res.row_status, res.flagged, lse, logits, label="topk>1024")
+
+
+@pytest.mark.parametrize("p_top", [1.0, 0.8])
+def test_sampler_topk2048_rows(dev, ts, p_top, route):
+    """64 rows with top_k = 2,048 at the full vocabulary (the fast route's
+    largest top-k, one merge list of about four thousand candidates), with
+    and without top-p, against the oracle."""
+    w = workloads.get("spec_decode")
+    rows = 64
+    logits = workloads.make_logits(w, slice(0, rows))
+    params = np.zeros(rows, dtype=workloads.PARAMS_DTYPE)
+    params["temperature"] = np.linspace(0.4, 1.2, rows).astype(np.float32)
+    params["top_k"] = 2048
+    params["top_p"] = p_top
+    params["n_logprobs"] = np.arange(rows) % 21
+    params["seed"] = np.arange(rows, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15) + np.uint64(5)
+    say("sampler top_k 2048", p_top, route)
+    got = _run_sampler(ts, dev, logits, params, 0, 20)
+    res, lse = _oracle_ref(logits, params, 0, 20)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, label=f"topk2048/{p_top}")
 
 
 def test_sampler_probes_outside_nucleus(dev, ts, route):

@@ -30,7 +30,7 @@ enum RowKind : int {
   KIND_EXACT = 5    // handled by the exact per-row kernel (large top_k)
 };
 
-constexpr int kFastTopKMax = 1024;
+constexpr int kFastTopKMax = 2048;
 
 __device__ __forceinline__ bool params_ok(const ts_row_params& p, int max_logprobs) {
   if (!(p.temperature >= 0.0f) || isinf(p.temperature)) return false;
@@ -100,14 +100,13 @@ __device__ __forceinline__ float gumbel_key(float l, float m, float inv_t, uint6
 }
 
 // ------------------------------------------------------------ workspace layout
-constexpr int kCandCap = 4096;    // logit candidates per chunk
 constexpr int kKeyCap = 64;       // Gumbel-key candidates per chunk (top-p-only rows)
 constexpr int kProbes = 8;        // probe points per top-p-only row
 constexpr int kMaxChunks = 128;   // chunks per row
 constexpr int kChunkThreads = 256;
 constexpr int kChunkVec = 16;     // float4 per thread
 constexpr int kChunkMax = kChunkThreads * kChunkVec * 4;  // 16384 logits
-constexpr int kListMax = 2048;    // merged candidates a row may keep in LDS
+constexpr int kListMax = 4096;    // merged candidates a row may keep in LDS
 constexpr float kKeyMargin = 1e-4f;  // rounding margin between chunk-local and row keys
 
 struct ChunkRec {  // one per (row, chunk); 64 bytes
@@ -121,6 +120,7 @@ struct ChunkRec {  // one per (row, chunk); 64 bytes
   float kfloor;    // every token whose key (l - cmax)/T + g >= kfloor is listed
   int pad[8];
 };
+static_assert(sizeof(ChunkRec) == 64, "64-byte chunk records");
 
 struct ProbeRec {  // a top-p-only row whose boundary lies below the listed logits
   double z;        // total temperature-scaled mass, relative to the row maximum
@@ -133,7 +133,7 @@ struct ProbeRec {  // a top-p-only row whose boundary lies below the listed logi
 struct FastLayout {
   int S;  // chunks per row
   int L;  // logits per chunk (multiple of 4; a slice's last chunk may be shorter)
-  int cc;  // candidate slots per chunk: min(kCandCap, L) (a chunk lists at most L)
+  int cc;  // candidate slots per chunk (cand_slots)
   int nsl;                      // column slices
   int cbase[TS_MAX_SLICES + 1];  // first chunk of each slice (chunks never straddle slices)
   size_t off_ctr, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part, total;
@@ -149,7 +149,26 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // the chunked path does not take.
 constexpr int64_t kWantChunks = 256;
 
-inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n) {
+// Candidate slots per chunk: a chunk lists every logit at or above a
+// threshold that at least its target count reach (chunk_target of the row's
+// need, at most max(kFastTopKMax, max_logprobs, 64)); twice the largest
+// target plus 64 leaves room for the logits that tie with or lie just above
+// the threshold.  A chunk that lists more is an overflow: its row takes the
+// exact per-row kernel (same results).
+inline int cand_slots(int L, int S, int max_logprobs) {
+  int64_t M = kFastTopKMax;
+  if (max_logprobs > M) M = max_logprobs;
+  int64_t mc = M;
+  if (M > 64) {
+    mc = (3 * M + 2 * S - 1) / (2 * S);
+    if (mc < 64) mc = 64;
+    if (mc > M) mc = M;
+  }
+  int64_t cc = (2 * mc + 64 + 63) / 64 * 64;
+  return static_cast<int>(cc < L ? cc : L);
+}
+
+inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n, int max_logprobs) {
   FastLayout l{};
   int64_t vocab = 0;
   for (int s = 0; s < n; ++s) vocab += cols[s];
@@ -169,7 +188,6 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n) {
   L = (L + 3) / 4 * 4;
   if (L < 4) L = 4;
   l.L = static_cast<int>(L);
-  l.cc = l.L < kCandCap ? l.L : kCandCap;
   l.nsl = n;
   int64_t total = 0;
   l.cbase[0] = 0;
@@ -180,6 +198,7 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n) {
   l.S = (L > kChunkMax || total > kMaxChunks || n >= kMaxChunks || total < 1)
             ? 0
             : static_cast<int>(total);
+  l.cc = cand_slots(l.L, l.S > 0 ? l.S : 1, max_logprobs);
   const size_t R = static_cast<size_t>(rows);
   const size_t RS = R * static_cast<size_t>(l.S);
   size_t off = 0;
@@ -206,7 +225,7 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n) {
 // The chunked path needs every slice to start at a column that is a multiple
 // of 4 (a float4 of a chunk then holds one Philox block of four tokens).
 inline bool fast_path_supported(int64_t rows, const int64_t* cols, int n) {
-  const FastLayout l = make_layout(rows, cols, n);
+  const FastLayout l = make_layout(rows, cols, n, 0);
   if (l.S == 0) return false;
   int64_t off = 0;
   for (int s = 0; s < n; ++s) {

@@ -209,6 +209,18 @@ __device__ __forceinline__ float wave_qth_hi16(float x, int q) {
   return key_floor_value(K);
 }
 
+__device__ __forceinline__ float wave_qth2_hi16(const float (&t)[4], int q) {
+  const uint32_t k0 = order_key(t[0]), k1 = order_key(t[1]);
+  uint32_t K = 0u;
+#pragma unroll
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t cand = K | (1u << b);
+    const int cnt = __popcll(__ballot(k0 >= cand)) + __popcll(__ballot(k1 >= cand));
+    if (cnt >= q) K = cand;
+  }
+  return key_floor_value(K);
+}
+
 __device__ __forceinline__ float wave_qth4_hi16(const float (&t)[4], int q) {
   const uint32_t k0 = order_key(t[0]), k1 = order_key(t[1]), k2 = order_key(t[2]),
                  k3 = order_key(t[3]);
@@ -439,11 +451,13 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   // logit makes the sum NaN; +inf makes it NaN too (inf - inf); a thread
   // holding only -inf and NaN scans for NaN afterwards.
   const int M = __builtin_amdgcn_readfirstlane(chunk_target(cand_target(kind, p, V), S));
-  const bool four = M > 64 && M < n;
+  // Per-thread largest values kept for the candidate threshold: the maximum
+  // (M <= 64), the two largest (M <= 256) or the four largest (beyond).
+  const int tk = (M <= 64 || M >= n) ? 1 : (M <= 256 ? 2 : 4);
   float t[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   float lm = -INFINITY, ls = 0.0f, lt = 0.0f;
   const float sc = inv_t * kLog2e;
-  if (four) {
+  if (tk == 4) {
 #pragma unroll
     for (int j = 0; j < AV; ++j) {
       const float4 f = v[j];
@@ -459,6 +473,18 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
         }
       }
     }
+  } else if (tk == 2) {
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const float4 f = v[j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float x = lane(f, q);
+        t[1] = fmaxf(t[1], fminf(t[0], x));
+        t[0] = fmaxf(t[0], x);
+      }
+    }
+    lm = t[0];
   } else {
 #pragma unroll
     for (int j = 0; j < AV; ++j) {
@@ -488,7 +514,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
       }
     }
   }
-  if (!four) t[0] = lm;
+  if (tk == 1) t[0] = lm;
   int flag = lm == INFINITY ? 1 : 0;
   if (lm == -INFINITY) {
 #pragma unroll
@@ -516,13 +542,15 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   // Logit candidate threshold tf: at least M logits of the chunk are >= tf.
   // M <= 64: every wave holds ceil(M/4) per-thread maxima >= its own q-th
   // largest, so the smallest of the four wave values works.  64 < M <= 256:
-  // the same over per-thread top-4 values.  M > 256: the M-th largest of the
-  // block's 4 * 256 top-4 values, by radix selection in LDS.
+  // the same over each thread's two largest values.  M > 256: the M-th
+  // largest of the block's 4 * 256 top-4 values, by radix selection in LDS.
   if (M < n && M <= 256) {
     const int q = (M + AW - 1) / AW;
-    const float tw = four ? wave_qth4_hi16(t, q) : wave_qth_hi16(t[0], q);
+    const float tw = tk == 4   ? wave_qth4_hi16(t, q)
+                     : tk == 2 ? wave_qth2_hi16(t, q)
+                               : wave_qth_hi16(t[0], q);
     if (lane_id == 0) sh.wthr[wave] = tw;
-  } else if (M < n) {
+  } else if (M < n && M <= 4 * AT) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sh.keys4[4 * tid + i] = order_key(t[i]);
   }
@@ -544,11 +572,11 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     tf = sh.wthr[0];
 #pragma unroll
     for (int w = 1; w < AW; ++w) tf = fminf(tf, sh.wthr[w]);
-  } else if (M < n) {
+  } else if (M < n && M <= 4 * AT) {
     const uint32_t kk = lds_kth_largest<AT>(sh.keys4, 4 * AT, static_cast<uint32_t>(M), sh.hist,
                                             sh.ru, &sh.sel_d, &sh.sel_above);
     tf = key_floor_value(kk);
-  }
+  }  // a larger target than the block's 4 * AT top-4 values lists the whole chunk
 
   // Every valid logit >= tf goes to the chunk's candidate list.  Slots come
   // from a block-wide exclusive scan of the per-thread counts, so writing a
@@ -646,42 +674,76 @@ struct MergeSmem {
 
 __device__ __forceinline__ void push_row(int* ctr, int* list, int r) { list[atomicAdd(ctr, 1)] = r; }
 
-// Bitonic sort of n (a power of two, <= kListMax) packed candidates in LDS,
-// largest first.  Each thread takes up to kListMax / (2 BT) compare-exchange
-// pairs per stage, loads all of them before comparing, so a stage costs one
-// LDS round trip and one barrier.
-__device__ void lds_bitonic_desc(unsigned long long* s, int n) {
-  constexpr int PAIRS = kListMax / (2 * BT);
-  const int tid = threadIdx.x, half = n >> 1;
-  for (int k = 2; k <= n; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      int lo[PAIRS];
-      unsigned long long a[PAIRS], b[PAIRS];
+// One compare-exchange stage between entries J apart within a lane's P
+// registers (J a compile-time constant, so the registers are never indexed
+// at run time).
+template <int P, int J>
+__device__ __forceinline__ void sort_lane_stage(unsigned long long (&v)[P], int base, int k) {
 #pragma unroll
-      for (int t = 0; t < PAIRS; ++t) {
-        const int q = tid + t * BT;
-        lo[t] = ((q & ~(j - 1)) << 1) | (q & (j - 1));  // j is a power of two
-        if (q < half) {
-          a[t] = s[lo[t]];
-          b[t] = s[lo[t] + j];
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < PAIRS; ++t) {
-        const int q = tid + t * BT;
-        if (q < half) {
-          const bool desc = (lo[t] & k) == 0;
-          if (desc ? (a[t] < b[t]) : (a[t] > b[t])) {
-            s[lo[t]] = b[t];
-            s[lo[t] + j] = a[t];
-          }
-        }
-      }
-      __syncthreads();
-    }
+  for (int i = 0; i < P; ++i) {
+    if ((i & J) || i + J >= P) continue;
+    const unsigned long long a = v[i], b = v[i + J];
+    const unsigned long long hi = a > b ? a : b, lo = a > b ? b : a;
+    const bool desc = ((base + i) & k) == 0;
+    v[i] = desc ? hi : lo;
+    v[i + J] = desc ? lo : hi;
   }
 }
 
+// Bitonic sort, largest first, of the 256 * P packed candidates in s (LDS;
+// P = 2, 4, 8 or 16).  Wave w holds entries w * 64P .. (w + 1) * 64P - 1, lane l
+// of it P consecutive ones in registers, so the compare-exchange stages
+// between entries of one lane run in registers, those within a wave by lane
+// shuffles, and only the few stages that pair entries of different waves go
+// through LDS (the power-of-two strides of an all-LDS network crowd a few
+// banks).  Every thread of the workgroup calls it.
+template <int P>
+__device__ void block_sort_desc(unsigned long long* s) {
+  constexpr int N = BT * P;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int base = w * kWave * P + lane * P;
+  unsigned long long v[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) v[i] = s[base + i];
+  for (int k = 2; k <= N; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= kWave * P) {
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < P; ++i) s[base + i] = v[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          const int x = base + i;
+          const unsigned long long y = s[x ^ j];
+          const bool keep_max = ((x & k) == 0) == ((x & j) == 0);
+          v[i] = keep_max ? (v[i] > y ? v[i] : y) : (v[i] < y ? v[i] : y);
+        }
+      } else if (j >= P) {
+        const int lm = j / P;
+#pragma unroll
+        for (int i = 0; i < P; ++i) {
+          const int x = base + i;
+          const unsigned long long y = shfl_xor_u64(v[i], lm);
+          const bool keep_max = ((x & k) == 0) == ((x & j) == 0);
+          v[i] = keep_max ? (v[i] > y ? v[i] : y) : (v[i] < y ? v[i] : y);
+        }
+      } else if (j == 8) {
+        sort_lane_stage<P, 8>(v, base, k);
+      } else if (j == 4) {
+        sort_lane_stage<P, 4>(v, base, k);
+      } else if (j == 2) {
+        sort_lane_stage<P, 2>(v, base, k);
+      } else {
+        sort_lane_stage<P, 1>(v, base, k);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < P; ++i) s[base + i] = v[i];
+  __syncthreads();
+}
 
 // Largest key offset (key - base) over the entries of sh.list[0, U) with
 // key >= base, as a bit count: offsets fit in span_bits bits.
@@ -906,9 +968,9 @@ __device__ uint32_t list_mass_key(MergeSmem& sh, int U, uint32_t kmin, float m, 
 __device__ int trim_and_sort(MergeSmem& sh, int U, int need, uint32_t floor_key) {
   const int tid = threadIdx.x;
   int cap = need + 64;
-  if (cap > 256) cap = cap <= 1024 ? 1024 : kListMax;  // what the sort pads to anyway
+  if (cap > 256) cap = cap <= 1024 ? 1024 : 2048;  // what the sort pads to anyway
   int C = U;
-  if (U > cap) {
+  if (U > cap && U > BT) {  // up to one entry per thread is ranked directly instead
     uint32_t rmax = 0u;
     for (int i = tid; i < U; i += BT) rmax = max(rmax, cand_key(sh.list[i]) - floor_key);
     if (tid == 0) sh.rmax = 0u;
@@ -959,14 +1021,18 @@ __device__ int trim_and_sort(MergeSmem& sh, int U, int need, uint32_t floor_key)
     C = sh.nlist;
   }
   if (C <= BT) {
-    // Rank sort: entry x goes to position #{y > x} (read all, then write).
+    // Rank sort: entry x goes to position #{y > x} (read all, then write);
+    // eight entries per step in flight, two per 16-byte read.
+    typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
     const unsigned long long x = tid < C ? sh.list[tid] : 0ull;
     int rank = 0;
     if (tid < C) {
+      const u64x2* l2 = reinterpret_cast<const u64x2*>(sh.list);
       int j = 0;
-      for (; j + 4 <= C; j += 4) {
-        rank += (sh.list[j] > x) + (sh.list[j + 1] > x) + (sh.list[j + 2] > x) +
-                (sh.list[j + 3] > x);
+      for (; j + 8 <= C; j += 8) {
+        const u64x2 a = l2[j / 2], b = l2[j / 2 + 1], c = l2[j / 2 + 2], d = l2[j / 2 + 3];
+        rank += (a.x > x) + (a.y > x) + (b.x > x) + (b.y > x) + (c.x > x) + (c.y > x) +
+                (d.x > x) + (d.y > x);
       }
       for (; j < C; ++j) rank += sh.list[j] > x;
     }
@@ -975,11 +1041,14 @@ __device__ int trim_and_sort(MergeSmem& sh, int U, int need, uint32_t floor_key)
     __syncthreads();
     return C;
   }
-  int n2 = 1;
+  int n2 = 2 * BT;
   while (n2 < C) n2 <<= 1;
   for (int i = C + tid; i < n2; i += BT) sh.list[i] = 0ull;
   __syncthreads();
-  lds_bitonic_desc(sh.list, n2);
+  if (n2 == 2 * BT) block_sort_desc<2>(sh.list);
+  else if (n2 == 4 * BT) block_sort_desc<4>(sh.list);
+  else if (n2 == 8 * BT) block_sort_desc<8>(sh.list);
+  else block_sort_desc<16>(sh.list);  // long tie runs only
   return C;
 }
 
@@ -1185,6 +1254,13 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   int need = n_eff > 1 ? n_eff : 1;
   if (kind == KIND_TOPK && p.top_k > need) need = p.top_k;
   if (kind == KIND_TOPP && need < 64) need = 64;
+  // Most rows use a short prefix of the list: the top N, a top-k set of at
+  // most 192, or the 64-entry head of a top-p-only row (its boundary further
+  // down goes to the probe pass).  Those lists are trimmed to the prefix and
+  // sorted, and the top-p boundary is a prefix sum over them.  Longer top-k
+  // sets stay unsorted: the k-th key and the top-p boundary are found by
+  // count- and mass-weighted radix selection (sorting a list of a few
+  // thousand entries in one workgroup costs several times more).
   bool sorted = need <= 192;
   if (sorted) {
     U = trim_and_sort(sh, U, need < U ? need : U, floor_key);
@@ -1479,9 +1555,8 @@ bool env_flag(const char* name) {
 
 size_t sampler_workspace_size(int64_t rows, const int64_t* slice_cols, int n_slices,
                               int max_logprobs) {
-  (void)max_logprobs;
   if (!fast_path_supported(rows, slice_cols, n_slices)) return 256;
-  return make_layout(rows, slice_cols, n_slices).total;
+  return make_layout(rows, slice_cols, n_slices, max_logprobs).total;
 }
 
 hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspace_bytes,
@@ -1493,7 +1568,7 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
   for (int s = 0; s < a.lv.n; ++s) cols[s] = a.lv.off[s + 1] - a.lv.off[s];
   if (env_flag("TS_SAMPLER_EXACT") || !fast_path_supported(a.rows, cols, a.lv.n))
     return launch_sampler_finish(a, nullptr, ws, stream);
-  const FastLayout lay = make_layout(a.rows, cols, a.lv.n);
+  const FastLayout lay = make_layout(a.rows, cols, a.lv.n, a.max_logprobs);
   // float4 loads: every slice 16-byte aligned with rows and widths of whole float4s.
   int vec = 1;
   for (int s = 0; s < a.lv.n; ++s) {
