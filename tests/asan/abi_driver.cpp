@@ -64,6 +64,13 @@ int main() {
   expect(sampler_sample(nullptr, 0, 100, 100, nullptr, 0, 5, nullptr, nullptr, nullptr, nullptr,
                         nullptr, nullptr, 0, nullptr), TS_OK, "sample empty");
 
+  expect(sampler_sample_noalloc(Ff, -1, 100, 100, Fp, 0, 5, Fi, Ff, Fi, Ff, Fi, nullptr), TS_EINVAL,
+         "noalloc rows<0");
+  expect(sampler_sample_noalloc(Ff, 4096, 262144, 262144, Fp, 0, 20, Fi, Ff, Fi, Ff, Fi, nullptr),
+         TS_EUNSUPPORTED, "noalloc too large");
+  expect(sampler_sample_noalloc(nullptr, 0, 100, 100, nullptr, 0, 5, nullptr, nullptr, nullptr,
+                                nullptr, nullptr, nullptr), TS_OK, "noalloc empty");
+
   // slice calls with the largest accepted table, and one entry past it
   static const float* ptrs[TS_MAX_SLICES + 1];
   static int64_t cols[TS_MAX_SLICES + 1], lds[TS_MAX_SLICES + 1];

@@ -42,8 +42,10 @@ def test_header_constants_match_binding():
     for name, val in [("TS_MAX_LOGPROBS", ts.TS_MAX_LOGPROBS), ("TS_MAX_SLICES", ts.TS_MAX_SLICES),
                       ("TS_LOGPROBS_PROCESSED", ts.TS_LOGPROBS_PROCESSED),
                       ("TS_PROBE_SMALL_OPERANDS", ts.TS_PROBE_SMALL_OPERANDS),
+                      ("TS_NOALLOC_SCRATCH_BYTES", "(64ull << 20)"),
                       ("TS_PROBE_RANDOM_OPERANDS", ts.TS_PROBE_RANDOM_OPERANDS)]:
-        assert re.search(rf"#define {name} {val}\b", text)
+        assert re.search(rf"#define {name} {re.escape(str(val))}", text), name
+    assert ts.TS_NOALLOC_SCRATCH_BYTES == 64 << 20
     assert workloads.PARAMS_DTYPE.itemsize == ts.PARAMS_BYTES
 
 
@@ -313,3 +315,21 @@ def test_gumbel_keys_validation():
     assert gk(*args, 4, FAKE + 2, FAKE, None) == ts.TS_EINVAL          # keys misaligned
     assert b"misaligned" in ts.lib.ts_last_error()
 
+
+def test_sampler_noalloc_validation():
+    """The no-allocation variant validates on the host: bad sizes, and shapes
+    whose workspace exceeds the built-in scratch, are rejected before any HIP
+    call."""
+    f = ts.lib.sampler_sample_noalloc
+    args = lambda rows, vocab, lp: (FAKE, rows, vocab, vocab, FAKE, 0, lp, FAKE, FAKE, FAKE,  # noqa: E731
+                                    FAKE, FAKE, None)
+    assert f(*args(-1, 100, 5)) == ts.TS_EINVAL
+    assert f(*args(8, 100, -1)) == ts.TS_EINVAL
+    assert f(*args(0, 100, 5)) == ts.TS_OK
+    big = (4096, 262144, 20)
+    assert ts.sampler_workspace_bytes(*big) > ts.TS_NOALLOC_SCRATCH_BYTES
+    assert f(*args(*big)) == ts.TS_EUNSUPPORTED
+    assert b"scratch" in ts.lib.ts_last_error()
+    # the headline shapes fit the built-in scratch
+    for shape in [(640, 151936, 20), (256, 151936, 5), (1024, 262144, 20)]:
+        assert ts.sampler_workspace_bytes(*shape) <= ts.TS_NOALLOC_SCRATCH_BYTES, shape

@@ -15,7 +15,7 @@ CSRC = os.path.join(ROOT, "top_sampling_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Every source of the library: host code only, sanitized.
 SOURCES = ["api.hip", "lmhead_gemm.hip", "lmhead_fp8.hip", "sampler_fast.hip", "sampler_exact.hip",
-           "assemble.hip", "clock_probe.hip", "noise_readout.hip"]
+           "assemble.hip", "clock_probe.hip", "noise_readout.hip", "noalloc.hip"]
 
 
 def _compile(args):

@@ -38,6 +38,7 @@ TS_MAX_LOGPROBS = 1024
 TS_MAX_SLICES = 64
 TS_LOGPROBS_PROCESSED = 1
 TS_PROBE_SMALL_OPERANDS, TS_PROBE_RANDOM_OPERANDS = 0, 1
+TS_NOALLOC_SCRATCH_BYTES = 64 << 20
 PARAMS_BYTES = 24
 
 # (name, restype, argtypes) of every symbol the headers declare
@@ -51,6 +52,8 @@ SYMBOLS = {
     "sampler_workspace_bytes": (_SZ, [_I64, _I64, _I32]),
     "sampler_sample": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _I32, _VP, _VP, _VP, _VP,
                                       _VP, _VP, _SZ, _VP]),
+    "sampler_sample_noalloc": (ctypes.c_int, [_VP, _I64, _I64, _I64, _VP, _I64, _I32, _VP, _VP,
+                                              _VP, _VP, _VP, _VP]),
     "sampler_workspace_bytes_slices": (_SZ, [_I64, _VP, _I32, _I32]),
     "sampler_sample_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _I32, _VP, _VP,
                                              _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -269,6 +272,29 @@ def sampler_sample(logits, params, row_offset: int = 0, max_logprobs: int = 0, o
         _ptr(out.topn_ids) if max_logprobs > 0 else None,
         _ptr(out.topn_logprobs) if max_logprobs > 0 else None,
         _ptr(out.row_status), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+    return out
+
+
+def sampler_sample_noalloc(logits, params, row_offset: int = 0, max_logprobs: int = 0, out=None,
+                           stream=None) -> SampleOutput:
+    """``sampler_sample`` with the library's built-in scratch as the
+    workspace (no workspace argument; nothing is allocated by the call
+    itself, ``out`` aside when it is not given).  Calls that overlap on one
+    GPU share the scratch and must be serialised."""
+    torch = _torch()
+    rows, vocab = logits.shape
+    if logits.dtype != torch.float32 or logits.stride(1) != 1:
+        raise ValueError("logits must be fp32 with unit column stride")
+    if params.dtype != torch.uint8 or params.numel() != PARAMS_BYTES * rows:
+        raise ValueError("params must be rows x 24 bytes (uint8)")
+    if out is None:
+        out = allocate_sample_output(rows, max_logprobs, logits.device)
+    _check(lib.sampler_sample_noalloc(
+        _ptr(logits), rows, vocab, logits.stride(0), _ptr(params), row_offset, max_logprobs,
+        _ptr(out.token_ids), _ptr(out.token_logprobs),
+        _ptr(out.topn_ids) if max_logprobs > 0 else None,
+        _ptr(out.topn_logprobs) if max_logprobs > 0 else None,
+        _ptr(out.row_status), _stream_ptr(stream)))
     return out
 
 

@@ -32,6 +32,11 @@ constexpr int64_t kMaxDim = 0x7fffffff;
 
 }  // namespace
 
+namespace ts {
+// A failure recorded for ts_last_error by other source files of the library.
+int fail_message(int code, const char* msg) { return fail(code, "%s", msg); }
+}  // namespace ts
+
 extern "C" {
 
 const char* ts_status_string(int status) {
