@@ -72,17 +72,24 @@ def _oracle_sample_part(job):
     import oracle
 
     logits, params, row_offset, max_logprobs = job
-    oracle.sample(logits, params, row_offset, max_logprobs)
-    return logits.shape[0]
+    res = oracle.sample(logits, params, row_offset, max_logprobs)
+    return (logits.shape[0], res.token_ids, res.topn_ids, res.row_status, res.flag_top_p,
+            res.flag_tie)
 
 
-def cpu_baseline(x, wt, wq, wsc, logits_sample, params, max_logprobs, rows: int, pool, workers):
+def cpu_baseline(x, wt, wq, wsc, logits_sample, params, max_logprobs, rows: int, pool, workers,
+                 gpu_out=None, row_offset: int = 0):
     """The CPU oracle as it stands, timed on a bounded sample of the workload:
     the float64 projection of `rows` rows against the whole lm_head (for the
     FP8 workload: the oracle's per-row quantization of those rows, then its
     projection from the same lm_head codes the GPU uses), with as many BLAS
     threads as host cores, then the full-sort sampler on those rows, split by
-    rows over a process pool of the same size.  Scaled to rows/s."""
+    rows over a process pool of the same size.  Scaled to rows/s.
+
+    Returns (baseline, flagged): the second counts the rows the oracle flags
+    as ambiguous on these logits (the step's own) and, with ``gpu_out`` (the
+    step's token ids, top-N ids and row status as numpy arrays), how many
+    unflagged rows differ from the GPU's."""
     import numpy as np
     import threadpoolctl
 
@@ -114,12 +121,25 @@ def cpu_baseline(x, wt, wq, wsc, logits_sample, params, max_logprobs, rows: int,
             project()
         t1 = time.perf_counter()
     cuts = np.linspace(0, rows, workers + 1).astype(int)
-    jobs = [(logits_sample[a:b], params[a:b], int(a), max_logprobs)
+    jobs = [(logits_sample[a:b], params[a:b], row_offset + int(a), max_logprobs)
             for a, b in zip(cuts[:-1], cuts[1:]) if b > a]
-    done = sum(pool.map(_oracle_sample_part, jobs)) if pool is not None else \
-        sum(map(_oracle_sample_part, jobs))
+    parts = pool.map(_oracle_sample_part, jobs) if pool is not None else \
+        list(map(_oracle_sample_part, jobs))
     t2 = time.perf_counter()
-    assert done == rows
+    assert sum(p[0] for p in parts) == rows
+    cat = lambda i: np.concatenate([p[i] for p in parts])  # noqa: E731
+    tok, topn, status, ftp, ftie = (cat(i) for i in range(1, 6))
+    flagged = ftp | ftie
+    counts = {"rows_checked": rows, "flagged": int(flagged.sum()),
+              "flagged_top_p": int(ftp.sum()), "flagged_key_tie": int(ftie.sum()),
+              "source": "the oracle on the step's own logits (first rows of the batch)"}
+    if gpu_out is not None:
+        g_tok, g_topn, g_status = (a[:rows] for a in gpu_out)
+        ok = ~flagged
+        counts["unflagged_token_id_mismatches"] = int((g_tok[ok] != tok[ok]).sum())
+        counts["unflagged_topn_id_mismatches"] = int((g_topn[ok] != topn[ok]).any(axis=1).sum()) \
+            if topn.ndim == 2 and topn.shape[1] else 0
+        counts["row_status_mismatches"] = int((g_status != status).sum())
     procs = len(jobs) if pool is not None else 1
     proj = (f"{what} against the full lm_head ({t1 - t0:.1f}s, BLAS threads {threads}) + "
             if project is not None else "")
@@ -130,7 +150,7 @@ def cpu_baseline(x, wt, wq, wsc, logits_sample, params, max_logprobs, rows: int,
         "kind": "oracle",
         "sample": f"{rows} rows: {proj}full-sort sampler ({t2 - t1:.1f}s, "
                   f"{procs} processes)",
-    }
+    }, counts
 
 
 def time_alone(fn, stream, scratch, runs: int, warmup: int = 5) -> dict:
@@ -362,6 +382,33 @@ def main():
     sl_ms = sum(a.elapsed_time(b) for a, b in ev_sl) / args.steps
     n_diff = int((out_sl.token_ids != out.token_ids).sum())
 
+    # The sampler on the same logits with every row's top_k forced to 1,000,
+    # then to 2,048 (temperature, top-p, seeds and logprobs as drawn): a
+    # top_k above 1,024 must not cost much more than one below.
+    topk_ms = {}
+    for k in (1000, 2048):
+        pk = params_np.copy()
+        pk["top_k"] = k
+        pk_dev = ts.params_to_device(pk, dev)
+        ws_k = ts.allocate_workspace(rows, vocab, w.max_logprobs, dev)
+        out_k = ts.allocate_sample_output(rows, w.max_logprobs, dev)
+
+        def sample_k():
+            ts.sampler_sample(batch, pk_dev, w.row_offset, w.max_logprobs, out=out_k,
+                              workspace=ws_k, stream=stream)
+
+        for _ in range(max(1, args.warmup)):
+            sample_k()
+        ev_k = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        for a, b in ev_k:
+            a.record(stream)
+            sample_k()
+            b.record(stream)
+        torch.cuda.synchronize()
+        topk_ms[k] = sum(a.elapsed_time(b) for a, b in ev_k) / args.steps
+        del ws_k, out_k, pk_dev
+
     # Each kernel alone, cold (a 512 MiB scratch write before every run).
     iso = {}
     if args.iso_runs > 0:
@@ -421,6 +468,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(smp_gbs / HBM_PEAK_GBS, 4),
                 "traffic": None}
 
+    rps = lambda ms: round(rows / (ms * 1e-3), 1)  # noqa: E731
     metric = METRIC if w.name == "spec_decode" else (
         f"sampled rows/s + sampler HBM GB/s + lm_head TFLOP/s at {rows} rows x V={vocab:,}")
     line = {
@@ -441,23 +489,31 @@ def main():
                    "description": w.description},
         "kernels": {
             gemm_kernel: {"ms": round(gemm_ms, 4), "tflops": gemm_tflops and round(gemm_tflops, 1),
-                          "frac_mfma_peak": gemm_tflops and round(gemm_tflops / peak_tf, 4)},
+                          "frac_mfma_peak": gemm_tflops and round(gemm_tflops / peak_tf, 4),
+                          "rows_per_s": rps(gemm_ms)},
             "assemble": {"ms": round(asm_ms, 4), "gbs": round(asm_gbs, 1),
-                         "frac_hbm_peak": round(asm_gbs / HBM_PEAK_GBS, 4)},
+                         "frac_hbm_peak": round(asm_gbs / HBM_PEAK_GBS, 4),
+                         "rows_per_s": rps(asm_ms)},
             "sampler": {"ms": round(smp_ms, 4), "gbs": round(smp_gbs, 1),
                         "frac_hbm_peak": round(smp_gbs / HBM_PEAK_GBS, 4),
-                        "rows_per_s": round(rows / (smp_ms * 1e-3), 1)},
+                        "rows_per_s": rps(smp_ms)},
             "sampler_slices": {"ms": round(sl_ms, 4), "gbs": round(sampler_bytes / (sl_ms * 1e-3) / 1e9, 1),
                                "frac_hbm_peak": round(sampler_bytes / (sl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                               "rows_per_s": rps(sl_ms),
                                "saves_ms_vs_assemble_then_sample": round(asm_ms + smp_ms - sl_ms, 4),
                                "token_ids_differing_from_stitched": n_diff},
+            "sampler_top_k_1000_every_row": {"ms": round(topk_ms[1000], 4),
+                                             "rows_per_s": rps(topk_ms[1000])},
+            "sampler_top_k_2048_every_row": {"ms": round(topk_ms[2048], 4),
+                                             "rows_per_s": rps(topk_ms[2048]),
+                                             "vs_top_k_1000": round(topk_ms[2048] / topk_ms[1000], 3)},
         },
         "roofline": roof,
     }
     if not flops:  # sampler-only workload: there is no projection to report
         del line["kernels"][gemm_kernel]
     if quant_ms is not None:
-        line["kernels"]["quantize_hidden"] = {"ms": round(quant_ms, 4)}
+        line["kernels"]["quantize_hidden"] = {"ms": round(quant_ms, 4), "rows_per_s": rps(quant_ms)}
     if iso:
         algo = {"lmhead_gemm": gemm_bytes, "lmhead_e4m3": gemm_bytes, "assemble": asm_bytes,
                 "sampler": sampler_bytes, "sampler_slices": sampler_bytes}
@@ -474,8 +530,13 @@ def main():
     if not args.no_cpu_baseline:
         sample_rows = min(args.cpu_rows, rows)
         logits_sample = batch[:sample_rows].cpu().numpy()
-        line["cpu_baseline"] = cpu_baseline(x, wt, wq, wsc, logits_sample, params_np, w.max_logprobs,
-                                            sample_rows, pool, workers)
+        gpu_out = (out.token_ids.cpu().numpy(), out.topn_ids.cpu().numpy(),
+                   out.row_status.cpu().numpy())
+        line["cpu_baseline"], line["flagged_rows"] = cpu_baseline(
+            x, wt, wq, wsc, logits_sample, params_np, w.max_logprobs, sample_rows, pool, workers,
+            gpu_out, w.row_offset)
+    else:
+        line["flagged_rows"] = None
     if pool is not None:
         pool.close()
         pool.join()
