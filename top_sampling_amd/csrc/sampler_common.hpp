@@ -102,6 +102,7 @@ __device__ __forceinline__ float gumbel_key(float l, float m, float inv_t, uint6
 // ------------------------------------------------------------ workspace layout
 constexpr int kKeyCap = 64;       // Gumbel-key candidates per chunk (top-p-only rows)
 constexpr int kProbes = 8;        // probe points per top-p-only row
+
 constexpr int kMaxChunks = 128;   // chunks per row
 constexpr int kChunkThreads = 256;
 constexpr int kChunkVec = 16;     // float4 per thread
@@ -136,7 +137,8 @@ struct FastLayout {
   int cc;  // candidate slots per chunk (cand_slots)
   int nsl;                      // column slices
   int cbase[TS_MAX_SLICES + 1];  // first chunk of each slice (chunks never straddle slices)
-  size_t off_ctr, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part, total;
+  size_t off_ctr, off_order, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part,
+      total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -204,6 +206,8 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n, int max_
   size_t off = 0;
   l.off_ctr = off;  // [0] exact rows, [1] probe rows
   off = align_up(off + 256, 256);
+  l.off_order = off;  // the chunk pass's row order (heaviest rows first)
+  off = align_up(off + R * sizeof(int), 256);
   l.off_exact = off;
   off = align_up(off + R * sizeof(int), 256);
   l.off_probe = off;

@@ -9,6 +9,10 @@
 // HBM once by the chunk pass; the probe pass re-reads only the rows that need
 // it.
 //
+// O  row order    one workgroup: the order the chunk pass takes the rows in,
+//                 rows that draw Gumbel keys over every token first, then
+//                 rows with long top-k lists, then the rest (a slow row near
+//                 the end of the grid would leave a tail).
 // A  chunk pass   one 256-thread workgroup per (row, chunk of <= 16384
 //                 logits), the chunk held in registers (16 float4 per
 //                 thread).  Per chunk, in one pass over the loaded values:
@@ -39,7 +43,7 @@
 //                 by top-p iff that mass is below p times the total, so the
 //                 first probe (by key) that is kept is the Gumbel-max winner.
 // X  finish       (sampler_exact.hip) settles probe rows; rows that no fast
-//                 route settles (candidate or key overflow, top_k > 1024, no
+//                 route settles (candidate or key overflow, top_k > 2048, no
 //                 kept probe) run the exact per-row kernel.
 #include <stdlib.h>
 
@@ -416,15 +420,122 @@ __device__ __forceinline__ int chunk_keys(const float4 (&v)[AV], float cmax, flo
   return sh.nkey;
 }
 
+// ------------------------------------------------------------- row order
+// The chunk pass's cost per row differs by a factor of three between row
+// kinds: rows that draw Gumbel keys over every token (full-vocabulary and
+// top-p-only rows) are the slowest, rows with a long top-k list next.  With
+// the rows taken in their own order, such rows near the end of the grid
+// leave a slow tail; this single workgroup writes the order the chunk pass
+// takes them in instead (those classes first, each class in row order).
+// It also clears the exact- and probe-row counters of this call.
+constexpr int OT = 256;
+
+// The four filter fields of a row's parameters in one 16-byte read (two
+// 8-byte loads: rows are 24 bytes apart), issued before any of them is
+// tested, so the checks below cost one memory round trip, not four.
+__device__ __forceinline__ ts_row_params load_filter_params(const ts_row_params* row) {
+  const uint2* q = reinterpret_cast<const uint2*>(row);
+  const uint2 x = q[0], y = q[1];
+  ts_row_params p;
+  p.temperature = __uint_as_float(x.x);
+  p.top_k = static_cast<int>(x.y);
+  p.top_p = __uint_as_float(y.x);
+  p.n_logprobs = static_cast<int>(y.y);
+  p.seed = 0;
+  return p;
+}
+
+__device__ __forceinline__ int chunk_cost_class(const ts_row_params& p, int V, int max_logprobs) {
+  const int kind = row_kind(p, V, max_logprobs);
+  if (kind == KIND_BAD || kind == KIND_EXACT) return 3;  // the chunk pass skips them
+  if (kind == KIND_TOPP || kind == KIND_FULL) return 0;
+  return cand_target(kind, p, V) > 256 ? 1 : 2;
+}
+
+__global__ __launch_bounds__(OT) void order_rows_kernel(SamplerArgs a, FastLayout lay,
+                                                        uint8_t* __restrict__ ws) {
+  __shared__ int wsum[OT / kWave][4];
+  const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
+  const int rows = static_cast<int>(a.rows);
+  if (tid < 2) reinterpret_cast<int*>(ws + lay.off_ctr)[tid] = 0;
+  // Thread t takes rows [t * per, (t + 1) * per): counts per class, then a
+  // block-wide exclusive scan gives each class's slots in row order.
+  const int per = (rows + OT - 1) / OT;
+  const int r0 = tid * per, r1 = min(rows, r0 + per);
+  // Up to kKeep rows per thread keep their class in registers (one read of
+  // the parameters); beyond that the second loop reads them again.
+  constexpr int kKeep = 4;
+  int cls[kKeep];
+  int cnt[4] = {0, 0, 0, 0};
+  ts_row_params pk[kKeep];  // all issued before any is tested (rows >= 1)
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) pk[i] = load_filter_params(a.params + min(r0 + i, rows - 1));
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i)
+    cls[i] = r0 + i < r1 ? chunk_cost_class(pk[i], a.vocab, a.max_logprobs) : 3;
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) {
+    if (r0 + i >= r1) break;
+    cnt[0] += cls[i] == 0;
+    cnt[1] += cls[i] == 1;
+    cnt[2] += cls[i] == 2;
+    cnt[3] += cls[i] == 3;
+  }
+  for (int r = r0 + kKeep; r < r1; ++r) {
+    const int k = chunk_cost_class(load_filter_params(a.params + r), a.vocab, a.max_logprobs);
+    cnt[0] += k == 0;
+    cnt[1] += k == 1;
+    cnt[2] += k == 2;
+    cnt[3] += k == 3;
+  }
+  int incl[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    incl[k] = cnt[k];
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(incl[k], d, kWave);
+      if (lane_id >= d) incl[k] += t;
+    }
+    if (lane_id == kWave - 1) wsum[wave][k] = incl[k];
+  }
+  __syncthreads();
+  int pos[4], base = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int before = 0, total = 0;
+    for (int w = 0; w < OT / kWave; ++w) {
+      const int c = wsum[w][k];
+      before += w < wave ? c : 0;
+      total += c;
+    }
+    pos[k] = base + before + incl[k] - cnt[k];
+    base += total;
+  }
+  int* order = reinterpret_cast<int*>(ws + lay.off_order);
+  for (int r = r0; r < r1; ++r) {
+    int k = 3;
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i)
+      if (r == r0 + i) k = cls[i];
+    if (r >= r0 + kKeep) k = chunk_cost_class(load_filter_params(a.params + r), a.vocab, a.max_logprobs);
+    const int at = k == 0 ? pos[0]++ : (k == 1 ? pos[1]++ : (k == 2 ? pos[2]++ : pos[3]++));
+    order[at] = r;
+  }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLayout lay,
                                                         uint8_t* __restrict__ ws) {
   __shared__ ChunkSmem sh;
   const int S = lay.S;
-  const int bid = blockIdx.x;
-  const int r = bid / S, c = bid - r * S;
+  // Workgroup -> (row, chunk) through the row order; a chunk's records
+  // and lists sit at its own index bid = r * S + c.
+  const int wg = blockIdx.x / S, c = blockIdx.x - wg * S;
+  const int r = __builtin_amdgcn_readfirstlane(
+      reinterpret_cast<const int*>(ws + lay.off_order)[wg]);
+  const int bid = r * S + c;
   const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
-  if (bid == 0 && tid < 2) reinterpret_cast<int*>(ws + lay.off_ctr)[tid] = 0;
   // The chunk's loads go out first, so the parameter read and the row-kind
   // decision overlap them (rows the chunk pass skips waste one chunk read).
   const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
@@ -1452,13 +1563,14 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       return;
     }
     trim_and_sort(sh, nk, nk, 0u);
+    const int np = nk < kProbes ? nk : kProbes;
     if (tid == 0) {
       ProbeRec pr;
       pr.z = sh.z;
       pr.m = m;
       pr.lse = lse;
       pr.inv_t = inv_t;
-      pr.npts = nk < kProbes ? nk : kProbes;
+      pr.npts = np;
       for (int i = 0; i < kProbes; ++i) {
         const int id = i < pr.npts ? cand_id(sh.list[i]) : 0;
         pr.id[i] = id;
@@ -1577,6 +1689,7 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
            (cols[s] % 4 == 0);
   }
   const unsigned chunks = static_cast<unsigned>(a.rows) * static_cast<unsigned>(lay.S);
+  hipLaunchKernelGGL(order_rows_kernel, dim3(1), dim3(OT), 0, stream, a, lay, ws);
   if (vec)
     hipLaunchKernelGGL(chunk_pass_kernel<true>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
   else
