@@ -416,6 +416,30 @@ def test_sampler_topk2048_rows(dev, ts, p_top, route):
              res.row_status, res.flagged, lse, logits, label=f"topk2048/{p_top}")
 
 
+def test_sampler_many_rows_mixed_kinds(dev, ts, route):
+    """2,600 rows of every kind, interleaved (greedy, short and long top-k,
+    top-k beyond the fast route, top-p only, no filter, invalid parameters),
+    with a row offset: more rows than the chunk pass's row-order pre-pass
+    keeps in registers (it reads the remaining rows' parameters twice), so
+    its class counts, slots and second read are all exercised."""
+    rows, V = 2600, 3000
+    g = np.random.default_rng(2600)
+    logits = (g.standard_normal((rows, V)) * 1.3).astype(np.float32)
+    params = np.zeros(rows, dtype=workloads.PARAMS_DTYPE)
+    kinds = [(0.0, 0, 1.0), (0.8, 20, 1.0), (0.7, 700, 0.9), (0.9, 2500, 0.95), (1.0, 0, 0.85),
+             (0.6, 0, 1.0), (-1.0, 0, 1.0), (1.1, 50, 0.7), (0.5, 1, 1.0), (0.8, 0, 0.6)]
+    for r in range(rows):
+        t, k, p = kinds[(r * 7 + r // 13) % len(kinds)]
+        params[r] = (t, k, p, r % 6, 0)
+    params["seed"] = np.arange(rows, dtype=np.uint64) * np.uint64(0xD1B54A32D192ED03) + np.uint64(11)
+    say("sampler many rows", rows, V, route)
+    got = _run_sampler(ts, dev, logits, params, 77, 5)
+    res, lse = _oracle_ref(logits, params, 77, 5)
+    assert (res.row_status == 1).sum() == (params["temperature"] < 0).sum() > 0
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, label="many rows")
+
+
 def test_sampler_probes_outside_nucleus(dev, ts, route):
     """Top-p-only rows whose nucleus (about 120 of 200 raised logits) is past
     the listed head but holds only a tenth of the mass: the best Gumbel keys
