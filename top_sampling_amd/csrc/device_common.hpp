@@ -156,6 +156,32 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// One DPP move of a 64-bit value, as two 32-bit moves (same control).
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long old,
+                                                      unsigned long long src) {
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(old), static_cast<int>(src), CTRL, ROW_MASK, 0xF, BOUND_ZERO));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+      static_cast<int>(old >> 32), static_cast<int>(src >> 32), CTRL, ROW_MASK, 0xF, BOUND_ZERO));
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Maximum of a 64-bit value over the wave, uniform, by DPP (as
+// wave_max_uniform).  Every lane must be active.
+__device__ __forceinline__ unsigned long long wave_max_u64_uniform(unsigned long long v) {
+  unsigned long long t;
+  t = dpp_u64<0xB1, 0xF, false>(v, v);   v = t > v ? t : v;  // quad_perm [1,0,3,2]
+  t = dpp_u64<0x4E, 0xF, false>(v, v);   v = t > v ? t : v;  // quad_perm [2,3,0,1]
+  t = dpp_u64<0x124, 0xF, false>(v, v);  v = t > v ? t : v;  // row_ror:4
+  t = dpp_u64<0x128, 0xF, false>(v, v);  v = t > v ? t : v;  // row_ror:8
+  t = dpp_u64<0x142, 0xA, false>(v, v);  v = t > v ? t : v;  // row_bcast:15 into rows 1, 3
+  t = dpp_u64<0x143, 0xC, false>(v, v);  v = t > v ? t : v;  // row_bcast:31 into rows 2, 3
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), 63);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
 // The eight 8-lane group maxima of v, two order statistics of them, both
 // uniform: the return value is the smallest (eight lanes, one per group,
 // reach it) and `second` the second largest (two lanes of different groups

@@ -1069,6 +1069,46 @@ __device__ uint32_t list_mass_key(MergeSmem& sh, int U, uint32_t kmin, float m, 
 }
 
 
+// The n (<= kTopNSmall) largest entries of sh.list[0, U), largest first, into
+// sh.list[0, n): n rounds of a block-wide maximum below the previous round's
+// (the entries are unique: the low word is the inverted token id).  A round
+// costs about 1,600 cycles, trimming a list of a thousand or more entries by
+// radix selection and sorting the rest about 15,000: below 9 entries the
+// rounds are cheaper.
+constexpr int kTopNSmall = 8;
+
+__device__ void top_n_small(MergeSmem& sh, int U, int n) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  // The thread's entries (at most kListMax / BT) in registers, 0 past the list.
+  constexpr int kPer = kListMax / BT;
+  unsigned long long mine[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) mine[q] = tid + q * BT < U ? sh.list[tid + q * BT] : 0ull;
+  // Per round: the wave maximum by DPP, the four posted in one of two LDS
+  // slots (alternating, so one barrier per round suffices).
+  unsigned long long* post = sh.smass + kTopNSmall;  // [2][BW]
+  unsigned long long last = ~0ull;
+  for (int r = 0; r < n; ++r) {
+    unsigned long long best = 0ull;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      if (mine[q] < last && mine[q] > best) best = mine[q];
+    best = wave_max_u64_uniform(best);
+    if (lane == 0) post[(r & 1) * BW + w] = best;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < BW; ++q) {
+      const unsigned long long o = post[(r & 1) * BW + q];
+      best = o > best ? o : best;
+    }
+    if (tid == 0) sh.smass[r] = best;
+    last = best;
+  }
+  __syncthreads();
+  if (tid < n) sh.list[tid] = sh.smass[tid];
+  __syncthreads();
+}
+
 // Keeps the entries of sh.list[0, U) (all with key >= floor_key) that are at
 // least the need-th largest, plus whatever shares its radix bin when the list
 // is long (at most need + 64 entries, or the power of two the sort pads to,
@@ -1508,7 +1548,10 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   // Top-N log-probabilities (and the greedy token): the n_eff largest, sorted.
   if (!sorted && need > 192) {
     const int nt = n_eff > 1 ? n_eff : 1;
-    trim_and_sort(sh, U, nt < U ? nt : U, floor_key);
+    if (nt <= kTopNSmall && nt <= U)
+      top_n_small(sh, U, nt);
+    else
+      trim_and_sort(sh, U, nt < U ? nt : U, floor_key);
   }
   if (kind == KIND_GREEDY) token = cand_id(sh.list[0]);  // largest logit, lowest id
   if (proc && probe) {  // the kept mass lies beyond the listed logits
