@@ -27,10 +27,14 @@ constexpr int kTileStoreFloats = 32 * kTileStoreStride;
 // One wave writes its TM x TN accumulator blocks, block (i, j) covering rows
 // row0 + 32 i .. +31 and columns col0 + 32 j .. +31 of C (row-major, leading
 // dimension ldc, rows >= M and columns >= N dropped).  With SCALED, every value
-// is multiplied by row_scale[row] * col_scale[col] (that product first).  The
-// wave's scratch is lds + wave * kTileStoreFloats; every wave of the workgroup
-// must be past its last read of that LDS before any wave calls this.  Stores
-// are non-temporal; a ragged column tail falls back to 4-byte stores.
+// is multiplied by row_scale[row] * col_scale[col] (that product first); the
+// wave reads all the scales it needs up front, in one round trip, rather than
+// a few per block (one memory latency per block made the FP8 epilogue a third
+// of that kernel).  The wave's scratch is lds + wave * kTileStoreFloats; every
+// wave of the workgroup must be past its last read of that LDS before any
+// wave calls this.  The 16-byte row stores are ordinary (write-back) stores:
+// non-temporal ones were slower for the FP8 kernel and no faster for the bf16
+// one.  A ragged column tail falls back to 4-byte stores.
 template <bool SCALED, int TM, int TN, typename Acc>
 __device__ __forceinline__ void store_tile_rows(const Acc (&acc)[TM][TN], float* lds, int wave,
                                                 int lane, float* __restrict__ C, int64_t ldc,
@@ -42,6 +46,25 @@ __device__ __forceinline__ void store_tile_rows(const Acc (&acc)[TM][TN], float*
   float* scr = lds + wave * kTileStoreFloats;
   const int frow = lane & 31, fhalf = lane >> 5;
   const int c0 = (lane & 7) * 4;  // this lane's four columns within a block row
+  // Scales of this lane's rows (four per row block) and columns (four per
+  // column block); a column past N gets 0 (never stored), a row past M 1.
+  float rsv[TM][4], csv[TN][4];
+  if (SCALED) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = row0 + i * 32 + (lane >> 3) + 8 * q;
+        rsv[i][q] = row < M ? row_scale[row] : 1.0f;
+      }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int col = col0 + j * 32 + c0 + t;
+        csv[j][t] = col < N ? col_scale[col] : 0.0f;
+      }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -57,11 +80,6 @@ __device__ __forceinline__ void store_tile_rows(const Acc (&acc)[TM][TN], float*
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int col = col0 + j * 32 + c0;
-      f32x4v cs = {1.0f, 1.0f, 1.0f, 1.0f};
-      if (SCALED) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) cs[t] = col + t < N ? col_scale[col + t] : 0.0f;
-      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rr = (lane >> 3) + 8 * q;
@@ -69,17 +87,16 @@ __device__ __forceinline__ void store_tile_rows(const Acc (&acc)[TM][TN], float*
         f32x4v v = *reinterpret_cast<const f32x4v*>(scr + rr * SP + c0);
         if (row >= M || col >= N) continue;
         if (SCALED) {
-          const float rs = row_scale[row];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] = v[t] * (rs * cs[t]);
+          for (int t = 0; t < 4; ++t) v[t] = v[t] * (rsv[i][q] * csv[j][t]);
         }
         float* dst = C + static_cast<int64_t>(row) * ldc + col;
         if (col + 3 < N) {
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4v*>(dst));
+          *reinterpret_cast<f32x4v*>(dst) = v;
         } else {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
-            if (col + t < N) __builtin_nontemporal_store(v[t], dst + t);
+            if (col + t < N) dst[t] = v[t];
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
