@@ -305,10 +305,20 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void lmhead_gemm_dl_kern
   }
 
   if (vec_out) {
-    __syncthreads();  // every wave is done reading the stage buffers
-    static_assert(NW * kTileStoreFloats * 4 <= 2 * STAGE, "tile-store scratch fits the stages");
-    store_tile_rows<false>(acc, reinterpret_cast<float*>(lds), wave, lane, C, ldc, m0 + wm0,
-                           n0 + wn0, M, N, nullptr, nullptr);
+    // Scratch in the stage buffer the last step did not use, when one buffer
+    // holds every wave's: every wave was done reading it at that step's
+    // barrier and nothing was loaded into it, so each wave starts its
+    // epilogue as soon as its own MFMAs are issued.  Otherwise the scratch
+    // spans both buffers, after a barrier.
+    if constexpr (NW * kTileStoreFloats * 4 <= STAGE) {
+      store_tile_rows<false>(acc, reinterpret_cast<float*>(lds + (((ksteps - 1) & 1) ^ 1) * STAGE),
+                             wave, lane, C, ldc, m0 + wm0, n0 + wn0, M, N, nullptr, nullptr);
+    } else {
+      static_assert(NW * kTileStoreFloats * 4 <= 2 * STAGE, "tile-store scratch fits the stages");
+      __syncthreads();  // every wave is done reading the stage buffers
+      store_tile_rows<false>(acc, reinterpret_cast<float*>(lds), wave, lane, C, ldc, m0 + wm0,
+                             n0 + wn0, M, N, nullptr, nullptr);
+    }
     return;
   }
 #pragma unroll
