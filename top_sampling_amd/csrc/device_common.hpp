@@ -67,6 +67,15 @@ __device__ __forceinline__ U32x4 token_words(uint64_t seed, uint64_t row, uint32
                        static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
 }
 
+// Word q (0..3, known only at run time) of a Philox block, by selects: an
+// indexed read of the four-word array would go through per-lane scratch
+// memory, a store and a load in every call.
+__device__ __forceinline__ uint32_t word_at(const U32x4& w, int q) {
+  const uint32_t lo = (q & 1) ? w.v[1] : w.v[0];
+  const uint32_t hi = (q & 1) ? w.v[3] : w.v[2];
+  return (q & 2) ? hi : lo;
+}
+
 // Standard Gumbel noise from one 32-bit word: u = ((x >> 9) + 1/2) * 2^-23 is
 // exact in fp32 and lies in [2^-24, 1 - 2^-24]; g = -ln(-ln u).  Both
 // logarithms use the hardware base-2 logarithm (v_log_f32) scaled by ln 2:
@@ -177,6 +186,22 @@ __device__ __forceinline__ unsigned long long wave_max_u64_uniform(unsigned long
   t = dpp_u64<0x128, 0xF, false>(v, v);  v = t > v ? t : v;  // row_ror:8
   t = dpp_u64<0x142, 0xA, false>(v, v);  v = t > v ? t : v;  // row_bcast:15 into rows 1, 3
   t = dpp_u64<0x143, 0xC, false>(v, v);  v = t > v ? t : v;  // row_bcast:31 into rows 2, 3
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), 63);
+  return (static_cast<unsigned long long>(hi) << 32) | lo;
+}
+
+// Sum of a 64-bit value over the wave, uniform: the moves of
+// wave_max_u64_uniform, with lanes outside a move's row mask adding zero
+// (a sum, unlike a maximum, must not take a lane's own value twice).
+// Every lane must be active.
+__device__ __forceinline__ unsigned long long wave_sum_u64_uniform(unsigned long long v) {
+  v += dpp_u64<0xB1, 0xF, false>(0ull, v);   // quad_perm [1,0,3,2]
+  v += dpp_u64<0x4E, 0xF, false>(0ull, v);   // quad_perm [2,3,0,1]
+  v += dpp_u64<0x124, 0xF, false>(0ull, v);  // row_ror:4
+  v += dpp_u64<0x128, 0xF, false>(0ull, v);  // row_ror:8: every lane holds its row's sum
+  v += dpp_u64<0x142, 0xA, false>(0ull, v);  // row_bcast:15: rows 1, 3 add rows 0, 2
+  v += dpp_u64<0x143, 0xC, false>(0ull, v);  // row_bcast:31: rows 2, 3 add rows 0 + 1
   const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(v), 63);
   const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(v >> 32), 63);
   return (static_cast<unsigned long long>(hi) << 32) | lo;

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(256) void gumbel_keys_kernel(
   const uint64_t seed = seeds[i], row = static_cast<uint64_t>(rows[i]);
   if (words) {
     const U32x4 w = token_words(seed, row, static_cast<uint32_t>(id) >> 2);
-    words[i] = w.v[id & 3];
+    words[i] = word_at(w, id & 3);
   }
   if (keys) keys[i] = gumbel_key(logits[i], row_max[i], 1.0f / temperature[i], seed, row, id);
 }

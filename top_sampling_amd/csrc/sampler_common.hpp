@@ -96,7 +96,7 @@ __device__ __forceinline__ int cand_id(unsigned long long c) {
 __device__ __forceinline__ float gumbel_key(float l, float m, float inv_t, uint64_t seed,
                                             uint64_t grow, int id) {
   const U32x4 w = token_words(seed, grow, static_cast<uint32_t>(id) >> 2);
-  return (l - m) * inv_t + gumbel_from_word(w.v[id & 3]);
+  return (l - m) * inv_t + gumbel_from_word(word_at(w, id & 3));
 }
 
 // ------------------------------------------------------------ workspace layout

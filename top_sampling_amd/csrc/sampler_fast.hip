@@ -764,6 +764,11 @@ struct MergeSmem {
     ChunkRec recs[kMaxChunks];     // read once at the start of the merge
     uint32_t hist[RB];             // radix bins (counts), used afterwards
     unsigned long long mhist[RB];  // radix bins (fixed-point mass)
+    struct {                       // a top-k row's in-list probes (no radix round runs then)
+      unsigned long long key[kProbes];         // best Gumbel keys, packed with the ids
+      uint32_t logit[kProbes];                 // their logits' order keys
+      unsigned long long psum[BW][kProbes + 1];  // per-wave mass sums
+    } pr;
   };
   int nkey[kMaxChunks];         // the chunks' Gumbel-key list lengths
   int pos[kMaxChunks + 1];
@@ -782,6 +787,10 @@ struct MergeSmem {
   uint32_t floor_key;
   double z;
 };
+// Three merge workgroups share a CU at this size; 384 bytes more (53,824)
+// left room for only two, measured as 6-8 us more per merge call.
+static_assert(sizeof(MergeSmem) <= 53440, "three merge workgroups per CU");
+
 
 __device__ __forceinline__ void push_row(int* ctr, int* list, int r) { list[atomicAdd(ctr, 1)] = r; }
 
@@ -1069,44 +1078,157 @@ __device__ uint32_t list_mass_key(MergeSmem& sh, int U, uint32_t kmin, float m, 
 }
 
 
-// The n (<= kTopNSmall) largest entries of sh.list[0, U), largest first, into
-// sh.list[0, n): n rounds of a block-wide maximum below the previous round's
-// (the entries are unique: the low word is the inverted token id).  A round
-// costs about 1,600 cycles, trimming a list of a thousand or more entries by
-// radix selection and sorting the rest about 15,000: below 9 entries the
-// rounds are cheaper.
-constexpr int kTopNSmall = 8;
-
-__device__ void top_n_small(MergeSmem& sh, int U, int n) {
+// The n (1 <= n <= 64) largest of the nonzero 64-bit values the threads hold
+// in registers (P per thread, 0 for none, all distinct), largest first, into
+// out[0, ...), with each one's 32-bit payload into out_pay when PAY.  A lower
+// bound of the n-th largest comes from the waves: each has ceil(n / 4)
+// threads whose largest value reaches its own bound (built on the top 16 bits
+// of the high word, one ballot per bit), so at least n values reach the
+// smallest of the four bounds.  The values at or above it are gathered and
+// ranked directly.  Returns the number written, min(n, #values), or -1 when
+// more than BT values reach the bound (nothing written: the caller takes
+// another route).  A few thousand cycles where rounds of a block maximum
+// cost about 1,600 each.  Scratch: sh.smass, sh.skey, sh.ru, sh.nsmall.
+// Every thread of the block calls it; out may be sh.list, since the values
+// are in registers by then.
+template <int P, bool PAY>
+__device__ int top_n_regs(const unsigned long long (&v)[P], const uint32_t (&pay)[P], int n,
+                          unsigned long long* out, uint32_t* out_pay, MergeSmem& sh) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
-  // The thread's entries (at most kListMax / BT) in registers, 0 past the list.
-  constexpr int kPer = kListMax / BT;
-  unsigned long long mine[kPer];
+  unsigned long long mx = 0ull;
 #pragma unroll
-  for (int q = 0; q < kPer; ++q) mine[q] = tid + q * BT < U ? sh.list[tid + q * BT] : 0ull;
-  // Per round: the wave maximum by DPP, the four posted in one of two LDS
-  // slots (alternating, so one barrier per round suffices).
-  unsigned long long* post = sh.smass + kTopNSmall;  // [2][BW]
-  unsigned long long last = ~0ull;
-  for (int r = 0; r < n; ++r) {
-    unsigned long long best = 0ull;
+  for (int q = 0; q < P; ++q) mx = v[q] > mx ? v[q] : mx;
+  const int qn = (n + BW - 1) / BW;
+  const uint32_t mh = static_cast<uint32_t>(mx >> 32);
+  uint32_t K = 0u;
 #pragma unroll
-    for (int q = 0; q < kPer; ++q)
-      if (mine[q] < last && mine[q] > best) best = mine[q];
-    best = wave_max_u64_uniform(best);
-    if (lane == 0) post[(r & 1) * BW + w] = best;
-    __syncthreads();
+  for (int b = 31; b >= 16; --b) {
+    const uint32_t cand = K | (1u << b);
+    if (__popcll(__ballot(mh >= cand)) >= qn) K = cand;
+  }
+  if (lane == 0) sh.ru[w] = K;
+  if (tid == 0) sh.nsmall = 0;
+  __syncthreads();
+  uint32_t t = sh.ru[0];
 #pragma unroll
-    for (int q = 0; q < BW; ++q) {
-      const unsigned long long o = post[(r & 1) * BW + q];
-      best = o > best ? o : best;
+  for (int j = 1; j < BW; ++j) t = min(t, sh.ru[j]);
+  const unsigned long long tb = static_cast<unsigned long long>(t) << 32;
+  // Gathered one atomic per wave: the count from a ballot, each lane's
+  // offset from mbcnt (every lane is active here).
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    const bool keep = v[q] != 0ull && v[q] >= tb;
+    const unsigned long long bal = __ballot(keep);
+    if (bal == 0ull) continue;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&sh.nsmall, __popcll(bal));
+    base = __builtin_amdgcn_readfirstlane(base);
+    const int slot = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                static_cast<uint32_t>(bal >> 32),
+                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
+    if (keep && slot < BT) {
+      sh.smass[slot] = v[q];
+      if (PAY) sh.skey[slot] = pay[q];
     }
-    if (tid == 0) sh.smass[r] = best;
-    last = best;
   }
   __syncthreads();
-  if (tid < n) sh.list[tid] = sh.smass[tid];
+  const int C = sh.nsmall;
+  if (C > BT) {
+    __syncthreads();
+    return -1;
+  }
+  const int nn = n < C ? n : C;
+  if (tid < C) {
+    const unsigned long long x = sh.smass[tid];
+    int rank = 0;
+    for (int j = 0; j < C; ++j) rank += sh.smass[j] > x ? 1 : 0;
+    if (rank < nn) {
+      out[rank] = x;
+      if (PAY) out_pay[rank] = sh.skey[tid];
+    }
+  }
   __syncthreads();
+  return nn;
+}
+
+// Top-p over a long top-k list without locating the boundary.  The list's
+// best few Gumbel keys over the entries at or above the k-th key (kmin) are
+// taken in key order; token v is kept iff the entries with a larger logit
+// carry less than p times the top-k mass, which is exactly the set the
+// boundary search keeps (its boundary is the largest key whose entries at
+// or above it reach that mass).  The first kept one is therefore the
+// Gumbel-max winner over the kept set.  Masses in the same 2^-40 fixed point
+// and compared in the same double arithmetic as the boundary search, so the
+// decision is the same.  Returns the winner's id, or -1 when none of the
+// probes is kept or the list is longer than kRegList (then the caller
+// searches the boundary).
+constexpr int kRegList = 2048;  // list entries the register routines take (8 per thread)
+
+__device__ int topk_probe_winner(MergeSmem& sh, int U, uint32_t kmin, float m, float inv_t,
+                                 float top_p, uint64_t seed, uint64_t grow) {
+  constexpr int P = kRegList / BT;
+  if (U > kRegList) return -1;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  unsigned long long gk[P], wm[P];
+  uint32_t lk[P];
+  unsigned long long tot = 0ull;
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    gk[q] = 0ull;
+    wm[q] = 0ull;
+    lk[q] = 0u;
+    const int i = tid + q * BT;
+    if (q * BT < U && i < U) {
+      const unsigned long long e = sh.list[i];
+      const uint32_t key = cand_key(e);
+      if (key >= kmin) {
+        const int id = cand_id(e);
+        gk[q] = pack_cand(order_key(gumbel_key(key_to_float(key), m, inv_t, seed, grow, id)), id);
+        lk[q] = key;
+        wm[q] = list_mass(key, m, inv_t);
+        tot += wm[q];
+      }
+    }
+  }
+  const int np = top_n_regs<P, true>(gk, lk, kProbes, sh.pr.key, sh.pr.logit, sh);
+  if (np <= 0) return -1;
+  uint32_t pl[kProbes];
+#pragma unroll
+  for (int j = 0; j < kProbes; ++j) pl[j] = j < np ? sh.pr.logit[j] : 0xffffffffu;
+  unsigned long long acc[kProbes];
+#pragma unroll
+  for (int j = 0; j < kProbes; ++j) acc[j] = 0ull;
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    if (q * BT >= U) continue;
+#pragma unroll
+    for (int j = 0; j < kProbes; ++j) acc[j] += lk[q] > pl[j] ? wm[q] : 0ull;
+  }
+#pragma unroll
+  for (int j = 0; j < kProbes; ++j) acc[j] = wave_sum_u64_uniform(acc[j]);
+  tot = wave_sum_u64_uniform(tot);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < kProbes; ++j) sh.pr.psum[w][j] = acc[j];
+    sh.pr.psum[w][kProbes] = tot;
+  }
+  __syncthreads();
+  unsigned long long all = 0ull;
+#pragma unroll
+  for (int x = 0; x < BW; ++x) all += sh.pr.psum[x][kProbes];
+  const double target = static_cast<double>(top_p) * static_cast<double>(all);
+  int id = -1;
+  for (int j = 0; j < np; ++j) {
+    unsigned long long a = 0ull;
+#pragma unroll
+    for (int x = 0; x < BW; ++x) a += sh.pr.psum[x][j];
+    if (static_cast<double>(a) < target) {
+      id = cand_id(sh.pr.key[j]);
+      break;
+    }
+  }
+  __syncthreads();
+  return id;
 }
 
 // Keeps the entries of sh.list[0, U) (all with key >= floor_key) that are at
@@ -1412,13 +1534,24 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   // sets stay unsorted: the k-th key and the top-p boundary are found by
   // count- and mass-weighted radix selection (sorting a list of a few
   // thousand entries in one workgroup costs several times more).
-  bool sorted = need <= 192;
+  // A top-p-only row whose listed logits carry less than p times the row's
+  // mass has its boundary below the list: it goes to the probe pass without
+  // sorting its head (only its top N are needed here).
+  bool early_probe = false;
+  if (kind == KIND_TOPP && need <= 192) {
+    double wsum = 0.0;
+    for (int i = tid; i < U; i += BT)
+      wsum += static_cast<double>(fast_exp((key_to_float(cand_key(sh.list[i])) - m) * inv_t));
+    const double wlist = block_sum<BT, double>(wsum, sh.dscan);
+    early_probe = (force & 1) || wlist < static_cast<double>(p.top_p) * sh.z;
+  }
+  bool sorted = need <= 192 && !early_probe;
   if (sorted) {
     U = trim_and_sort(sh, U, need < U ? need : U, floor_key);
     sorted = U <= BT;  // long tie runs keep more: those rows take the selection path
   }
   int token = -1;
-  bool probe = false;
+  bool probe = early_probe;
   // The kept set's smallest key and its temperature-scaled mass (for the
   // processed log-probabilities).
   uint32_t kept_key = 0u;
@@ -1486,10 +1619,14 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       block_best<BT>(gk, gi, sh.rf, sh.ri);
       token = gi;
     }
-  } else if (kind == KIND_TOPK || kind == KIND_TOPP) {
+  } else if (!early_probe && (kind == KIND_TOPK || kind == KIND_TOPP)) {
     const uint32_t kmin = kind == KIND_TOPK ? list_kth_key(sh, U, p.top_k, floor_key) : 0u;
     uint32_t kept = kmin;
-    if (p.top_p < 1.0f) {
+    // Top-k with top-p, plain log-probabilities: the list's best Gumbel keys
+    // settle most rows without the boundary search.
+    if (kind == KIND_TOPK && p.top_p < 1.0f && !proc)
+      token = topk_probe_winner(sh, U, kmin, m, inv_t, p.top_p, p.seed, grow);
+    if (token < 0 && p.top_p < 1.0f) {
       double target;
       if (kind == KIND_TOPK) {
         unsigned long long mine = 0ull;
@@ -1519,7 +1656,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       }
     }
     kept_key = kept;
-    if (proc && !probe) {
+    if (proc && !probe) {  // (no probe winner: proc rows never take that route)
       unsigned long long mk = 0ull;
       for (int i = tid; i < U; i += BT) {
         const uint32_t key = cand_key(sh.list[i]);
@@ -1527,7 +1664,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       }
       zk = static_cast<double>(block_sum<BT, unsigned long long>(mk, sh.uscan)) * kMassUnit;
     }
-    if (!probe) {
+    if (!probe && token < 0) {
       float gk = -INFINITY;
       int gi = 0x7fffffff;
       for (int i = tid; i < U; i += BT) {
@@ -1546,12 +1683,21 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   }
 
   // Top-N log-probabilities (and the greedy token): the n_eff largest, sorted.
-  if (!sorted && need > 192) {
+  if (!sorted && (need > 192 || early_probe)) {
     const int nt = n_eff > 1 ? n_eff : 1;
-    if (nt <= kTopNSmall && nt <= U)
-      top_n_small(sh, U, nt);
-    else
-      trim_and_sort(sh, U, nt < U ? nt : U, floor_key);
+    int got = -1;
+    if (nt <= 64 && U <= kRegList) {
+      constexpr int kPer = kRegList / BT;
+      unsigned long long mine[kPer];
+      uint32_t none[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        mine[q] = tid + q * BT < U ? sh.list[tid + q * BT] : 0ull;
+        none[q] = 0u;
+      }
+      got = top_n_regs<kPer, false>(mine, none, nt, sh.list, nullptr, sh);
+    }
+    if (got < 0) trim_and_sort(sh, U, nt < U ? nt : U, floor_key);
   }
   if (kind == KIND_GREEDY) token = cand_id(sh.list[0]);  // largest logit, lowest id
   if (proc && probe) {  // the kept mass lies beyond the listed logits
@@ -1605,7 +1751,19 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       if (tid == 0) push_row(&ctr[0], exact_list, r);
       return;
     }
-    trim_and_sort(sh, nk, nk, 0u);
+    int got = -1;
+    if (nk <= kRegList) {
+      constexpr int kPer = kRegList / BT;
+      unsigned long long mine[kPer];
+      uint32_t none[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        mine[q] = tid + q * BT < nk ? sh.list[tid + q * BT] : 0ull;
+        none[q] = 0u;
+      }
+      got = top_n_regs<kPer, false>(mine, none, kProbes, sh.list, nullptr, sh);
+    }
+    if (got < 0) trim_and_sort(sh, nk, nk, 0u);
     const int np = nk < kProbes ? nk : kProbes;
     if (tid == 0) {
       ProbeRec pr;
