@@ -109,6 +109,7 @@ constexpr int kChunkVec = 16;     // float4 per thread
 constexpr int kChunkMax = kChunkThreads * kChunkVec * 4;  // 16384 logits
 constexpr int kListMax = 4096;    // merged candidates a row may keep in LDS
 constexpr float kKeyMargin = 1e-4f;  // rounding margin between chunk-local and row keys
+constexpr float kLnKeysPerChunk = 3.17805383f;  // ln 24: a top-p chunk's expected key count at most 24
 
 struct ChunkRec {  // one per (row, chunk); 64 bytes
   float cmax;      // chunk maximum

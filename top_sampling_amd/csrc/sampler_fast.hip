@@ -113,13 +113,18 @@ __device__ __forceinline__ uint32_t lds_kth_largest(const uint32_t* keys, int nk
 }
 
 // ------------------------------------------------------------------ A: chunks
+// Tokens of a top-p-only row whose uniform may lift them over the key bar,
+// queued per wave (at most kQueueCap; drained when a float4 step could fill it).
+constexpr int kQueueCap = 320;
+
 struct ChunkSmem {
   uint32_t hist[RB];
   uint32_t keys4[4 * AT];  // per-thread top-4 keys (block-level selection)
   int klist[kKeyCap];
   float wthr[AW];
-  float wbar[AW];
-  float wsec[AW];  // posted second-largest group maxima (top-p key bars)
+  float qx[AW][kQueueCap];     // x = (l - cmax) / T
+  uint32_t qw[AW][kQueueCap];  // the token's Philox word
+  uint16_t qe[AW][kQueueCap];  // its index in the chunk
   float rm[AW], rs[AW], rt[AW];
   int rb[AW];
   float rf[AW];
@@ -283,141 +288,139 @@ __device__ __forceinline__ uint32_t u_floor_bits(float xm, float bar) {
   return th > 0.0f ? static_cast<uint32_t>(th) : 0u;
 }
 
-__device__ __forceinline__ void insert3(float key, int id, float (&k)[3], int (&i)[3]) {
-  if (!better(key, id, k[2], i[2])) return;
-  if (better(key, id, k[1], i[1])) {
-    k[2] = k[1];
-    i[2] = i[1];
-    if (better(key, id, k[0], i[0])) {
-      k[1] = k[0];
-      i[1] = i[0];
-      k[0] = key;
-      i[0] = id;
-    } else {
-      k[1] = key;
-      i[1] = id;
-    }
-  } else {
-    k[2] = key;
-    i[2] = id;
-  }
-}
-
 // ------------------------------------------------------------- Gumbel keys
-// Gumbel keys of one chunk of a full-vocabulary or top-p-only row, drawn by
-// the chunk pass from the logits in its registers, relative to the chunk
-// maximum: x = (l - cmax) / T, key = x + g.  Full rows list the chunk's best
-// key (floor: that key); top-p-only rows list every key at or above the
-// floor.  Every thread of the workgroup calls it, with sh.nkey zero and
-// sh.wsec all -inf.  Returns the number of keys (above kKeyCap: overflow, the
-// list is not written).
-__device__ __forceinline__ int chunk_keys(const float4 (&v)[AV], float cmax, float inv_t, bool topp,
-                                          uint64_t seed, uint64_t grow, int c0,
-                                          int* __restrict__ klist_out, ChunkSmem& sh,
-                                          float& kfloor) {
-  const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
-  kfloor = INFINITY;
-  {
-    // Full rows keep each thread's best key; the chunk maximum's key is at
-    // least the smallest Gumbel value, so no token below that bar needs its
-    // noise.  Top-p-only rows keep each thread's best three.  The bar a token
-    // must clear is the larger of the thread's own (its best, or its third
-    // best) and the wave's, refreshed after five of the sixteen float4s: for
-    // full rows the wave's largest best key (a token under it cannot be the
-    // chunk's best); for top-p rows a value eight keys of the chunk reach,
-    // the larger of two: the smallest of the wave's eight 8-lane group
-    // maxima of the best keys, and the smallest of the second-largest group
-    // maxima the four waves have posted in LDS (two keys per wave; a stale
-    // or missing post is lower, so it still holds).  The top-p key floor
-    // below is raised to every wave's bar, so a token skipped under a bar is
-    // under the floor and the key list above the floor stays complete; whole
-    // waves skip the Gumbel draw once a few good keys are known.
-    float kb[3] = {-INFINITY, -INFINITY, -INFINITY};
-    int ib[3] = {0x7fffffff, 0x7fffffff, 0x7fffffff};
-    float wbar = topp ? -INFINITY : kMinGumbel;
-    volatile float* posted = sh.wsec;
+// Best Gumbel key of one chunk of a full-vocabulary row, drawn by the chunk
+// pass from the logits in its registers, relative to the chunk maximum:
+// x = (l - cmax) / T, key = x + g.  A token needs its noise only if its
+// key can clear the bar: the larger of the thread's best key so far and the
+// wave's, refreshed after five of the sixteen float4s (the chunk maximum's
+// key is at least the smallest Gumbel value, the bar's start).  Every
+// thread of the workgroup calls it, with sh.nkey zero.  Returns the number
+// of keys listed (1, or 0 for an all-padding chunk); kfloor is the key.
+__device__ __forceinline__ int chunk_best_key(const float4 (&v)[AV], float cmax, float inv_t,
+                                              uint64_t seed, uint64_t grow, int c0,
+                                              int* __restrict__ klist_out, ChunkSmem& sh,
+                                              float& kfloor) {
+  const int tid = threadIdx.x;
+  float kb = -INFINITY;
+  int ib = 0x7fffffff;
+  float wbar = kMinGumbel;
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
-      const int e = 4 * (j * AT + tid);
-      float x[4];
+  for (int j = 0; j < AV; ++j) {
+    const int e = 4 * (j * AT + tid);
+    float x[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = (lane(v[j], q) - cmax) * inv_t;
-      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      const float bar = fmaxf(wbar, topp ? kb[2] : kb[0]);
-      if (xm + kGumbelMax >= bar) {  // else no key here can clear the bar (or all padding)
-        const uint32_t th = u_floor_bits(xm, bar);
-        const U32x4 w = token_words(seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
+    for (int q = 0; q < 4; ++q) x[q] = (lane(v[j], q) - cmax) * inv_t;
+    const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    const float bar = fmaxf(wbar, kb);
+    if (xm + kGumbelMax >= bar) {  // else no key here can clear the bar (or all padding)
+      const uint32_t th = u_floor_bits(xm, bar);
+      const U32x4 w = token_words(seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          if ((w.v[q] >> 9) < th || x[q] == -INFINITY) continue;
-          const float key = x[q] + gumbel_from_word(w.v[q]);
-          const int id = c0 + e + q;
-          if (topp) {
-            insert3(key, id, kb, ib);
-          } else if (better(key, id, kb[0], ib[0])) {
-            kb[0] = key;
-            ib[0] = id;
-          }
-        }
-      }
-      // Refreshed early and then less often: the bar rises fastest at first.
-      if (j == 0 || j == 1 || j == 3 || j == 7 || j == 11) {
-        if (topp) {
-          float second;
-          const float own = wave_group_floors(kb[0], second);
-          if (lane_id == 0) posted[wave] = second;
-          float b = posted[0];
-#pragma unroll
-          for (int w = 1; w < AW; ++w) b = fminf(b, posted[w]);
-          wbar = fmaxf(wbar, fmaxf(own, uniform_f32(b)));
-        } else {
-          wbar = fmaxf(wbar, wave_max_uniform(kb[0]));
+      for (int q = 0; q < 4; ++q) {
+        if ((w.v[q] >> 9) < th || x[q] == -INFINITY) continue;
+        const float key = x[q] + gumbel_from_word(w.v[q]);
+        const int id = c0 + e + q;
+        if (better(key, id, kb, ib)) {
+          kb = key;
+          ib = id;
         }
       }
     }
-    if (!topp) {
-      float k1 = kb[0];
-      int i1 = ib[0];
-      block_best<AT>(k1, i1, sh.rf, sh.ri);
-      if (tid == 0 && i1 != 0x7fffffff) {
-        klist_out[0] = i1;
-        sh.nkey = 1;
-      }
-      kfloor = k1;
-    } else {
-      // Floor F >= every thread's third-best key, so the tokens with key >=
-      // F all sit in the threads' top-three lists, and F >= every wave's
-      // final bar, so no skipped token lies at or above it.  F is also raised
-      // to the smallest of the four waves' third-largest best keys to keep
-      // the list short (at least twelve entries when that raises it, eight
-      // when a wave's bar does).
-      const float f0 = block_max<AT>(kb[2], sh.rf);
-      const float tw = wave_qth(kb[0], 3);
-      if (lane_id == 0) {
-        sh.wthr[wave] = tw;
-        sh.wbar[wave] = wbar;
-      }
-      __syncthreads();
-      float g = sh.wthr[0], wb = sh.wbar[0];
-#pragma unroll
-      for (int w = 1; w < AW; ++w) {
-        g = fminf(g, sh.wthr[w]);
-        wb = fmaxf(wb, sh.wbar[w]);
-      }
-      kfloor = fmaxf(fmaxf(f0, g), wb);
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        if (ib[i] != 0x7fffffff && kb[i] >= kfloor) {
-          const int slot = atomicAdd(&sh.nkey, 1);
-          if (slot < kKeyCap) sh.klist[slot] = ib[i];
-        }
-      }
-      __syncthreads();
-      if (sh.nkey <= kKeyCap && tid < sh.nkey) klist_out[tid] = sh.klist[tid];
-    }
+    // Refreshed early and then less often: the bar rises fastest at first.
+    if (j == 0 || j == 1 || j == 3 || j == 7 || j == 11) wbar = fmaxf(wbar, wave_max_uniform(kb));
   }
+  block_best<AT>(kb, ib, sh.rf, sh.ri);
+  if (tid == 0 && ib != 0x7fffffff) {
+    klist_out[0] = ib;
+    sh.nkey = 1;
+  }
+  kfloor = kb;
   __syncthreads();
   return sh.nkey;
+}
+
+// Gumbel keys of one chunk of a top-p-only row, relative to the chunk
+// maximum as above.  The chunk lists every key at or above the bar
+// B = ln(sum of exp x over the chunk) - ln 24.  A token reaches B with
+// probability 1 - exp(-exp(x - B)) <= exp(x - B), so at most 24 keys do on
+// average; their count is a sum of independent draws, so more than the
+// list's 64 has odds below 1e-10 and none at all e^-24 (the merge's floor
+// is the highest chunk bar, so the row's union holds about 24 keys or more).
+// A token is tested with a floor on its uniform from the largest x of its
+// float4; the few that pass are queued per wave in LDS and their keys
+// computed together, so a wave runs the two logarithms once per 64 queued
+// tokens rather than whenever one lane's token passes.  Every thread of the
+// workgroup calls it, with sh.nkey zero.  Returns the number of keys (above
+// kKeyCap: overflow, the list is not written); kfloor = B.
+__device__ __forceinline__ int chunk_keys_topp(const float4 (&v)[AV], float cmax, float inv_t,
+                                               float tmass, uint64_t seed, uint64_t grow, int c0,
+                                               int* __restrict__ klist_out, ChunkSmem& sh,
+                                               float& kfloor) {
+  const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
+  const float bar = uniform_f32(__builtin_amdgcn_logf(tmass) * kLn2 - kLnKeysPerChunk);
+  kfloor = bar;
+  float* qx = sh.qx[wave];
+  uint32_t* qw = sh.qw[wave];
+  uint16_t* qe = sh.qe[wave];
+  int qn = 0;  // the wave's queue length (uniform)
+  // Lanes read what other lanes wrote: each drain is fenced at wavefront
+  // scope before (the writes are seen) and after (later writes cannot
+  // overtake the reads).
+  auto drain = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int i = lane_id; i < qn; i += kWave) {
+      if (qx[i] + gumbel_from_word(qw[i]) >= bar) {
+        const int slot = atomicAdd(&sh.nkey, 1);
+        if (slot < kKeyCap) sh.klist[slot] = c0 + qe[i];
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    qn = 0;
+  };
+#pragma unroll
+  for (int j = 0; j < AV; ++j) {
+    if (qn > kQueueCap - 4 * kWave) drain();
+    const int e = 4 * (j * AT + tid);
+    float x[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[q] = (lane(v[j], q) - cmax) * inv_t;
+    const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    uint32_t wq[4] = {0u, 0u, 0u, 0u};
+    bool pass[4] = {false, false, false, false};
+    if (xm + kGumbelMax >= bar) {  // else no key here can reach the bar (or all padding)
+      const uint32_t th = u_floor_bits(xm, bar);
+      const U32x4 w = token_words(seed, grow, static_cast<uint32_t>(c0 + e) >> 2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wq[q] = w.v[q];
+        pass[q] = (w.v[q] >> 9) >= th && x[q] != -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const unsigned long long bal = __ballot(pass[q]);
+      if (bal == 0ull) continue;
+      if (pass[q]) {
+        const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                  static_cast<uint32_t>(bal >> 32),
+                                  __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
+        qx[slot] = x[q];
+        qw[slot] = wq[q];
+        qe[slot] = static_cast<uint16_t>(e + q);
+      }
+      qn += __popcll(bal);
+    }
+  }
+  drain();
+  __syncthreads();
+  const int nk = sh.nkey;
+  if (nk <= kKeyCap && tid < nk) klist_out[tid] = sh.klist[tid];
+  return nk;
 }
 
 // ------------------------------------------------------------- row order
@@ -649,7 +652,6 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     sh.ncand = 0;
     sh.nkey = 0;
   }
-  if (tid < AW) sh.wsec[tid] = -INFINITY;
   // Logit candidate threshold tf: at least M logits of the chunk are >= tf.
   // M <= 64: every wave holds ceil(M/4) per-thread maxima >= its own q-th
   // largest, so the smallest of the four wave values works.  64 < M <= 256:
@@ -735,8 +737,10 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   float kfloor = INFINITY;
   if ((kind == KIND_FULL || kind == KIND_TOPP) && !ovf) {
     int* klist_out = reinterpret_cast<int*>(ws + lay.off_key) + static_cast<size_t>(bid) * kKeyCap;
-    nkey = chunk_keys(v, cmax, inv_t, kind == KIND_TOPP, p.seed,
-                      static_cast<uint64_t>(a.row_offset + r), c0, klist_out, sh, kfloor);
+    const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
+    nkey = kind == KIND_TOPP
+               ? chunk_keys_topp(v, cmax, inv_t, tmass, p.seed, grow, c0, klist_out, sh, kfloor)
+               : chunk_best_key(v, cmax, inv_t, p.seed, grow, c0, klist_out, sh, kfloor);
   }
   if (tid == 0) {
     const bool key_ovf = nkey > kKeyCap;
