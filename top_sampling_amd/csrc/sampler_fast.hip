@@ -1775,12 +1775,34 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       pr.m = m;
       pr.lse = lse;
       pr.inv_t = inv_t;
-      pr.npts = np;
+      // Only a probe whose logit exceeds every earlier probe's can be the
+      // first kept one: top-p keeps the logits from a boundary up, so a
+      // probe at or below an earlier, unkept probe's logit is not kept
+      // either (the probe pass's sums keep that order: a sum of more
+      // nonnegative terms never rounds below one of fewer).  The kept list
+      // is therefore increasing in logit and usually two or three long.
+      int pid[kProbes];
+      float pl[kProbes];
+#pragma unroll
       for (int i = 0; i < kProbes; ++i) {
-        const int id = i < pr.npts ? cand_id(sh.list[i]) : 0;
-        pr.id[i] = id;
-        pr.pt[i] = i < pr.npts ? logit_at(a.lv, r, id) : INFINITY;
+        pid[i] = i < np ? cand_id(sh.list[i]) : 0;
+        pl[i] = i < np ? logit_at(a.lv, r, pid[i]) : -INFINITY;
       }
+      int nh = 0;
+      float hi = -INFINITY;
+      for (int i = 0; i < np; ++i) {
+        if (i == 0 || pl[i] > hi) {
+          pr.id[nh] = pid[i];
+          pr.pt[nh] = pl[i];
+          hi = pl[i];
+          ++nh;
+        }
+      }
+      for (int i = nh; i < kProbes; ++i) {
+        pr.id[i] = 0;
+        pr.pt[i] = INFINITY;
+      }
+      pr.npts = nh;
       reinterpret_cast<ProbeRec*>(ws + lay.off_prec)[r] = pr;
       push_row(&ctr[1], probe_list, r);
     }
@@ -1798,6 +1820,46 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
 
 // ------------------------------------------------------------------- P: probe
 // Mass strictly above each probe logit, per (probe row, chunk).
+// This thread's sums of the weights exp((l - m) / T) of the chunk's logits
+// above each of the row's NP probe logits.  Four float4 per thread in flight
+// per step (a fourth of the round trips of one at a time); each thread
+// still takes its elements in the order e = 4 tid + 4 PT j, j = 0, 1, ...
+template <int NP>
+__device__ __forceinline__ void probe_sums(const float* __restrict__ src, int n, int vec,
+                                           const ProbeRec& pr, float (&acc)[kProbes]) {
+  const int tid = threadIdx.x;
+  const float sc = pr.inv_t * kLog2e;
+  float pt[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) pt[i] = pr.pt[i];
+  constexpr int U = 4;
+  for (int e0 = 4 * tid; e0 < n; e0 += 4 * PT * U) {
+    float4 f[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = e0 + 4 * PT * u;
+      if (vec && e + 3 < n) {
+        f[u] = load_stream4(src + e);
+      } else {
+        f[u].x = e + 0 < n ? load_stream(src + e + 0) : -INFINITY;
+        f[u].y = e + 1 < n ? load_stream(src + e + 1) : -INFINITY;
+        f[u].z = e + 2 < n ? load_stream(src + e + 2) : -INFINITY;
+        f[u].w = e + 3 < n ? load_stream(src + e + 3) : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float l = lane(f[u], q);
+        const float wt = __builtin_amdgcn_exp2f((l - pr.m) * sc);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) acc[i] += l > pt[i] ? wt : 0.0f;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(PT) void probe_kernel(SamplerArgs a, FastLayout lay,
                                                    uint8_t* __restrict__ ws, int vec) {
   __shared__ double part[kProbes][PW];
@@ -1810,48 +1872,30 @@ __global__ __launch_bounds__(PT) void probe_kernel(SamplerArgs a, FastLayout lay
     const int r = probe_list[li];
     const ProbeRec pr = reinterpret_cast<const ProbeRec*>(ws + lay.off_prec)[r];
     const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
-    const float* __restrict__ src = geo.src;
-    const int n = geo.n;
-    const float sc = pr.inv_t * kLog2e;
     float acc[kProbes];
 #pragma unroll
     for (int i = 0; i < kProbes; ++i) acc[i] = 0.0f;
-    // Four float4 per thread in flight per step (a fourth of the round trips
-    // of one at a time); each thread still takes its elements in the order
-    // e = 4 tid + 4 PT j, j = 0, 1, ...
-    constexpr int U = 4;
-    for (int e0 = 4 * tid; e0 < n; e0 += 4 * PT * U) {
-      float4 f[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = e0 + 4 * PT * u;
-        if (vec && e + 3 < n) {
-          f[u] = load_stream4(src + e);
-        } else {
-          f[u].x = e + 0 < n ? load_stream(src + e + 0) : -INFINITY;
-          f[u].y = e + 1 < n ? load_stream(src + e + 1) : -INFINITY;
-          f[u].z = e + 2 < n ? load_stream(src + e + 2) : -INFINITY;
-          f[u].w = e + 3 < n ? load_stream(src + e + 3) : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float l = lane(f[u], q);
-          const float wt = __builtin_amdgcn_exp2f((l - pr.m) * sc);
-#pragma unroll
-          for (int i = 0; i < kProbes; ++i) acc[i] += l > pr.pt[i] ? wt : 0.0f;
-        }
-      }
+    // The row's probe count (1..kProbes, most often two or three) fixes how
+    // many comparisons each logit takes.
+    const int np = __builtin_amdgcn_readfirstlane(pr.npts);
+    switch (np) {
+      case 1: probe_sums<1>(geo.src, geo.n, vec, pr, acc); break;
+      case 2: probe_sums<2>(geo.src, geo.n, vec, pr, acc); break;
+      case 3: probe_sums<3>(geo.src, geo.n, vec, pr, acc); break;
+      case 4: probe_sums<4>(geo.src, geo.n, vec, pr, acc); break;
+      case 5: probe_sums<5>(geo.src, geo.n, vec, pr, acc); break;
+      case 6: probe_sums<6>(geo.src, geo.n, vec, pr, acc); break;
+      case 7: probe_sums<7>(geo.src, geo.n, vec, pr, acc); break;
+      default: probe_sums<kProbes>(geo.src, geo.n, vec, pr, acc); break;
     }
 #pragma unroll
     for (int i = 0; i < kProbes; ++i) {
+      if (i >= np) break;
       const double s = wave_sum(static_cast<double>(acc[i]));
       if (lane_id == 0) part[i][wave] = s;
     }
     __syncthreads();
-    if (tid < kProbes) {
+    if (tid < np) {
       double t = 0.0;
       for (int k = 0; k < PW; ++k) t += part[tid][k];
       reinterpret_cast<double*>(ws + lay.off_part)[(static_cast<size_t>(li) * S + c) * kProbes + tid] = t;
