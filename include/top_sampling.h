@@ -219,14 +219,14 @@ int sampler_sample(const float* logits, int64_t rows, int64_t vocab, int64_t ld_
  * workspace.  The call allocates and frees nothing.
  *   - TS_EUNSUPPORTED if sampler_workspace_bytes(rows, vocab, max_logprobs)
  *     exceeds TS_NOALLOC_SCRATCH_BYTES (e.g. 640 x 151,936 x 20 needs about
- *     39 MB and fits; use sampler_sample with a caller workspace beyond it).
+ *     43 MB and fits; use sampler_sample with a caller workspace beyond it).
  *   - Every call on a GPU shares that GPU's array: calls that overlap on one
  *     GPU (different streams, or different host threads) race and must be
  *     serialised by the caller.  The array needs no clearing between calls.
  *   - TS_EHIP if no HIP device is current or the array's device address
  *     cannot be obtained.
  */
-#define TS_NOALLOC_SCRATCH_BYTES (64ull << 20)
+#define TS_NOALLOC_SCRATCH_BYTES (96ull << 20)
 int sampler_sample_noalloc(const float* logits, int64_t rows, int64_t vocab, int64_t ld_logits,
                            const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
                            int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,

@@ -42,10 +42,10 @@ def test_header_constants_match_binding():
     for name, val in [("TS_MAX_LOGPROBS", ts.TS_MAX_LOGPROBS), ("TS_MAX_SLICES", ts.TS_MAX_SLICES),
                       ("TS_LOGPROBS_PROCESSED", ts.TS_LOGPROBS_PROCESSED),
                       ("TS_PROBE_SMALL_OPERANDS", ts.TS_PROBE_SMALL_OPERANDS),
-                      ("TS_NOALLOC_SCRATCH_BYTES", "(64ull << 20)"),
+                      ("TS_NOALLOC_SCRATCH_BYTES", "(96ull << 20)"),
                       ("TS_PROBE_RANDOM_OPERANDS", ts.TS_PROBE_RANDOM_OPERANDS)]:
         assert re.search(rf"#define {name} {re.escape(str(val))}", text), name
-    assert ts.TS_NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert ts.TS_NOALLOC_SCRATCH_BYTES == 96 << 20
     assert workloads.PARAMS_DTYPE.itemsize == ts.PARAMS_BYTES
 
 

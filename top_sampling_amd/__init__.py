@@ -38,7 +38,7 @@ TS_MAX_LOGPROBS = 1024
 TS_MAX_SLICES = 64
 TS_LOGPROBS_PROCESSED = 1
 TS_PROBE_SMALL_OPERANDS, TS_PROBE_RANDOM_OPERANDS = 0, 1
-TS_NOALLOC_SCRATCH_BYTES = 64 << 20
+TS_NOALLOC_SCRATCH_BYTES = 96 << 20
 PARAMS_BYTES = 24
 
 # (name, restype, argtypes) of every symbol the headers declare

@@ -124,6 +124,21 @@ struct ChunkRec {  // one per (row, chunk); 64 bytes
 };
 static_assert(sizeof(ChunkRec) == 64, "64-byte chunk records");
 
+// A Gumbel-key candidate as the chunk pass lists it: the token, its logit and
+// its Philox word, so the merge forms the key (l - m) / T + g without reading
+// the logit or drawing the word again.
+struct KeyRec {
+  int id;
+  float logit;
+  uint32_t word;
+  int pad;
+};
+static_assert(sizeof(KeyRec) == 16, "16-byte key records");
+
+__device__ __forceinline__ float key_of(const KeyRec& k, float m, float inv_t) {
+  return (k.logit - m) * inv_t + gumbel_from_word(k.word);
+}
+
 struct ProbeRec {  // a top-p-only row whose boundary lies below the listed logits
   double z;        // total temperature-scaled mass, relative to the row maximum
   float m, lse, inv_t;
@@ -218,7 +233,7 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n, int max_
   l.off_cand = off;
   off = align_up(off + RS * static_cast<size_t>(l.cc) * sizeof(unsigned long long), 256);
   l.off_key = off;
-  off = align_up(off + RS * kKeyCap * sizeof(int), 256);
+  off = align_up(off + RS * kKeyCap * sizeof(KeyRec), 256);
   l.off_prec = off;
   off = align_up(off + R * sizeof(ProbeRec), 256);
   l.off_part = off;

@@ -120,10 +120,10 @@ constexpr int kQueueCap = 320;
 struct ChunkSmem {
   uint32_t hist[RB];
   uint32_t keys4[4 * AT];  // per-thread top-4 keys (block-level selection)
-  int klist[kKeyCap];
+  KeyRec klist[kKeyCap];
   float wthr[AW];
-  float qx[AW][kQueueCap];     // x = (l - cmax) / T
-  uint32_t qw[AW][kQueueCap];  // the token's Philox word
+  float ql[AW][kQueueCap];     // the token's logit
+  uint32_t qw[AW][kQueueCap];  // its Philox word
   uint16_t qe[AW][kQueueCap];  // its index in the chunk
   float rm[AW], rs[AW], rt[AW];
   int rb[AW];
@@ -299,11 +299,12 @@ __device__ __forceinline__ uint32_t u_floor_bits(float xm, float bar) {
 // of keys listed (1, or 0 for an all-padding chunk); kfloor is the key.
 __device__ __forceinline__ int chunk_best_key(const float4 (&v)[AV], float cmax, float inv_t,
                                               uint64_t seed, uint64_t grow, int c0,
-                                              int* __restrict__ klist_out, ChunkSmem& sh,
+                                              KeyRec* __restrict__ klist_out, ChunkSmem& sh,
                                               float& kfloor) {
   const int tid = threadIdx.x;
-  float kb = -INFINITY;
+  float kb = -INFINITY, kl = 0.0f;
   int ib = 0x7fffffff;
+  uint32_t kw = 0u;
   float wbar = kMinGumbel;
 #pragma unroll
   for (int j = 0; j < AV; ++j) {
@@ -324,16 +325,19 @@ __device__ __forceinline__ int chunk_best_key(const float4 (&v)[AV], float cmax,
         if (better(key, id, kb, ib)) {
           kb = key;
           ib = id;
+          kl = lane(v[j], q);
+          kw = w.v[q];
         }
       }
     }
     // Refreshed early and then less often: the bar rises fastest at first.
     if (j == 0 || j == 1 || j == 3 || j == 7 || j == 11) wbar = fmaxf(wbar, wave_max_uniform(kb));
   }
+  const int mine = ib;
   block_best<AT>(kb, ib, sh.rf, sh.ri);
-  if (tid == 0 && ib != 0x7fffffff) {
-    klist_out[0] = ib;
-    sh.nkey = 1;
+  if (ib != 0x7fffffff) {
+    if (mine == ib) klist_out[0] = KeyRec{ib, kl, kw, 0};  // ids are unique: one writer
+    if (tid == 0) sh.nkey = 1;
   }
   kfloor = kb;
   __syncthreads();
@@ -355,12 +359,12 @@ __device__ __forceinline__ int chunk_best_key(const float4 (&v)[AV], float cmax,
 // kKeyCap: overflow, the list is not written); kfloor = B.
 __device__ __forceinline__ int chunk_keys_topp(const float4 (&v)[AV], float cmax, float inv_t,
                                                float tmass, uint64_t seed, uint64_t grow, int c0,
-                                               int* __restrict__ klist_out, ChunkSmem& sh,
+                                               KeyRec* __restrict__ klist_out, ChunkSmem& sh,
                                                float& kfloor) {
   const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
   const float bar = uniform_f32(__builtin_amdgcn_logf(tmass) * kLn2 - kLnKeysPerChunk);
   kfloor = bar;
-  float* qx = sh.qx[wave];
+  float* ql = sh.ql[wave];
   uint32_t* qw = sh.qw[wave];
   uint16_t* qe = sh.qe[wave];
   int qn = 0;  // the wave's queue length (uniform)
@@ -372,9 +376,10 @@ __device__ __forceinline__ int chunk_keys_topp(const float4 (&v)[AV], float cmax
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int i = lane_id; i < qn; i += kWave) {
-      if (qx[i] + gumbel_from_word(qw[i]) >= bar) {
+      const float l = ql[i];
+      if ((l - cmax) * inv_t + gumbel_from_word(qw[i]) >= bar) {
         const int slot = atomicAdd(&sh.nkey, 1);
-        if (slot < kKeyCap) sh.klist[slot] = c0 + qe[i];
+        if (slot < kKeyCap) sh.klist[slot] = KeyRec{c0 + qe[i], l, qw[i], 0};
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -409,7 +414,7 @@ __device__ __forceinline__ int chunk_keys_topp(const float4 (&v)[AV], float cmax
         const int slot = qn + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
                                   static_cast<uint32_t>(bal >> 32),
                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
-        qx[slot] = x[q];
+        ql[slot] = lane(v[j], q);
         qw[slot] = wq[q];
         qe[slot] = static_cast<uint16_t>(e + q);
       }
@@ -736,7 +741,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   int nkey = 0;
   float kfloor = INFINITY;
   if ((kind == KIND_FULL || kind == KIND_TOPP) && !ovf) {
-    int* klist_out = reinterpret_cast<int*>(ws + lay.off_key) + static_cast<size_t>(bid) * kKeyCap;
+    KeyRec* klist_out = reinterpret_cast<KeyRec*>(ws + lay.off_key) + static_cast<size_t>(bid) * kKeyCap;
     const uint64_t grow = static_cast<uint64_t>(a.row_offset + r);
     nkey = kind == KIND_TOPP
                ? chunk_keys_topp(v, cmax, inv_t, tmass, p.seed, grow, c0, klist_out, sh, kfloor)
@@ -790,7 +795,11 @@ struct MergeSmem {
   float m, lse, kmin;
   uint32_t floor_key;
   double z;
+  // The radix-bin union as 4,096 words (kListMax): scratch for per-entry
+  // values when no radix round runs.
+  __device__ uint32_t* hist4() { return reinterpret_cast<uint32_t*>(mhist); }
 };
+static_assert(2 * RB >= kListMax, "the radix-bin union holds a word per list entry");
 // Three merge workgroups share a CU at this size; 384 bytes more (53,824)
 // left room for only two, measured as 6-8 us more per merge call.
 static_assert(sizeof(MergeSmem) <= 53440, "three merge workgroups per CU");
@@ -1357,51 +1366,102 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   }
   __syncthreads();
   const float inv_t = kind == KIND_GREEDY ? 0.0f : 1.0f / p.temperature;
-  if (tid == 0) {
-    int st = 0;
-    for (int c = 0; c < S; ++c)
-      if (sh.recs[c].status == 1) st = 1;
-    if (st == 0)
-      for (int c = 0; c < S; ++c)
-        if (sh.recs[c].status == 2) st = 2;
-    float m = -INFINITY;
-    uint32_t fl = 0u;
-    int tot = 0;
-    if (st != 1) {
-      for (int c = 0; c < S; ++c) {
-        m = fmaxf(m, sh.recs[c].cmax);
-        if (sh.recs[c].kt > fl) fl = sh.recs[c].kt;
-        sh.pos[c] = tot;
-        tot += sh.recs[c].ncand;
+  if (S <= kWave) {
+    // One chunk per lane of the first wave: the row's statistics by wave
+    // reductions rather than a walk over the records by one thread.
+    if (tid < kWave) {
+      const bool has = tid < S;
+      const ChunkRec& rc = sh.recs[has ? tid : 0];
+      const int status = has ? rc.status : 0;
+      const int st = __any(status == 1) ? 1 : (__any(status == 2) ? 2 : 0);
+      const float cm = has ? rc.cmax : -INFINITY;
+      float m = -INFINITY;
+      uint32_t fl = 0u;
+      int tot = 0;
+      if (st != 1) {
+        m = wave_max(cm);
+        fl = has ? rc.kt : 0u;
+#pragma unroll
+        for (int o = kWave / 2; o > 0; o >>= 1) fl = max(fl, static_cast<uint32_t>(__shfl_xor(static_cast<int>(fl), o, kWave)));
+        const int nc = has ? rc.ncand : 0;
+        const int inc = wave_inclusive_scan(nc);
+        if (has) sh.pos[tid] = inc - nc;
+        tot = __shfl(inc, kWave - 1, kWave);
       }
-    }
-    sh.pos[S] = tot;
-    float se = 0.0f;
-    double z = 0.0;
-    float kmin = -INFINITY;
-    if (m > -INFINITY) {
-      for (int c = 0; c < S; ++c) {
-        if (!(sh.recs[c].cmax > -INFINITY)) continue;
-        se += sh.recs[c].sumexp * fast_exp(sh.recs[c].cmax - m);
+      float se = 0.0f, kf = -INFINITY;
+      double z = 0.0;
+      if (m > -INFINITY && has && cm > -INFINITY) {
+        se = rc.sumexp * fast_exp(cm - m);
         if (kind == KIND_TOPP || (proc && kind == KIND_FULL)) {
-          const float shift = (sh.recs[c].cmax - m) * inv_t;
-          z += static_cast<double>(sh.recs[c].tmass) *
-               static_cast<double>(__builtin_amdgcn_exp2f(shift * kLog2e));
-          if (kind == KIND_TOPP) kmin = fmaxf(kmin, sh.recs[c].kfloor + shift);
+          const float shift = (cm - m) * inv_t;
+          z = static_cast<double>(rc.tmass) * static_cast<double>(__builtin_amdgcn_exp2f(shift * kLog2e));
+          if (kind == KIND_TOPP) kf = rc.kfloor + shift;
         }
       }
+      se = wave_sum(se);
+      z = wave_sum(z);
+      kf = wave_max(kf);
+      if (tid == 0) {
+        sh.status = st;
+        sh.m = m;
+        sh.floor_key = fl;
+        sh.total = tot;
+        sh.pos[S] = tot;
+        sh.lse = m + logf(se);
+        sh.z = z;
+        sh.kmin = kf + kKeyMargin;
+        sh.nlist = 0;
+        sh.rmax = 0u;
+      }
     }
-    sh.status = st;
-    sh.m = m;
-    sh.floor_key = fl;
-    sh.total = tot;
-    sh.lse = m + logf(se);
-    sh.z = z;
-    sh.kmin = kmin + kKeyMargin;
-    sh.nlist = 0;
-    sh.rmax = 0u;
+    __syncthreads();
+  } else {
+    if (tid == 0) {
+      int st = 0;
+      for (int c = 0; c < S; ++c)
+        if (sh.recs[c].status == 1) st = 1;
+      if (st == 0)
+        for (int c = 0; c < S; ++c)
+          if (sh.recs[c].status == 2) st = 2;
+      float m = -INFINITY;
+      uint32_t fl = 0u;
+      int tot = 0;
+      if (st != 1) {
+        for (int c = 0; c < S; ++c) {
+          m = fmaxf(m, sh.recs[c].cmax);
+          if (sh.recs[c].kt > fl) fl = sh.recs[c].kt;
+          sh.pos[c] = tot;
+          tot += sh.recs[c].ncand;
+        }
+      }
+      sh.pos[S] = tot;
+      float se = 0.0f;
+      double z = 0.0;
+      float kmin = -INFINITY;
+      if (m > -INFINITY) {
+        for (int c = 0; c < S; ++c) {
+          if (!(sh.recs[c].cmax > -INFINITY)) continue;
+          se += sh.recs[c].sumexp * fast_exp(sh.recs[c].cmax - m);
+          if (kind == KIND_TOPP || (proc && kind == KIND_FULL)) {
+            const float shift = (sh.recs[c].cmax - m) * inv_t;
+            z += static_cast<double>(sh.recs[c].tmass) *
+                 static_cast<double>(__builtin_amdgcn_exp2f(shift * kLog2e));
+            if (kind == KIND_TOPP) kmin = fmaxf(kmin, sh.recs[c].kfloor + shift);
+          }
+        }
+      }
+      sh.status = st;
+      sh.m = m;
+      sh.floor_key = fl;
+      sh.total = tot;
+      sh.lse = m + logf(se);
+      sh.z = z;
+      sh.kmin = kmin + kKeyMargin;
+      sh.nlist = 0;
+      sh.rmax = 0u;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (sh.status == 1 || !(sh.m > -INFINITY)) {
     write_bad<BT>(a, r, TS_ROW_BAD_LOGITS);
     return;
@@ -1562,14 +1622,15 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
   double zk = 0.0;
   if (kind == KIND_FULL) {
     zk = sh.z;
-    const int* keys = reinterpret_cast<const int*>(ws + lay.off_key) +
-                      static_cast<size_t>(r) * S * kKeyCap;
+    const KeyRec* keys = reinterpret_cast<const KeyRec*>(ws + lay.off_key) +
+                         static_cast<size_t>(r) * S * kKeyCap;
     float gk = -INFINITY;
     int gi = 0x7fffffff;
     for (int c = tid; c < S; c += BT) {
       if (sh.nkey[c] < 1) continue;
-      const int id = keys[static_cast<size_t>(c) * kKeyCap];
-      const float key = gumbel_key(logit_at(a.lv, r, id), m, inv_t, p.seed, grow, id);
+      const KeyRec k = keys[static_cast<size_t>(c) * kKeyCap];
+      const int id = k.id;
+      const float key = key_of(k, m, inv_t);
       if (better(key, id, gk, gi)) {
         gk = key;
         gi = id;
@@ -1732,9 +1793,11 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     // Top-p-only row whose boundary lies below the listed logits: the
     // chunks' key candidates, complete above the highest chunk floor,
     // sorted by row key; the best few become probes.
-    const int* keys = reinterpret_cast<const int*>(ws + lay.off_key) +
-                      static_cast<size_t>(r) * S * kKeyCap;
+    const KeyRec* keys = reinterpret_cast<const KeyRec*>(ws + lay.off_key) +
+                         static_cast<size_t>(r) * S * kKeyCap;
     const float kmin = sh.kmin;
+    // The listed keys' logits ride along in the radix-bin space (free here).
+    uint32_t* klog = sh.hist4();
     __syncthreads();
     if (tid == 0) sh.nlist = 0;
     __syncthreads();
@@ -1742,11 +1805,14 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     for (int g = tid; g < kspan; g += BT) {
       const int c = g / kKeyCap, i = g - c * kKeyCap;
       if (i >= sh.nkey[c]) continue;
-      const int id = keys[g];
-      const float key = gumbel_key(logit_at(a.lv, r, id), m, inv_t, p.seed, grow, id);
+      const KeyRec k = keys[g];
+      const float key = key_of(k, m, inv_t);
       if (key >= kmin) {
         const int slot = atomicAdd(&sh.nlist, 1);
-        if (slot < kListMax) sh.list[slot] = pack_cand(order_key(key), id);
+        if (slot < kListMax) {
+          sh.list[slot] = pack_cand(order_key(key), k.id);
+          klog[slot] = __float_as_uint(k.logit);
+        }
       }
     }
     __syncthreads();
@@ -1759,15 +1825,16 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     if (nk <= kRegList) {
       constexpr int kPer = kRegList / BT;
       unsigned long long mine[kPer];
-      uint32_t none[kPer];
+      uint32_t lg[kPer];
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
-        mine[q] = tid + q * BT < nk ? sh.list[tid + q * BT] : 0ull;
-        none[q] = 0u;
+        const int i = tid + q * BT;
+        mine[q] = i < nk ? sh.list[i] : 0ull;
+        lg[q] = i < nk ? klog[i] : 0u;
       }
-      got = top_n_regs<kPer, false>(mine, none, kProbes, sh.list, nullptr, sh);
+      got = top_n_regs<kPer, true>(mine, lg, kProbes, sh.list, sh.pr.logit, sh);
     }
-    if (got < 0) trim_and_sort(sh, nk, nk, 0u);
+    if (got < 0) trim_and_sort(sh, nk, nk, 0u);  // (logits read again below)
     const int np = nk < kProbes ? nk : kProbes;
     if (tid == 0) {
       ProbeRec pr;
@@ -1786,7 +1853,9 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
 #pragma unroll
       for (int i = 0; i < kProbes; ++i) {
         pid[i] = i < np ? cand_id(sh.list[i]) : 0;
-        pl[i] = i < np ? logit_at(a.lv, r, pid[i]) : -INFINITY;
+        pl[i] = i >= np ? -INFINITY
+                : got >= 0 ? __uint_as_float(sh.pr.logit[i])
+                           : logit_at(a.lv, r, pid[i]);
       }
       int nh = 0;
       float hi = -INFINITY;
