@@ -58,6 +58,7 @@ constexpr int AV = kChunkVec;
 constexpr int RB = 2048;
 constexpr int BT = 256;
 constexpr int BW = BT / kWave;
+constexpr int kRegList = 2048;  // merge-list entries the register routines take (8 per thread)
 constexpr int PT = 256;
 constexpr int PW = PT / kWave;
 
@@ -1175,7 +1176,6 @@ __device__ int top_n_regs(const unsigned long long (&v)[P], const uint32_t (&pay
 // decision is the same.  Returns the winner's id, or -1 when none of the
 // probes is kept or the list is longer than kRegList (then the caller
 // searches the boundary).
-constexpr int kRegList = 2048;  // list entries the register routines take (8 per thread)
 
 __device__ int topk_probe_winner(MergeSmem& sh, int U, uint32_t kmin, float m, float inv_t,
                                  float top_p, uint64_t seed, uint64_t grow) {
@@ -1837,11 +1837,13 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     if (got < 0) trim_and_sort(sh, nk, nk, 0u);  // (logits read again below)
     const int np = nk < kProbes ? nk : kProbes;
     if (tid == 0) {
-      ProbeRec pr;
-      pr.z = sh.z;
-      pr.m = m;
-      pr.lse = lse;
-      pr.inv_t = inv_t;
+      // Written field by field into the record (a local copy indexed by the
+      // running count would live in per-lane scratch memory).
+      ProbeRec* dst = reinterpret_cast<ProbeRec*>(ws + lay.off_prec) + r;
+      dst->z = sh.z;
+      dst->m = m;
+      dst->lse = lse;
+      dst->inv_t = inv_t;
       // Only a probe whose logit exceeds every earlier probe's can be the
       // first kept one: top-p keeps the logits from a boundary up, so a
       // probe at or below an earlier, unkept probe's logit is not kept
@@ -1859,20 +1861,20 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
       }
       int nh = 0;
       float hi = -INFINITY;
-      for (int i = 0; i < np; ++i) {
-        if (i == 0 || pl[i] > hi) {
-          pr.id[nh] = pid[i];
-          pr.pt[nh] = pl[i];
+#pragma unroll
+      for (int i = 0; i < kProbes; ++i) {
+        if (i < np && (i == 0 || pl[i] > hi)) {
+          dst->id[nh] = pid[i];
+          dst->pt[nh] = pl[i];
           hi = pl[i];
           ++nh;
         }
       }
       for (int i = nh; i < kProbes; ++i) {
-        pr.id[i] = 0;
-        pr.pt[i] = INFINITY;
+        dst->id[i] = 0;
+        dst->pt[i] = INFINITY;
       }
-      pr.npts = nh;
-      reinterpret_cast<ProbeRec*>(ws + lay.off_prec)[r] = pr;
+      dst->npts = nh;
       push_row(&ctr[1], probe_list, r);
     }
     return;
