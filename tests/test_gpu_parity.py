@@ -527,6 +527,29 @@ def test_sampler_long_topk_tie_runs(dev, ts, route):
     assert np.all(got["row_status"] == 0)
 
 
+def test_sampler_long_topk_probe_fallback(dev, ts, route):
+    """Top-k sets longer than 192 with top-p: the merge first checks the
+    list's eight best Gumbel keys against the top-p mass and searches the
+    boundary only when none is kept.  With p of a few percent on flat logits
+    the kept set is a handful of tokens and the eight probes all fall outside
+    it (the search runs); with p near 1 the first probe is kept."""
+    rng = np.random.default_rng(29)
+    rows, V = 24, 20000
+    logits = (rng.standard_normal((rows, V)) * 1.2).astype(np.float32)
+    params = np.zeros(rows, dtype=workloads.PARAMS_DTYPE)
+    params["temperature"] = np.array([0.5, 1.5] * 12, dtype=np.float32)
+    params["top_k"] = np.array([300, 1000, 2000] * 8, dtype=np.int32)
+    params["top_p"] = np.repeat(np.array([0.01, 0.03, 0.9, 0.99], dtype=np.float32), 6)
+    params["n_logprobs"] = np.arange(rows) % 9
+    params["seed"] = np.arange(rows, dtype=np.uint64) * np.uint64(977) + np.uint64(13)
+    say("sampler long top-k probe fallback", route)
+    got = _run_sampler(ts, dev, logits, params, 5, 8)
+    res, lse = _oracle_ref(logits, params, 5, 8)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, label="probe fallback")
+    assert np.all(got["row_status"] == 0)
+
+
 def _kept_by_definition(l, t, k, p):
     """The kept set written out from its definition, by brute force on a
     short row: v is in the top-k set iff fewer than k logits are strictly

@@ -131,17 +131,51 @@ __device__ __forceinline__ bool better_u(uint32_t ka, int ia, uint32_t kb, int i
   return ka > kb || (ka == kb && ia < ib);
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// A DPP move of a 4- or 8-byte value (as one or two 32-bit moves); lanes
+// with no source, or outside the row mask, get zero.
+template <int CTRL, int ROW_MASK, typename T>
+__device__ __forceinline__ T dpp_or_zero(T src) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(
+        T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, src), CTRL, ROW_MASK, 0xF, false));
+  } else {
+    static_assert(sizeof(T) == 8, "4- or 8-byte values");
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, src);
+    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(u)), CTRL, ROW_MASK, 0xF, false));
+    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        0, static_cast<int>(static_cast<uint32_t>(u >> 32)), CTRL, ROW_MASK, 0xF, false));
+    return __builtin_bit_cast(T, (static_cast<unsigned long long>(hi) << 32) | lo);
+  }
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+// Lane 63's value of a 4- or 8-byte value, in scalar registers.
+template <typename T>
+__device__ __forceinline__ T read_lane63(T v) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  } else {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), 63);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), 63);
+    return __builtin_bit_cast(T, (static_cast<unsigned long long>(hi) << 32) | lo);
+  }
+}
+
+// Sum over the wave, returned to every lane (uniform), by DPP: a butterfly
+// within each 16-lane row (quad permutations, then row rotations by 4 and
+// 8), then row 1 adds row 0 and row 3 row 2 (broadcast of lane 15), and
+// row 3 adds rows 0 + 1 (broadcast of lane 31); lane 63 holds the total.
+// Every lane must be active.
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  v += dpp_or_zero<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v += dpp_or_zero<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v += dpp_or_zero<0x124, 0xF>(v);  // row_ror:4
+  v += dpp_or_zero<0x128, 0xF>(v);  // row_ror:8
+  v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return read_lane63(v);
 }
 
 // One DPP move of a float (ctrl and row_mask are compile-time constants);
@@ -164,6 +198,9 @@ __device__ __forceinline__ float wave_max_uniform(float v) {
   v = fmaxf(v, dpp_f32<0x143, 0xC>(v, v));  // row_bcast:31 into rows 2 and 3
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+
+// Maximum over the wave (the DPP form above), returned to every lane.
+__device__ __forceinline__ float wave_max(float v) { return wave_max_uniform(v); }
 
 // One DPP move of a 64-bit value, as two 32-bit moves (same control).
 template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
@@ -231,15 +268,21 @@ __device__ __forceinline__ void wave_best_u(uint32_t& k, int& i) {
   }
 }
 
-// Inclusive prefix sum within a wave (lane order).
+// Inclusive prefix sum within a wave (lane order), by DPP: shifts right by
+// 1, 2, 4 and 8 lanes within each 16-lane row (a lane shifted in from
+// outside the row adds zero) give every row its own prefix sums; then row
+// 1 adds row 0's total and row 3 row 2's (row broadcast of lane 15), and
+// rows 2 and 3 add the first two rows' total (row broadcast of lane 31).
+// Six DPP steps instead of six cross-lane shuffles through the LDS
+// crossbar.  Every lane must be active.
 template <typename T>
 __device__ __forceinline__ T wave_inclusive_scan(T v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const T u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
+  v += dpp_or_zero<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_or_zero<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_or_zero<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_or_zero<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_or_zero<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_or_zero<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
   return v;
 }
 

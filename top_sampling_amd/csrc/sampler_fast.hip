@@ -500,12 +500,7 @@ __global__ __launch_bounds__(OT) void order_rows_kernel(SamplerArgs a, FastLayou
   int incl[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    incl[k] = cnt[k];
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int t = __shfl_up(incl[k], d, kWave);
-      if (lane_id >= d) incl[k] += t;
-    }
+    incl[k] = wave_inclusive_scan(cnt[k]);
     if (lane_id == kWave - 1) wsum[wave][k] = incl[k];
   }
   __syncthreads();
@@ -709,12 +704,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
       if (lane(v[j], q) >= tf && e + q < n) cm |= 1ull << (4 * j + q);
   }
   const int cnt = __popcll(cm);
-  int incl = cnt;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int t = __shfl_up(incl, d, kWave);
-    if (lane_id >= d) incl += t;
-  }
+  const int incl = wave_inclusive_scan(cnt);
   if (lane_id == kWave - 1) sh.wcnt[wave] = incl;
   __syncthreads();
   int slot = incl - cnt, total = 0;
