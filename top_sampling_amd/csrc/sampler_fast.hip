@@ -636,11 +636,20 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     for (int j = 0; j < AV; ++j)
       flag |= (isnan(v[j].x) || isnan(v[j].y) || isnan(v[j].z) || isnan(v[j].w)) ? 1 : 0;
   }
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(lm, o, kWave), s2 = __shfl_xor(ls, o, kWave),
-                t2 = __shfl_xor(lt, o, kWave);
-    merge_stats(lm, ls, lt, m2, s2, t2, inv_t);
+  // The wave's statistics: its maximum by DPP, each lane's sums rescaled to
+  // it (a lane's maximum is never NaN: it starts at -inf and fmaxf skips
+  // NaN), then DPP sums -- two exponentials per lane instead of four per
+  // step of a shuffle butterfly.
+  {
+    const float wm = wave_max_uniform(lm);
+    if (wm > -INFINITY) {
+      const bool live = lm > -INFINITY;
+      ls = live ? ls * fast_exp(lm - wm) : 0.0f;
+      lt = live ? lt * fast_exp((lm - wm) * inv_t) : 0.0f;
+    }
+    ls = wave_sum(ls);
+    lt = wave_sum(lt);
+    lm = wm;
   }
   flag = __any(flag) ? 1 : 0;
   if (lane_id == 0) {
@@ -1529,18 +1538,20 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
     }
   }
   {
-    // Thread t takes g = t, t + BT, ... four at a time (four loads in
-    // flight); its chunk index only moves forward, so it walks the chunk
+    // Thread t takes g = t, t + BT, ... eight at a time (eight loads in
+    // flight: a long top-k row's union, one to three thousand entries, in
+    // one round trip); its chunk index only moves forward, so it walks the chunk
     // offsets instead of searching them.  Slots come one atomic per wave:
     // the wave's count from a ballot, each lane's offset from mbcnt.  The
     // list's order is immaterial (every later step sorts, selects or takes a
     // maximum with id tie-breaks).
     const int lane_id = tid & (kWave - 1);
     int c = 0;
-    for (int g0 = tid; g0 < total; g0 += 4 * BT) {
-      unsigned long long x[4];
+    constexpr int kGather = 8;
+    for (int g0 = tid; g0 < total; g0 += kGather * BT) {
+      unsigned long long x[kGather];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kGather; ++u) {
         const int g = g0 + u * BT;
         x[u] = 0ull;
         if (g < total) {
@@ -1549,7 +1560,7 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kGather; ++u) {
         const bool keep = g0 + u * BT < total && cand_key(x[u]) >= floor_key;
         const unsigned long long bal = __ballot(keep);
         if (bal == 0ull) continue;
