@@ -1126,23 +1126,32 @@ __device__ int top_n_regs(const unsigned long long (&v)[P], const uint32_t (&pay
 #pragma unroll
   for (int j = 1; j < BW; ++j) t = min(t, sh.ru[j]);
   const unsigned long long tb = static_cast<unsigned long long>(t) << 32;
-  // Gathered one atomic per wave: the count from a ballot, each lane's
-  // offset from mbcnt (every lane is active here).
+  // Gathered with one atomic per wave: the wave's count from ballots, each
+  // lane's offset from the earlier ballots' counts and mbcnt (every lane is
+  // active here).
+  unsigned long long bal[P];
+  int wn = 0;
 #pragma unroll
   for (int q = 0; q < P; ++q) {
-    const bool keep = v[q] != 0ull && v[q] >= tb;
-    const unsigned long long bal = __ballot(keep);
-    if (bal == 0ull) continue;
-    int base = 0;
-    if (lane == 0) base = atomicAdd(&sh.nsmall, __popcll(bal));
+    bal[q] = __ballot(v[q] != 0ull && v[q] >= tb);
+    wn += __popcll(bal[q]);
+  }
+  int base = 0;
+  if (wn > 0) {
+    if (lane == 0) base = atomicAdd(&sh.nsmall, wn);
     base = __builtin_amdgcn_readfirstlane(base);
+  }
+#pragma unroll
+  for (int q = 0; q < P; ++q) {
+    if (bal[q] == 0ull) continue;
     const int slot = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                static_cast<uint32_t>(bal >> 32),
-                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
-    if (keep && slot < BT) {
+                                static_cast<uint32_t>(bal[q] >> 32),
+                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[q]), 0u)));
+    if (((bal[q] >> lane) & 1ull) && slot < BT) {
       sh.smass[slot] = v[q];
       if (PAY) sh.skey[slot] = pay[q];
     }
+    base += __popcll(bal[q]);
   }
   __syncthreads();
   const int C = sh.nsmall;
@@ -1204,9 +1213,19 @@ __device__ int topk_probe_winner(MergeSmem& sh, int U, uint32_t kmin, float m, f
   }
   const int np = top_n_regs<P, true>(gk, lk, kProbes, sh.pr.key, sh.pr.logit, sh);
   if (np <= 0) return -1;
+  // Only a probe whose logit exceeds every earlier probe's can be the first
+  // kept one (a probe at or below an earlier, unkept one's logit has at
+  // least its mass above it): usually two or three of the eight.
   uint32_t pl[kProbes];
+  uint32_t rec = 0u, hi = 0u;
 #pragma unroll
-  for (int j = 0; j < kProbes; ++j) pl[j] = j < np ? sh.pr.logit[j] : 0xffffffffu;
+  for (int j = 0; j < kProbes; ++j) {
+    pl[j] = j < np ? sh.pr.logit[j] : 0xffffffffu;
+    if (j < np && (j == 0 || pl[j] > hi)) {
+      rec |= 1u << j;
+      hi = pl[j];
+    }
+  }
   unsigned long long acc[kProbes];
 #pragma unroll
   for (int j = 0; j < kProbes; ++j) acc[j] = 0ull;
@@ -1214,10 +1233,12 @@ __device__ int topk_probe_winner(MergeSmem& sh, int U, uint32_t kmin, float m, f
   for (int q = 0; q < P; ++q) {
     if (q * BT >= U) continue;
 #pragma unroll
-    for (int j = 0; j < kProbes; ++j) acc[j] += lk[q] > pl[j] ? wm[q] : 0ull;
+    for (int j = 0; j < kProbes; ++j)
+      if ((rec >> j) & 1u) acc[j] += lk[q] > pl[j] ? wm[q] : 0ull;
   }
 #pragma unroll
-  for (int j = 0; j < kProbes; ++j) acc[j] = wave_sum_u64_uniform(acc[j]);
+  for (int j = 0; j < kProbes; ++j)
+    if ((rec >> j) & 1u) acc[j] = wave_sum_u64_uniform(acc[j]);
   tot = wave_sum_u64_uniform(tot);
   if (lane == 0) {
 #pragma unroll
@@ -1231,6 +1252,7 @@ __device__ int topk_probe_winner(MergeSmem& sh, int U, uint32_t kmin, float m, f
   const double target = static_cast<double>(top_p) * static_cast<double>(all);
   int id = -1;
   for (int j = 0; j < np; ++j) {
+    if (!((rec >> j) & 1u)) continue;
     unsigned long long a = 0ull;
 #pragma unroll
     for (int x = 0; x < BW; ++x) a += sh.pr.psum[x][j];
@@ -1559,19 +1581,28 @@ __global__ __launch_bounds__(BT) void merge_kernel(SamplerArgs a, FastLayout lay
           x[u] = cand[static_cast<size_t>(c) * lay.cc + (g - sh.pos[c])];
         }
       }
+      // One atomic per wave per round: the wave's count from the ballots,
+      // each lane's offset from the earlier ballots' counts and mbcnt (lane
+      // 0 holds the wave's smallest g, so it is active whenever any lane is).
+      unsigned long long bal[kGather];
+      int wn = 0;
 #pragma unroll
       for (int u = 0; u < kGather; ++u) {
-        const bool keep = g0 + u * BT < total && cand_key(x[u]) >= floor_key;
-        const unsigned long long bal = __ballot(keep);
-        if (bal == 0ull) continue;
-        // lane 0 holds the wave's smallest g, so it is active whenever any lane is
-        int base = 0;
-        if (lane_id == 0) base = atomicAdd(&sh.nlist, __popcll(bal));
-        base = __builtin_amdgcn_readfirstlane(base);
+        bal[u] = __ballot(g0 + u * BT < total && cand_key(x[u]) >= floor_key);
+        wn += __popcll(bal[u]);
+      }
+      if (wn == 0) continue;
+      int base = 0;
+      if (lane_id == 0) base = atomicAdd(&sh.nlist, wn);
+      base = __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+      for (int u = 0; u < kGather; ++u) {
+        if (bal[u] == 0ull) continue;
         const int slot = base + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                    static_cast<uint32_t>(bal >> 32),
-                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0u)));
-        if (keep && slot < kListMax) sh.list[slot] = x[u];
+                                    static_cast<uint32_t>(bal[u] >> 32),
+                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal[u]), 0u)));
+        if (((bal[u] >> lane_id) & 1ull) && slot < kListMax) sh.list[slot] = x[u];
+        base += __popcll(bal[u]);
       }
     }
   }
