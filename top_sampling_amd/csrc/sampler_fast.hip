@@ -902,35 +902,89 @@ __device__ __forceinline__ uint32_t high_bits(uint32_t off, int lowbit) {
 }
 
 // Order key of the k-th largest entry of sh.list[0, U) (1 <= k <= U), every
-// key >= base.  Radix selection over the offset key - base with 11-bit digits
+// key >= base.  Radix selection over the offset key - base with 10-bit digits
 // from its top bit down; as soon as the selected bin holds at most BT
 // entries, they are gathered and the k-th is found by ranking them directly
-// (ties: the key x with #{> x} < k' <= #{>= x} within the bin).
+// (ties: the key x with #{> x} < k' <= #{>= x} within the bin).  Three
+// barriers per round: the bins alternate between two buffers (the next
+// round's are cleared while this round's fill), as do the wave totals and
+// the selected digit, and the scan runs by DPP.
 __device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k, uint32_t base) {
-  const int tid = threadIdx.x;
+  constexpr int NB = 1024;         // bins per round (10-bit digits)
+  constexpr int BPT = NB / BT;     // bins per thread
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  uint32_t* bins = sh.hist4();     // [2][NB] bins, then the posts below
+  uint32_t* wpost = bins + 2 * NB;           // [BW] wave maxima
+  uint32_t* wtot = wpost + BW;               // [2][BW] wave totals
+  uint32_t* sel = wtot + 2 * BW;             // [2][4] digit, count above, count in bin
+  static_assert(2 * NB + 3 * BW + 8 <= 2 * RB, "bins and posts fit the radix-bin union");
+  // The span of the offsets (a DPP wave maximum, one post per wave), with
+  // the first round's bins cleared in the same phase.
+  uint32_t mx = 0u;
+  for (int i = tid; i < U; i += BT) {
+    const uint32_t key = cand_key(sh.list[i]);
+    if (key >= base) mx = max(mx, key - base);
+  }
+  mx = static_cast<uint32_t>(wave_max_u64_uniform(mx));
+  for (int b = tid; b < NB; b += BT) bins[b] = 0u;
+  if (lane == 0) wpost[w] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < BW; ++x) mx = max(mx, wpost[x]);
   uint32_t prefix = 0u, rem = static_cast<uint32_t>(k), hd = static_cast<uint32_t>(U);
-  int lowbit = list_span_bits(sh, U, base);
+  int lowbit = mx == 0u ? 0 : 32 - __builtin_clz(mx);
+  int buf = 0;
   while (lowbit > 0 && hd > static_cast<uint32_t>(BT)) {
-    const int width = lowbit < 11 ? lowbit : 11;
+    const int width = lowbit < 10 ? lowbit : 10;
     const int shift = lowbit - width;
     const uint32_t dmask = (1u << width) - 1u;
+    const int nb = 1 << width;
     const uint32_t hi = high_bits(prefix, lowbit);
-    for (int b = tid; b < RB; b += BT) sh.hist[b] = 0u;
-    __syncthreads();
+    uint32_t* h = bins + buf * NB;
+    uint32_t* hn = bins + (buf ^ 1) * NB;
     for (int i = tid; i < U; i += BT) {
       const uint32_t off = cand_key(sh.list[i]) - base;
-      if (high_bits(off, lowbit) == hi) atomicAdd(&sh.hist[(off >> shift) & dmask], 1u);
+      if (high_bits(off, lowbit) == hi) atomicAdd(&h[(off >> shift) & dmask], 1u);
+    }
+    for (int b = tid; b < NB; b += BT) hn[b] = 0u;  // the next round's bins
+    __syncthreads();
+    // Bins from the top digit down, BPT per thread: the digit d with
+    // above(d) < rem <= above(d) + count(d).
+    uint32_t hc[BPT], sum = 0u;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int b = nb - 1 - (tid * BPT + j);
+      hc[j] = b >= 0 ? h[b] : 0u;
+      sum += hc[j];
+    }
+    const uint32_t inc = wave_inclusive_scan(sum);
+    if (lane == kWave - 1) wtot[buf * BW + w] = inc;
+    __syncthreads();
+    uint32_t ex = inc - sum;
+#pragma unroll
+    for (int x = 0; x < BW; ++x) ex += x < w ? wtot[buf * BW + x] : 0u;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int b = nb - 1 - (tid * BPT + j);
+      if (b >= 0 && ex < rem && rem <= ex + hc[j]) {
+        sel[buf * 4 + 0] = static_cast<uint32_t>(b);
+        sel[buf * 4 + 1] = ex;
+        sel[buf * 4 + 2] = hc[j];
+      }
+      ex += hc[j];
     }
     __syncthreads();
-    select_digit_top<BT, RB / BT>(sh.hist, 1 << width, rem, sh.ru, &sh.sel_d, &sh.sel_above);
-    const uint32_t d = sh.sel_d;
-    rem -= sh.sel_above;
-    hd = sh.hist[d];
-    __syncthreads();
+    const uint32_t d = sel[buf * 4 + 0];
+    rem -= sel[buf * 4 + 1];
+    hd = sel[buf * 4 + 2];
     prefix |= d << shift;
     lowbit = shift;
+    buf ^= 1;
   }
-  if (lowbit == 0) return base + prefix;
+  if (lowbit == 0) {
+    __syncthreads();  // the posts are reused by the caller
+    return base + prefix;
+  }
   const uint32_t hi = high_bits(prefix, lowbit);
   if (tid == 0) sh.nsmall = 0;
   __syncthreads();
