@@ -901,15 +901,20 @@ __device__ __forceinline__ uint32_t high_bits(uint32_t off, int lowbit) {
   return lowbit >= 32 ? 0u : (off >> lowbit);
 }
 
-// Order key of the k-th largest entry of sh.list[0, U) (1 <= k <= U), every
-// key >= base.  Radix selection over the offset key - base with 10-bit digits
-// from its top bit down; as soon as the selected bin holds at most BT
-// entries, they are gathered and the k-th is found by ranking them directly
-// (ties: the key x with #{> x} < k' <= #{>= x} within the bin).  Three
-// barriers per round: the bins alternate between two buffers (the next
-// round's are cleared while this round's fill), as do the wave totals and
-// the selected digit, and the scan runs by DPP.
-__device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k, uint32_t base) {
+// Radix descent over the offsets key - base of the entries of sh.list[0, U)
+// (every key >= base), 10-bit digits from the offsets' top bit down: each
+// round keeps the digit whose bin holds the rem-th largest of the entries
+// that share the digits kept so far.  Three barriers per round: the next
+// round's bins are cleared while this round's fill (two buffers), the wave
+// totals and the kept digit alternate between two buffers too, and the
+// scan runs by DPP.  It stops when the kept bin holds at most `cap` entries
+// (with the entries above it when WITH_ABOVE) or no bits are left; on
+// return prefix holds the kept digits above bit `lowbit`, rem the rank
+// left within the kept bin, above the entries above it and hd its count.
+// Uses the radix-bin union; every thread of the block calls it.
+template <bool WITH_ABOVE>
+__device__ void radix_descend(MergeSmem& sh, int U, uint32_t base, uint32_t cap, int& lowbit,
+                              uint32_t& prefix, uint32_t& rem, uint32_t& above, uint32_t& hd) {
   constexpr int NB = 1024;         // bins per round (10-bit digits)
   constexpr int BPT = NB / BT;     // bins per thread
   const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
@@ -931,10 +936,12 @@ __device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k, uint32_t base) {
   __syncthreads();
 #pragma unroll
   for (int x = 0; x < BW; ++x) mx = max(mx, wpost[x]);
-  uint32_t prefix = 0u, rem = static_cast<uint32_t>(k), hd = static_cast<uint32_t>(U);
-  int lowbit = mx == 0u ? 0 : 32 - __builtin_clz(mx);
+  prefix = 0u;
+  above = 0u;
+  hd = static_cast<uint32_t>(U);
+  lowbit = mx == 0u ? 0 : 32 - __builtin_clz(mx);
   int buf = 0;
-  while (lowbit > 0 && hd > static_cast<uint32_t>(BT)) {
+  while (lowbit > 0 && (WITH_ABOVE ? above + hd : hd) > cap) {
     const int width = lowbit < 10 ? lowbit : 10;
     const int shift = lowbit - width;
     const uint32_t dmask = (1u << width) - 1u;
@@ -943,7 +950,9 @@ __device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k, uint32_t base) {
     uint32_t* h = bins + buf * NB;
     uint32_t* hn = bins + (buf ^ 1) * NB;
     for (int i = tid; i < U; i += BT) {
-      const uint32_t off = cand_key(sh.list[i]) - base;
+      const uint32_t key = cand_key(sh.list[i]);
+      if (key < base) continue;
+      const uint32_t off = key - base;
       if (high_bits(off, lowbit) == hi) atomicAdd(&h[(off >> shift) & dmask], 1u);
     }
     for (int b = tid; b < NB; b += BT) hn[b] = 0u;  // the next round's bins
@@ -974,17 +983,27 @@ __device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k, uint32_t base) {
       ex += hc[j];
     }
     __syncthreads();
-    const uint32_t d = sel[buf * 4 + 0];
-    rem -= sel[buf * 4 + 1];
+    const uint32_t ab = sel[buf * 4 + 1];
+    prefix |= sel[buf * 4 + 0] << shift;
+    rem -= ab;
+    above += ab;
     hd = sel[buf * 4 + 2];
-    prefix |= d << shift;
     lowbit = shift;
     buf ^= 1;
   }
-  if (lowbit == 0) {
-    __syncthreads();  // the posts are reused by the caller
-    return base + prefix;
-  }
+  __syncthreads();  // the posts are reused by the caller
+}
+
+// Order key of the k-th largest entry of sh.list[0, U) (1 <= k <= U), every
+// key >= base: radix descent until the kept bin holds at most BT entries,
+// which are then gathered and ranked directly (ties: the key x with
+// #{> x} < k' <= #{>= x} within the bin).
+__device__ uint32_t list_kth_key(MergeSmem& sh, int U, int k, uint32_t base) {
+  const int tid = threadIdx.x;
+  int lowbit;
+  uint32_t prefix, rem = static_cast<uint32_t>(k), above, hd;
+  radix_descend<false>(sh, U, base, static_cast<uint32_t>(BT), lowbit, prefix, rem, above, hd);
+  if (lowbit == 0) return base + prefix;
   const uint32_t hi = high_bits(prefix, lowbit);
   if (tid == 0) sh.nsmall = 0;
   __syncthreads();
@@ -1332,38 +1351,10 @@ __device__ int trim_and_sort(MergeSmem& sh, int U, int need, uint32_t floor_key)
   if (cap > 256) cap = cap <= 1024 ? 1024 : 2048;  // what the sort pads to anyway
   int C = U;
   if (U > cap && U > BT) {  // up to one entry per thread is ranked directly instead
-    uint32_t rmax = 0u;
-    for (int i = tid; i < U; i += BT) rmax = max(rmax, cand_key(sh.list[i]) - floor_key);
-    if (tid == 0) sh.rmax = 0u;
-    __syncthreads();
-    atomicMax(&sh.rmax, rmax);
-    __syncthreads();
-    rmax = sh.rmax;
-    const int hb = rmax == 0u ? -1 : 31 - __builtin_clz(rmax);
-    uint32_t prefix = 0u, rem = static_cast<uint32_t>(need), above = 0u;
-    int lowbit = hb + 1;
-    while (lowbit > 0) {
-      const int width = lowbit < 11 ? lowbit : 11;
-      const int shift = lowbit - width;
-      const uint32_t dmask = (1u << width) - 1u;
-      const uint32_t hi_pref = lowbit >= 32 ? 0u : (prefix >> lowbit);
-      for (int b = tid; b < RB; b += BT) sh.hist[b] = 0u;
-      __syncthreads();
-      for (int i = tid; i < U; i += BT) {
-        const uint32_t off = cand_key(sh.list[i]) - floor_key;
-        if ((lowbit >= 32 ? 0u : (off >> lowbit)) == hi_pref)
-          atomicAdd(&sh.hist[(off >> shift) & dmask], 1u);
-      }
-      __syncthreads();
-      select_digit_top<BT, RB / BT>(sh.hist, 1 << width, rem, sh.ru, &sh.sel_d, &sh.sel_above);
-      const uint32_t d = sh.sel_d, ab = sh.sel_above, hd = sh.hist[d];
-      __syncthreads();
-      above += ab;
-      rem -= ab;
-      prefix |= d << shift;
-      lowbit = shift;
-      if (above + hd <= static_cast<uint32_t>(cap)) break;
-    }
+    int lowbit;
+    uint32_t prefix, rem = static_cast<uint32_t>(need), above, hd;
+    radix_descend<true>(sh, U, floor_key, static_cast<uint32_t>(cap), lowbit, prefix, rem, above,
+                        hd);
     // Compact the entries >= floor + prefix to the front, in place: every
     // thread reads its entries before any is rewritten.
     const uint32_t fl2 = floor_key + prefix;
