@@ -1293,12 +1293,13 @@ __device__ int topk_probe_winner(MergeSmem& sh, int U, uint32_t kmin, float m, f
   uint32_t rec = 0u, hi = 0u;
 #pragma unroll
   for (int j = 0; j < kProbes; ++j) {
-    pl[j] = j < np ? sh.pr.logit[j] : 0xffffffffu;
+    pl[j] = __builtin_amdgcn_readfirstlane(j < np ? sh.pr.logit[j] : 0xffffffffu);
     if (j < np && (j == 0 || pl[j] > hi)) {
       rec |= 1u << j;
       hi = pl[j];
     }
   }
+  rec = __builtin_amdgcn_readfirstlane(rec);  // the same in every lane: scalar branches below
   unsigned long long acc[kProbes];
 #pragma unroll
   for (int j = 0; j < kProbes; ++j) acc[j] = 0ull;
