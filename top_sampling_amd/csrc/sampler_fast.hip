@@ -15,33 +15,41 @@
 //                 the end of the grid would leave a tail).
 // A  chunk pass   one 256-thread workgroup per (row, chunk of <= 16384
 //                 logits), the chunk held in registers (16 float4 per
-//                 thread).  Per chunk, in one pass over the loaded values:
-//                   - max, sum exp(l - max) and, for top-p-only rows, sum
-//                     exp((l - max) / T), rescaled as the maximum grows; a
-//                     NaN or +inf shows up as a NaN sum;
+//                 thread).  Per chunk:
+//                   - max, then sum exp(l - max) and, for top-p-only rows,
+//                     sum exp((l - max) / T); lanes and waves are combined by
+//                     rescaling to the larger maximum (DPP reductions); a
+//                     NaN or +inf shows up as a NaN sum or a flag;
 //                   - a logit candidate list holding at least the chunk's
 //                     share of the row's M largest, M = max(n_logprobs,
 //                     top_k) (64 for top-p-only rows): the threshold is
 //                     bounded by the q-th largest per-thread maximum (or
 //                     top-4 value) of each wave, found with one ballot per
 //                     key bit, or an LDS radix selection for large M;
-//                   - for full-vocabulary and top-p-only rows, Philox4x32-10
-//                     Gumbel keys, skipped for tokens whose uniform cannot
-//                     lift them over the running bar; every key above the
-//                     chunk's floor goes to a short key list.
+//                   - for full-vocabulary rows the chunk's best Philox4x32-10
+//                     Gumbel key (tokens whose uniform cannot lift them over
+//                     the running bar are skipped); for top-p-only rows every
+//                     key above a bar set from the chunk's own mass (about 24
+//                     on average), the passing tokens queued per wave and
+//                     their keys formed together.  Key lists hold the token,
+//                     its logit and its Philox word.
 // B  merge        one 256-thread workgroup per row: log-sum-exp; the union of
 //                 logit candidates above the highest chunk threshold is
 //                 exactly the row's logits above it.  Short prefixes (top N,
 //                 top-k up to 192, the head of a top-p row) are trimmed and
-//                 sorted in LDS; longer top-k sets are settled by count- and
-//                 mass-weighted radix selection without sorting.  Top-N,
-//                 greedy, top-k, top-p and Gumbel-max are exact on the list.
-//                 A top-p-only row whose boundary lies below the list takes
-//                 its best Gumbel keys as probes.
+//                 sorted in LDS; for longer top-k sets the k-th key comes
+//                 from radix selection and top-p from the list's best Gumbel
+//                 keys checked in key order against the top-k mass (the
+//                 mass-weighted boundary search only when none is kept).
+//                 Top-N, greedy, top-k, top-p and Gumbel-max are exact on
+//                 the list.  A top-p-only row whose boundary lies below the
+//                 list takes its best Gumbel keys as probes.
 // P  probe        chunk-parallel re-read of probe rows only: the mass of the
 //                 logits strictly above each probe's logit.  Token v is kept
 //                 by top-p iff that mass is below p times the total, so the
-//                 first probe (by key) that is kept is the Gumbel-max winner.
+//                 first probe (by key) that is kept is the Gumbel-max winner;
+//                 only probes that raise the logit maximum in key order can
+//                 be it, and only those are summed.
 // X  finish       (sampler_exact.hip) settles probe rows; rows that no fast
 //                 route settles (candidate or key overflow, top_k > 2048, no
 //                 kept probe) run the exact per-row kernel.
