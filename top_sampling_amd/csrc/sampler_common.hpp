@@ -155,6 +155,7 @@ struct FastLayout {
   int cbase[TS_MAX_SLICES + 1];  // first chunk of each slice (chunks never straddle slices)
   size_t off_ctr, off_order, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part,
       total;
+  int ordered;  // the chunk pass takes rows in the row-order pre-pass's order (else row order)
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

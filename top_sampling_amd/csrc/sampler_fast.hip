@@ -446,6 +446,7 @@ __device__ __forceinline__ int chunk_keys_topp(const float4 (&v)[AV], float cmax
 // takes them in instead (those classes first, each class in row order).
 // It also clears the exact- and probe-row counters of this call.
 constexpr int OT = 256;
+constexpr unsigned kOneRoundChunks = 1024;  // chunk workgroups resident at once (4 per CU x 256)
 
 // The four filter fields of a row's parameters in one 16-byte read (two
 // 8-byte loads: rows are 24 bytes apart), issued before any of them is
@@ -544,8 +545,13 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   // Workgroup -> (row, chunk) through the row order; a chunk's records
   // and lists sit at its own index bid = r * S + c.
   const int wg = blockIdx.x / S, c = blockIdx.x - wg * S;
-  const int r = __builtin_amdgcn_readfirstlane(
-      reinterpret_cast<const int*>(ws + lay.off_order)[wg]);
+  const int r = lay.ordered ? __builtin_amdgcn_readfirstlane(
+                                  reinterpret_cast<const int*>(ws + lay.off_order)[wg])
+                            : wg;
+  // Without the pre-pass the first workgroup clears this call's exact- and
+  // probe-row counters (the merge, which fills them, starts after this pass).
+  if (!lay.ordered && blockIdx.x == 0 && threadIdx.x < 2)
+    reinterpret_cast<int*>(ws + lay.off_ctr)[threadIdx.x] = 0;
   const int bid = r * S + c;
   const int tid = threadIdx.x, lane_id = tid & (kWave - 1), wave = tid / kWave;
   // The chunk's loads go out first, so the parameter read and the row-kind
@@ -2086,7 +2092,7 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
   for (int s = 0; s < a.lv.n; ++s) cols[s] = a.lv.off[s + 1] - a.lv.off[s];
   if (env_flag("TS_SAMPLER_EXACT") || !fast_path_supported(a.rows, cols, a.lv.n))
     return launch_sampler_finish(a, nullptr, ws, stream);
-  const FastLayout lay = make_layout(a.rows, cols, a.lv.n, a.max_logprobs);
+  FastLayout lay = make_layout(a.rows, cols, a.lv.n, a.max_logprobs);
   // float4 loads: every slice 16-byte aligned with rows and widths of whole float4s.
   int vec = 1;
   for (int s = 0; s < a.lv.n; ++s) {
@@ -2095,7 +2101,11 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
            (cols[s] % 4 == 0);
   }
   const unsigned chunks = static_cast<unsigned>(a.rows) * static_cast<unsigned>(lay.S);
-  hipLaunchKernelGGL(order_rows_kernel, dim3(1), dim3(OT), 0, stream, a, lay, ws);
+  // The row order only matters when the chunk workgroups take more than one
+  // round of the GPU (four per CU on 256 CUs); a smaller grid runs at once
+  // and skips the pre-pass launch (about 4 us, a tenth of a 64-row call).
+  lay.ordered = chunks > kOneRoundChunks ? 1 : 0;
+  if (lay.ordered) hipLaunchKernelGGL(order_rows_kernel, dim3(1), dim3(OT), 0, stream, a, lay, ws);
   if (vec)
     hipLaunchKernelGGL(chunk_pass_kernel<true>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
   else
