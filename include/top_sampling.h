@@ -16,7 +16,9 @@
  *   3. sampler_sample            -- the per-row sampler over
  *      batch x (speculative tokens + 1) rows: temperature, top-k, top-p,
  *      log-probabilities and seeded sampling (same section; the page names
- *      top-k, top-p and a non-negative max_logprobs, not their arithmetic).
+ *      top-k, top-p and a non-negative max_logprobs, not their arithmetic);
+ *   2+3. sampler_assemble_and_sample -- both in one call that reads the
+ *      received logits once.
  *
  * Conventions shared by every call
  *   - All pointers to bulk data are DEVICE pointers unless stated otherwise.
@@ -300,6 +302,34 @@ int sampler_sample_ex(const float* const* slices, const int64_t* slice_cols,
 int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* slice_cols,
                                   const int64_t* slice_ld, int32_t n_slices, int64_t rows,
                                   float* out, int64_t ld_out, void* stream);
+
+/*
+ * sampler_assemble_and_sample: sampler_assemble_vocab_slices followed by
+ * sampler_sample_ex on the same received slices, with one read of the
+ * logits instead of two.  The rank's step after the exchange on the page
+ * "Qwen4Exp batch-sharded sampling: inside vLLM PR #61018", section "What
+ * batch-sharded sampling is, in one paragraph", stitches the received
+ * vocabulary slices into its batch rows and samples them.  Here the
+ * sampler's first pass reads every logit of every row from the slices once,
+ * for its row statistics and candidates, and in the same pass writes it to
+ * `out`.
+ *   out, ld_out   as in sampler_assemble_vocab_slices: fp32
+ *                 [rows, sum slice_cols], written in full and bit-exact;
+ *                 the slices must not overlap it.
+ *   Every other argument and output, and the workspace
+ *   (sampler_workspace_bytes_slices), are as in sampler_sample_ex.
+ * `out` and the sampling outputs are those of the two calls in sequence.
+ * Shapes whose rows all take the exact per-row kernel (slices that start at
+ * a column not a multiple of 4) run the assembly kernel first instead.
+ * Arguments of both calls are validated before anything is enqueued.
+ */
+int sampler_assemble_and_sample(const float* const* slices, const int64_t* slice_cols,
+                                const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                                float* out, int64_t ld_out, const ts_row_params* params,
+                                int64_t row_offset, int32_t max_logprobs, int32_t flags,
+                                int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                                float* topn_logprobs, int32_t* row_status, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * ts_status_string: name of a TS_* return code (a static string; unknown

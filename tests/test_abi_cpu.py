@@ -287,6 +287,42 @@ def test_sampler_ex_validation():
     assert ex(ts.TS_LOGPROBS_PROCESSED) == ts.TS_EWORKSPACE
 
 
+def _assemble_sample(ptrs, cols, lds, rows=8, out=FAKE * 64, ld_out=None, flags=0,
+                     params=FAKE, max_logprobs=5, tok=FAKE, ws=None, nb=0):
+    n = len(ptrs)
+    ld_out = sum(cols) if ld_out is None else ld_out
+    P = (ctypes.c_void_p * max(n, 1))(*ptrs)
+    C = (ctypes.c_int64 * max(n, 1))(*cols)
+    L = (ctypes.c_int64 * max(n, 1))(*lds)
+    return ts.lib.sampler_assemble_and_sample(P, C, L, n, rows, out, ld_out, params, 0,
+                                              max_logprobs, flags, tok, FAKE, FAKE, FAKE, FAKE,
+                                              ws, nb, None)
+
+
+def test_assemble_and_sample_validation():
+    """Both calls' checks, every one before anything is enqueued: the
+    assembly's (output width, NULL or overlapping output) and the sampler's
+    (flags, parameters, workspace)."""
+    two = ([FAKE, FAKE * 2], [40, 60], [40, 60])
+    assert _assemble_sample([], [], []) == ts.TS_EINVAL
+    assert _assemble_sample([FAKE] * 65, [4] * 65, [4] * 65) == ts.TS_EUNSUPPORTED
+    assert _assemble_sample([FAKE, FAKE * 2], [40, -1], [40, 4]) == ts.TS_EINVAL
+    assert _assemble_sample([FAKE, None], [40, 60], [40, 60]) == ts.TS_EINVAL     # NULL slice
+    assert _assemble_sample(*two, ld_out=99) == ts.TS_EINVAL                      # ld_out < width
+    assert _assemble_sample(*two, out=None) == ts.TS_EINVAL                       # NULL out
+    assert _assemble_sample(*two, out=FAKE * 64 + 2) == ts.TS_EUNSUPPORTED        # misaligned out
+    assert _assemble_sample(*two, out=FAKE) == ts.TS_EINVAL                       # overlaps slice 0
+    assert _assemble_sample(*two, flags=2) == ts.TS_EINVAL                        # unknown flag
+    assert _assemble_sample(*two, max_logprobs=-1) == ts.TS_EINVAL
+    assert _assemble_sample(*two, params=None) == ts.TS_EINVAL
+    assert _assemble_sample(*two, tok=None) == ts.TS_EINVAL
+    assert _assemble_sample(*two) == ts.TS_EWORKSPACE                             # valid up to here
+    assert _assemble_sample(*two, flags=ts.TS_LOGPROBS_PROCESSED, ws=FAKE, nb=255) == \
+        ts.TS_EWORKSPACE
+    assert _assemble_sample(*two, rows=-1) == ts.TS_EINVAL
+    assert _assemble_sample(*two, rows=0, out=None, params=None, tok=None) == ts.TS_OK
+
+
 def test_mfma_clock_probe_validation():
     probe = ts.lib.ts_mfma_clock_probe
     rnd = ts.TS_PROBE_RANDOM_OPERANDS

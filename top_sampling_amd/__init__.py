@@ -60,6 +60,9 @@ SYMBOLS = {
     "sampler_sample_ex": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _I32, _I32, _VP,
                                          _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "sampler_assemble_vocab_slices": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _VP]),
+    "sampler_assemble_and_sample": (ctypes.c_int, [_VP, _VP, _VP, _I32, _I64, _VP, _I64, _VP, _I64,
+                                                   _I32, _I32, _VP, _VP, _VP, _VP, _VP, _VP, _SZ,
+                                                   _VP]),
     "ts_mfma_clock_probe": (ctypes.c_int, [_VP, _I32, _I64, _I32, _VP]),
     "ts_gumbel_keys": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP]),
     "ts_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -343,6 +346,38 @@ def sampler_sample_slices(slices, params, row_offset: int = 0, max_logprobs: int
         _ptr(out.topn_logprobs) if max_logprobs > 0 else None,
         _ptr(out.row_status), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
     return out
+
+
+def sampler_assemble_and_sample(slices, params, row_offset: int = 0, max_logprobs: int = 0,
+                                assembled=None, out=None, workspace=None, stream=None,
+                                processed: bool = False):
+    """``sampler_assemble_vocab_slices`` into ``assembled`` and
+    ``sampler_sample_slices`` of the same slices in one call, which reads the
+    logits once.  Returns ``(assembled, SampleOutput)``."""
+    torch = _torch()
+    n, rows, ptrs, cols, lds = _slice_arrays(slices)
+    total = sum(int(c) for c in cols)
+    if params.dtype != torch.uint8 or params.numel() != PARAMS_BYTES * rows:
+        raise ValueError("params must be rows x 24 bytes (uint8)")
+    device = slices[0].device
+    if assembled is None:
+        assembled = torch.empty(rows, total, dtype=torch.float32, device=device)
+    if assembled.shape != (rows, total) or assembled.stride(1) != 1 or \
+            assembled.dtype != torch.float32:
+        raise ValueError("assembled must be fp32 [rows, sum cols] with unit column stride")
+    if out is None:
+        out = allocate_sample_output(rows, max_logprobs, device)
+    if workspace is None:
+        nb = max(256, sampler_workspace_bytes_slices(rows, list(cols), max_logprobs))
+        workspace = torch.empty(nb, dtype=torch.uint8, device=device)
+    _check(lib.sampler_assemble_and_sample(
+        ptrs, cols, lds, n, rows, _ptr(assembled), assembled.stride(0), _ptr(params), row_offset,
+        max_logprobs, TS_LOGPROBS_PROCESSED if processed else 0,
+        _ptr(out.token_ids), _ptr(out.token_logprobs),
+        _ptr(out.topn_ids) if max_logprobs > 0 else None,
+        _ptr(out.topn_logprobs) if max_logprobs > 0 else None,
+        _ptr(out.row_status), _ptr(workspace), workspace.numel(), _stream_ptr(stream)))
+    return assembled, out
 
 
 def mfma_clock_probe(workgroups: int, iters: int, device, stream=None, random: bool = False):

@@ -181,11 +181,17 @@ size_t sampler_workspace_bytes_slices(int64_t rows, const int64_t* slice_cols, i
 namespace {
 
 // Validates everything but the logits, fills `a` and launches.
-int sample_common(ts::SamplerArgs& a, const int64_t* cols, int64_t rows, int64_t vocab,
-                  const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
-                  int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
-                  float* topn_logprobs, int32_t* row_status, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+// With `stitch` (an assembly the caller validated), the call also writes the
+// stitched batch buffer: inside the sampler's chunk pass when the call takes
+// it, else by the assembly kernel ahead of the sampler.  Either way nothing
+// is enqueued unless every argument is valid.
+static int sample_common(ts::SamplerArgs& a, const int64_t* cols, int64_t rows, int64_t vocab,
+                         const ts_row_params* params, int64_t row_offset, int32_t max_logprobs,
+                         int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                         float* topn_logprobs, int32_t* row_status, void* workspace,
+                         size_t workspace_bytes, void* stream,
+                         const ts::AssembleSlices* stitch = nullptr, float* stitch_out = nullptr,
+                         int64_t stitch_ld = 0) {
   if (max_logprobs < 0) return fail(TS_EINVAL, "max_logprobs < 0");
   if (max_logprobs > TS_MAX_LOGPROBS)
     return fail(TS_EUNSUPPORTED, "max_logprobs %d above %d", max_logprobs, TS_MAX_LOGPROBS);
@@ -212,9 +218,101 @@ int sample_common(ts::SamplerArgs& a, const int64_t* cols, int64_t rows, int64_t
   a.topn_ids = topn_ids;
   a.topn_logprobs = topn_logprobs;
   a.row_status = row_status;
+  if (stitch != nullptr) {
+    if (ts::sampler_takes_chunk_pass(rows, cols, a.lv.n)) {
+      a.asm_out = stitch_out;
+      a.asm_ld = stitch_ld;
+    } else {
+      const hipError_t ea = ts::launch_assemble(*stitch, rows, stitch_out, stitch_ld,
+                                                static_cast<hipStream_t>(stream));
+      if (ea != hipSuccess) return hip_status(ea, "assembly launch");
+    }
+  }
   const hipError_t e =
       ts::launch_sampler(a, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
   return hip_status(e, "sampler launch");
+}
+
+// The slice arrays of a sampler call into a.lv (and a.flags); *total gets the
+// summed width.
+static int sampler_view(ts::SamplerArgs& a, const float* const* slices,
+                        const int64_t* slice_cols, const int64_t* slice_ld, int32_t n_slices,
+                        int64_t rows, int32_t flags, int64_t* total_out) {
+  if (flags & ~TS_LOGPROBS_PROCESSED) return fail(TS_EINVAL, "unknown flag bits 0x%x", flags);
+  if (n_slices < 1 || n_slices > TS_MAX_SLICES)
+    return fail(n_slices < 1 ? TS_EINVAL : TS_EUNSUPPORTED, "n_slices %d not in [1, %d]",
+                n_slices, TS_MAX_SLICES);
+  if (rows < 0) return fail(TS_EINVAL, "rows < 0");
+  if (!slices || !slice_cols || !slice_ld) return fail(TS_EINVAL, "NULL slice arrays");
+  a.lv.n = n_slices;
+  a.flags = flags;
+  int64_t total = 0;
+  for (int i = 0; i < n_slices; ++i) {
+    const int64_t c = slice_cols[i];
+    if (c < 0) return fail(TS_EINVAL, "slice %d has negative width", i);
+    if (slice_ld[i] < c) return fail(TS_EINVAL, "slice %d leading dimension below its width", i);
+    if (rows > 0 && c > 0 && !slices[i]) return fail(TS_EINVAL, "slice %d is NULL", i);
+    if (slices[i] && !aligned(slices[i], 4)) return fail(TS_EUNSUPPORTED, "slice %d misaligned", i);
+    a.lv.ptr[i] = slices[i];
+    a.lv.ld[i] = slice_ld[i];
+    a.lv.off[i] = total;
+    total += c;
+    if (total > kMaxDim) return fail(TS_EUNSUPPORTED, "size above 2^31-1");
+  }
+  a.lv.off[n_slices] = total;
+  *total_out = total;
+  return TS_OK;
+}
+
+// The arguments of an assembly into s; *work is false when there is nothing
+// to copy.
+static int assembly_view(ts::AssembleSlices& s, const float* const* slices,
+                         const int64_t* slice_cols, const int64_t* slice_ld, int32_t n_slices,
+                         int64_t rows, float* out, int64_t ld_out, bool* work) {
+  *work = false;
+  if (n_slices < 1 || n_slices > TS_MAX_SLICES)
+    return fail(n_slices < 1 ? TS_EINVAL : TS_EUNSUPPORTED, "n_slices %d not in [1, %d]",
+                n_slices, TS_MAX_SLICES);
+  if (rows < 0) return fail(TS_EINVAL, "rows < 0");
+  if (!slices || !slice_cols || !slice_ld) return fail(TS_EINVAL, "NULL slice arrays");
+  s.n = n_slices;
+  int64_t total = 0;
+  bool vec4 = aligned(out, 16) && (ld_out % 4 == 0);
+  s.chunk_start[0] = 0;
+  for (int i = 0; i < n_slices; ++i) {
+    const int64_t c = slice_cols[i];
+    if (c < 0) return fail(TS_EINVAL, "slice %d has negative width", i);
+    if (slice_ld[i] < c) return fail(TS_EINVAL, "slice %d leading dimension below its width", i);
+    if (rows > 0 && c > 0 && !slices[i]) return fail(TS_EINVAL, "slice %d is NULL", i);
+    if (slices[i] && !aligned(slices[i], 4)) return fail(TS_EUNSUPPORTED, "slice %d misaligned", i);
+    s.ptr[i] = slices[i];
+    s.cols[i] = c;
+    s.ld[i] = slice_ld[i];
+    s.col_off[i] = total;
+    vec4 = vec4 && aligned(slices[i], 16) && (slice_ld[i] % 4 == 0) && (c % 4 == 0) &&
+           (total % 4 == 0);
+    s.chunk_start[i + 1] = s.chunk_start[i] + (c + ts::kAssembleChunk - 1) / ts::kAssembleChunk;
+    total += c;
+  }
+  if (ld_out < total) return fail(TS_EINVAL, "ld_out %lld below total width %lld",
+                                  (long long)ld_out, (long long)total);
+  if (rows == 0 || total == 0) return TS_OK;
+  if (!out) return fail(TS_EINVAL, "NULL out");
+  if (!aligned(out, 4)) return fail(TS_EUNSUPPORTED, "out misaligned");
+  if (s.chunk_start[n_slices] > kMaxDim) return fail(TS_EUNSUPPORTED, "too many column chunks");
+  // Slices must not overlap the output rows they are copied into.
+  const char* ob = reinterpret_cast<const char*>(out);
+  const char* oe = reinterpret_cast<const char*>(out + (rows - 1) * ld_out + total);
+  for (int i = 0; i < n_slices; ++i) {
+    if (s.cols[i] == 0) continue;
+    const char* sb = reinterpret_cast<const char*>(slices[i]);
+    const char* se =
+        reinterpret_cast<const char*>(slices[i] + (rows - 1) * slice_ld[i] + s.cols[i]);
+    if (sb < oe && ob < se) return fail(TS_EINVAL, "slice %d overlaps out", i);
+  }
+  s.vec4 = vec4 ? 1 : 0;
+  *work = true;
+  return TS_OK;
 }
 
 }  // namespace
@@ -251,32 +349,33 @@ int sampler_sample_ex(const float* const* slices, const int64_t* slice_cols,
                       int32_t flags, int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
                       float* topn_logprobs, int32_t* row_status, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  if (flags & ~TS_LOGPROBS_PROCESSED) return fail(TS_EINVAL, "unknown flag bits 0x%x", flags);
-  if (n_slices < 1 || n_slices > TS_MAX_SLICES)
-    return fail(n_slices < 1 ? TS_EINVAL : TS_EUNSUPPORTED, "n_slices %d not in [1, %d]",
-                n_slices, TS_MAX_SLICES);
-  if (rows < 0) return fail(TS_EINVAL, "rows < 0");
-  if (!slices || !slice_cols || !slice_ld) return fail(TS_EINVAL, "NULL slice arrays");
   ts::SamplerArgs a{};
-  a.lv.n = n_slices;
-  a.flags = flags;
   int64_t total = 0;
-  for (int i = 0; i < n_slices; ++i) {
-    const int64_t c = slice_cols[i];
-    if (c < 0) return fail(TS_EINVAL, "slice %d has negative width", i);
-    if (slice_ld[i] < c) return fail(TS_EINVAL, "slice %d leading dimension below its width", i);
-    if (rows > 0 && c > 0 && !slices[i]) return fail(TS_EINVAL, "slice %d is NULL", i);
-    if (slices[i] && !aligned(slices[i], 4)) return fail(TS_EUNSUPPORTED, "slice %d misaligned", i);
-    a.lv.ptr[i] = slices[i];
-    a.lv.ld[i] = slice_ld[i];
-    a.lv.off[i] = total;
-    total += c;
-    if (total > kMaxDim) return fail(TS_EUNSUPPORTED, "size above 2^31-1");
-  }
-  a.lv.off[n_slices] = total;
+  const int st = sampler_view(a, slices, slice_cols, slice_ld, n_slices, rows, flags, &total);
+  if (st != TS_OK) return st;
   return sample_common(a, slice_cols, rows, total, params, row_offset, max_logprobs, token_ids,
                        token_logprobs, topn_ids, topn_logprobs, row_status, workspace,
                        workspace_bytes, stream);
+}
+
+int sampler_assemble_and_sample(const float* const* slices, const int64_t* slice_cols,
+                                const int64_t* slice_ld, int32_t n_slices, int64_t rows,
+                                float* out, int64_t ld_out, const ts_row_params* params,
+                                int64_t row_offset, int32_t max_logprobs, int32_t flags,
+                                int32_t* token_ids, float* token_logprobs, int32_t* topn_ids,
+                                float* topn_logprobs, int32_t* row_status, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  ts::AssembleSlices s;
+  bool work = false;
+  int st = assembly_view(s, slices, slice_cols, slice_ld, n_slices, rows, out, ld_out, &work);
+  if (st != TS_OK) return st;
+  ts::SamplerArgs a{};
+  int64_t total = 0;
+  st = sampler_view(a, slices, slice_cols, slice_ld, n_slices, rows, flags, &total);
+  if (st != TS_OK) return st;
+  return sample_common(a, slice_cols, rows, total, params, row_offset, max_logprobs, token_ids,
+                       token_logprobs, topn_ids, topn_logprobs, row_status, workspace,
+                       workspace_bytes, stream, work ? &s : nullptr, out, ld_out);
 }
 
 int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
@@ -293,47 +392,10 @@ int sampler_sample_slices(const float* const* slices, const int64_t* slice_cols,
 int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* slice_cols,
                                   const int64_t* slice_ld, int32_t n_slices, int64_t rows,
                                   float* out, int64_t ld_out, void* stream) {
-  if (n_slices < 1 || n_slices > TS_MAX_SLICES)
-    return fail(n_slices < 1 ? TS_EINVAL : TS_EUNSUPPORTED, "n_slices %d not in [1, %d]",
-                n_slices, TS_MAX_SLICES);
-  if (rows < 0) return fail(TS_EINVAL, "rows < 0");
-  if (!slices || !slice_cols || !slice_ld) return fail(TS_EINVAL, "NULL slice arrays");
   ts::AssembleSlices s;
-  s.n = n_slices;
-  int64_t total = 0;
-  bool vec4 = aligned(out, 16) && (ld_out % 4 == 0);
-  s.chunk_start[0] = 0;
-  for (int i = 0; i < n_slices; ++i) {
-    const int64_t c = slice_cols[i];
-    if (c < 0) return fail(TS_EINVAL, "slice %d has negative width", i);
-    if (slice_ld[i] < c) return fail(TS_EINVAL, "slice %d leading dimension below its width", i);
-    if (rows > 0 && c > 0 && !slices[i]) return fail(TS_EINVAL, "slice %d is NULL", i);
-    if (slices[i] && !aligned(slices[i], 4)) return fail(TS_EUNSUPPORTED, "slice %d misaligned", i);
-    s.ptr[i] = slices[i];
-    s.cols[i] = c;
-    s.ld[i] = slice_ld[i];
-    s.col_off[i] = total;
-    vec4 = vec4 && aligned(slices[i], 16) && (slice_ld[i] % 4 == 0) && (c % 4 == 0) &&
-           (total % 4 == 0);
-    s.chunk_start[i + 1] = s.chunk_start[i] + (c + ts::kAssembleChunk - 1) / ts::kAssembleChunk;
-    total += c;
-  }
-  if (ld_out < total) return fail(TS_EINVAL, "ld_out %lld below total width %lld",
-                                  (long long)ld_out, (long long)total);
-  if (rows == 0 || total == 0) return TS_OK;
-  if (!out) return fail(TS_EINVAL, "NULL out");
-  if (!aligned(out, 4)) return fail(TS_EUNSUPPORTED, "out misaligned");
-  if (s.chunk_start[n_slices] > kMaxDim) return fail(TS_EUNSUPPORTED, "too many column chunks");
-  // Slices must not overlap the output rows they are copied into.
-  const char* ob = reinterpret_cast<const char*>(out);
-  const char* oe = reinterpret_cast<const char*>(out + (rows - 1) * ld_out + total);
-  for (int i = 0; i < n_slices; ++i) {
-    if (s.cols[i] == 0) continue;
-    const char* sb = reinterpret_cast<const char*>(slices[i]);
-    const char* se = reinterpret_cast<const char*>(slices[i] + (rows - 1) * slice_ld[i] + s.cols[i]);
-    if (sb < oe && ob < se) return fail(TS_EINVAL, "slice %d overlaps out", i);
-  }
-  s.vec4 = vec4 ? 1 : 0;
+  bool work = false;
+  const int st = assembly_view(s, slices, slice_cols, slice_ld, n_slices, rows, out, ld_out, &work);
+  if (st != TS_OK || !work) return st;
   const hipError_t e = ts::launch_assemble(s, rows, out, ld_out, static_cast<hipStream_t>(stream));
   return hip_status(e, "sampler_assemble_vocab_slices launch");
 }

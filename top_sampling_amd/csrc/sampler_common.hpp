@@ -156,6 +156,7 @@ struct FastLayout {
   size_t off_ctr, off_order, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part,
       total;
   int ordered;  // the chunk pass takes rows in the row-order pre-pass's order (else row order)
+  int asm_vec4;  // the stitched copy takes 16-byte stores (aligned base, ld a multiple of 4)
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

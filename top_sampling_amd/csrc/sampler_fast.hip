@@ -185,6 +185,30 @@ __device__ __forceinline__ void load_chunk(float4 (&v)[AV], const float* __restr
   }
 }
 
+// The chunk as load_chunk left it, written to dst (the stitched batch row at
+// the chunk's global column): slots past the chunk end are not written.
+// VEC4: dst 16-byte aligned and n % 4 == 0 (the chunk starts at a column that
+// is a multiple of 4).  Non-temporal stores: nothing reads them back here.
+__device__ __forceinline__ void store_chunk(const float4 (&v)[AV], float* __restrict__ dst, int n,
+                                            int tid, bool vec4) {
+  if (vec4) {
+    const int n4 = n >> 2;
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const int i4 = j * AT + tid;
+      if (i4 < n4) store_stream4(dst + 4 * i4, v[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < AV; ++j) {
+      const int e = 4 * (j * AT + tid);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (e + q < n) __builtin_nontemporal_store(lane(v[j], q), dst + e + q);
+    }
+  }
+}
+
 // (m, s, t): a maximum with sum exp(l - m) and sum exp((l - m) / T); merging
 // two rescales both sums to the larger maximum.
 __device__ __forceinline__ void merge_stats(float& m, float& s, float& t, float m2, float s2,
@@ -566,6 +590,12 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   // Row-uniform values in scalar registers, so the per-kind paths below are
   // real branches rather than flattened selects.
   const int kind = __builtin_amdgcn_readfirstlane(row_kind(p, V, a.max_logprobs));
+  // The stitched copy of the received slices, when the call asks for it:
+  // every chunk of every row, whatever route the row takes.
+  if (a.asm_out != nullptr) {
+    float* dst = a.asm_out + static_cast<int64_t>(r) * a.asm_ld + c0;
+    store_chunk(v, dst, n, tid, VEC && lay.asm_vec4);
+  }
   if (kind == KIND_BAD || kind == KIND_EXACT) return;
   ChunkRec* rec = reinterpret_cast<ChunkRec*>(ws + lay.off_chunk) + bid;
   // The temperature-scaled mass: top-p-only rows, and unfiltered rows when
@@ -2077,6 +2107,11 @@ bool env_flag(const char* name) {
 
 }  // namespace
 
+bool sampler_takes_chunk_pass(int64_t rows, const int64_t* slice_cols, int n_slices) {
+  return rows > 0 && !env_flag("TS_SAMPLER_EXACT") &&
+         fast_path_supported(rows, slice_cols, n_slices);
+}
+
 size_t sampler_workspace_size(int64_t rows, const int64_t* slice_cols, int n_slices,
                               int max_logprobs) {
   if (!fast_path_supported(rows, slice_cols, n_slices)) return 256;
@@ -2100,6 +2135,8 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
     vec &= (reinterpret_cast<uintptr_t>(a.lv.ptr[s]) % 16 == 0) && (a.lv.ld[s] % 4 == 0) &&
            (cols[s] % 4 == 0);
   }
+  lay.asm_vec4 = a.asm_out != nullptr && reinterpret_cast<uintptr_t>(a.asm_out) % 16 == 0 &&
+                 a.asm_ld % 4 == 0;
   const unsigned chunks = static_cast<unsigned>(a.rows) * static_cast<unsigned>(lay.S);
   // The row order only matters when the chunk workgroups take more than one
   // round of the GPU (four per CU on 256 CUs); a smaller grid runs at once

@@ -50,12 +50,20 @@ struct SamplerArgs {
   float* topn_logprobs;
   int32_t* row_status;    // may be null
   int flags;              // TS_LOGPROBS_PROCESSED
+  // Optional stitched copy of the logits, out[r * asm_ld + global column],
+  // written by the chunk pass as it reads them (null: none).  Only set when
+  // sampler_takes_chunk_pass() holds for the call.
+  float* asm_out;
+  int64_t asm_ld;
 };
 
 size_t sampler_workspace_size(int64_t rows, const int64_t* slice_cols, int n_slices,
                               int max_logprobs);
 hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+// Whether launch_sampler runs the chunk pass (which reads every logit once)
+// for these shapes; otherwise every row takes the exact per-row kernel.
+bool sampler_takes_chunk_pass(int64_t rows, const int64_t* slice_cols, int n_slices);
 
 // ------------------------------------------------------------------ assembly
 struct AssembleSlices {
