@@ -5,13 +5,16 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   1. lmhead_logits_local: bf16 hidden [rows, H] x lm_head [V, H] -> fp32 logits,
      written as n_slices vocabulary slices side by side (the slices the ranks
      of a tensor-parallel group each compute);
-  2. sampler_assemble_vocab_slices: the received slices stitched into the
-     batch buffer [rows, V] (receive side of the all-to-all);
-  3. sampler_sample: temperature / top-k / top-p / log-probabilities /
-     Gumbel-max sampling of every row.
-After the timed steps, sampler_sample_slices (the sampler reading the slices
-in place, with no stitching copy) is timed on its own over the same number of
-steps and reported beside the per-kernel times.
+  2+3. sampler_assemble_and_sample: the received slices stitched into the
+     batch buffer [rows, V] (receive side of the all-to-all) and
+     temperature / top-k / top-p / log-probabilities / Gumbel-max sampling of
+     every row, in one call whose first pass reads each logit once and writes
+     the stitched copy as it goes.
+After the timed steps the same work is timed the unfused way (projection,
+then sampler_assemble_vocab_slices, then sampler_sample on the stitched
+buffer), and each of those calls alone, as is sampler_sample_slices (the
+sampler reading the slices in place, with no stitched copy), each over the
+same number of steps; all of them are reported beside the step.
 Default workload: speculative decode, 128 requests x (4 draft + 1) = 640 rows,
 H = 4096, V = 151,936 (4 slices of 37,984).  --workload fp8 runs the pages'
 model shape (H = 2560, V = 248,320 in 8 slices) with an FP8 lm_head: each
@@ -319,9 +322,13 @@ def main():
         del full
     batch = torch.empty(rows, vocab, dtype=torch.float32, device=dev)
     out = ts.allocate_sample_output(rows, w.max_logprobs, dev)
+    out_unf = ts.allocate_sample_output(rows, w.max_logprobs, dev)
     ws = ts.allocate_workspace(rows, vocab, w.max_logprobs, dev)
 
-    def step(ev=None):
+    ws_sl = torch.empty(max(256, ts.sampler_workspace_bytes_slices(rows, widths, w.max_logprobs)),
+                        dtype=torch.uint8, device=dev)
+
+    def project(ev=None):
         if x is not None and w.fp8:
             ts.quantize_rows_e4m3(x, out=xq, scales=xsc, stream=stream)
             if ev is not None:
@@ -329,14 +336,41 @@ def main():
             ts.lmhead_logits_local_e4m3(xq, xsc, wq, wsc, out=local, stream=stream)
         elif x is not None:
             ts.lmhead_logits_local(x, wt, out=local, stream=stream)
+
+    def step(ev=None):
+        project(ev)
+        if ev is not None:
+            ev[0].record(stream)
+        ts.sampler_assemble_and_sample(slices, params, w.row_offset, w.max_logprobs,
+                                       assembled=batch, out=out, workspace=ws_sl, stream=stream)
+
+    def step_unfused(ev=None):
+        project()
         if ev is not None:
             ev[0].record(stream)
         ts.sampler_assemble_vocab_slices(slices, out=batch, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        ts.sampler_sample(batch, params, w.row_offset, w.max_logprobs, out=out, workspace=ws,
+        ts.sampler_sample(batch, params, w.row_offset, w.max_logprobs, out=out_unf, workspace=ws,
                           stream=stream)
 
+    # The same work unfused (projection, assembly, sampler on the stitched
+    # buffer), for comparison.  It runs before the step's warm-up and timed
+    # steps: a fresh process's first few dozen projections run slower (0.79
+    # against 0.70-0.72 ms at spec_decode) whichever form comes first, so
+    # this block takes that start-up cost.  The isolated cold medians below
+    # time both forms under the same conditions.
+    for _ in range(max(1, args.warmup)):
+        step_unfused()
+    evu = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evu:
+        e[3].record(stream)
+        step_unfused(e)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    unfused_step_ms = sum(e[3].elapsed_time(e[2]) for e in evu) / args.steps
+    asm_ms = sum(e[0].elapsed_time(e[1]) for e in evu) / args.steps
+    smp_ms = sum(e[1].elapsed_time(e[2]) for e in evu) / args.steps
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -357,12 +391,11 @@ def main():
     else:
         quant_ms = None
         gemm_ms = sum(e[3].elapsed_time(e[0]) for e in evs) / args.steps
-    asm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    smp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    fused_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
 
-    # The same slices sampled in place (no stitching copy), timed on its own.
-    ws_sl = torch.empty(max(256, ts.sampler_workspace_bytes_slices(rows, widths, w.max_logprobs)),
-                        dtype=torch.uint8, device=dev)
+    n_diff_unfused = int((out_unf.token_ids != out.token_ids).sum())
+
+    # The same slices sampled in place (no stitched copy), timed on its own.
     out_sl = ts.allocate_sample_output(rows, w.max_logprobs, dev)
 
     def sample_slices():
@@ -424,6 +457,11 @@ def main():
             iso["lmhead_gemm"] = time_alone(
                 lambda: ts.lmhead_logits_local(x, wt, out=local, stream=stream),
                 stream, scratch, args.iso_runs)
+        iso["assemble_and_sample"] = time_alone(
+            lambda: ts.sampler_assemble_and_sample(slices, params, w.row_offset, w.max_logprobs,
+                                                   assembled=batch, out=out, workspace=ws_sl,
+                                                   stream=stream),
+            stream, scratch, args.iso_runs)
         iso["assemble"] = time_alone(
             lambda: ts.sampler_assemble_vocab_slices(slices, out=batch, stream=stream),
             stream, scratch, args.iso_runs)
@@ -433,6 +471,7 @@ def main():
             stream, scratch, args.iso_runs)
         iso["sampler_slices"] = time_alone(sample_slices, stream, scratch, args.iso_runs)
         iso["step"] = time_alone(step, stream, scratch, args.iso_runs)
+        iso["step_unfused"] = time_alone(step_unfused, stream, scratch, args.iso_runs)
         del scratch
     copy_gbs = None if args.no_context else measured_copy_gbs(dev, stream)
     clock = None if args.no_context else measured_mfma_clock(ts, dev, stream)
@@ -441,6 +480,10 @@ def main():
     flops = 2.0 * rows * vocab * w.hidden if w.hidden else 0.0
     sampler_bytes = 4.0 * rows * vocab + rows * (24 + 12 + 8 * w.max_logprobs)
     asm_bytes = 2 * 4.0 * rows * vocab
+    # Fused: every logit read once from the slices and written once to the
+    # stitched buffer, plus the sampler's parameters and outputs.
+    fused_bytes = asm_bytes + sampler_bytes - 4.0 * rows * vocab
+    fused_gbs = fused_bytes / (fused_ms * 1e-3) / 1e9
     gemm_tflops = flops / (gemm_ms * 1e-3) / 1e12 if flops else None
     smp_gbs = sampler_bytes / (smp_ms * 1e-3) / 1e9
     asm_gbs = asm_bytes / (asm_ms * 1e-3) / 1e9
@@ -463,9 +506,9 @@ def main():
         roof = {"kernel": gemm_kernel, "bound": "hbm", "achieved": round(gemm_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
                 "traffic": recorded_traffic(w.name)}
-    else:
-        roof = {"kernel": "sampler", "bound": "hbm", "achieved": round(smp_gbs, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(smp_gbs / HBM_PEAK_GBS, 4),
+    else:  # sampler-only workload: the step is the fused assembly + sampler call
+        roof = {"kernel": "assemble_and_sample", "bound": "hbm", "achieved": round(fused_gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
                 "traffic": None}
 
     rps = lambda ms: round(rows / (ms * 1e-3), 1)  # noqa: E731
@@ -491,6 +534,11 @@ def main():
             gemm_kernel: {"ms": round(gemm_ms, 4), "tflops": gemm_tflops and round(gemm_tflops, 1),
                           "frac_mfma_peak": gemm_tflops and round(gemm_tflops / peak_tf, 4),
                           "rows_per_s": rps(gemm_ms)},
+            "assemble_and_sample": {"ms": round(fused_ms, 4), "gbs": round(fused_gbs, 1),
+                                    "frac_hbm_peak": round(fused_gbs / HBM_PEAK_GBS, 4),
+                                    "rows_per_s": rps(fused_ms),
+                                    "bytes": "slices read once + stitched buffer written once "
+                                             "+ parameters and outputs"},
             "assemble": {"ms": round(asm_ms, 4), "gbs": round(asm_gbs, 1),
                          "frac_hbm_peak": round(asm_gbs / HBM_PEAK_GBS, 4),
                          "rows_per_s": rps(asm_ms)},
@@ -501,7 +549,7 @@ def main():
                                "frac_hbm_peak": round(sampler_bytes / (sl_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                "rows_per_s": rps(sl_ms),
                                "saves_ms_vs_assemble_then_sample": round(asm_ms + smp_ms - sl_ms, 4),
-                               "token_ids_differing_from_stitched": n_diff},
+                               "token_ids_differing_from_step": n_diff},
             "sampler_top_k_1000_every_row": {"ms": round(topk_ms[1000], 4),
                                              "rows_per_s": rps(topk_ms[1000])},
             "sampler_top_k_2048_every_row": {"ms": round(topk_ms[2048], 4),
@@ -509,6 +557,10 @@ def main():
                                              "vs_top_k_1000": round(topk_ms[2048] / topk_ms[1000], 3)},
         },
         "roofline": roof,
+        "step_unfused": {"ms_per_step": round(unfused_step_ms, 4),
+                         "rows_per_s": rps(unfused_step_ms),
+                         "calls": "projection, sampler_assemble_vocab_slices, sampler_sample",
+                         "token_ids_differing_from_step": n_diff_unfused},
     }
     if not flops:  # sampler-only workload: there is no projection to report
         del line["kernels"][gemm_kernel]
@@ -516,13 +568,14 @@ def main():
         line["kernels"]["quantize_hidden"] = {"ms": round(quant_ms, 4), "rows_per_s": rps(quant_ms)}
     if iso:
         algo = {"lmhead_gemm": gemm_bytes, "lmhead_e4m3": gemm_bytes, "assemble": asm_bytes,
-                "sampler": sampler_bytes, "sampler_slices": sampler_bytes}
+                "sampler": sampler_bytes, "sampler_slices": sampler_bytes,
+                "assemble_and_sample": fused_bytes}
         for k, st in iso.items():
             if k in algo and algo[k]:
                 st["gbs_median"] = round(algo[k] / (st["median_ms"] * 1e-3) / 1e9, 1)
             if k in ("lmhead_gemm", "lmhead_e4m3") and flops:
                 st["tflops_median"] = round(flops / (st["median_ms"] * 1e-3) / 1e12, 1)
-            if k == "step":
+            if k in ("step", "step_unfused"):
                 st["rows_per_s_median"] = round(rows / (st["median_ms"] * 1e-3), 1)
         line["isolated_cold"] = {"runs": args.iso_runs, "warmup": 5,
                                  "scratch_write_bytes": 512 << 20, "kernels": iso}
