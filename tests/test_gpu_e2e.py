@@ -1,10 +1,12 @@
 """End to end on the GPU's own logits, at full size.
 
 One rank's step exactly as the bench times it: the projection writes the
-whole vocabulary into a local buffer, four column slices of it (the slices
-tensor-parallel ranks would exchange) are stitched into the batch buffer, and
-the sampler runs on that buffer (and, in place, on the slices).  The logits
-the sampler saw are copied back and the CPU oracle samples exactly those
+whole vocabulary into a local buffer; four column slices of it (the slices
+tensor-parallel ranks would exchange) are stitched into the batch buffer
+inside the sampler's first pass (sampler_assemble_and_sample).  The same
+slices also go through the separate assembly and the sampler on the stitched
+buffer, and through the sampler in place on the slices.  The logits the
+sampler saw are copied back and the CPU oracle samples exactly those
 values (page "Qwen4Exp batch-sharded sampling: inside vLLM PR #61018",
 section "What batch-sharded sampling is, in one paragraph": the rank projects
 its slice, the slices are swapped, and each rank samples its rows).
@@ -111,11 +113,18 @@ def test_step_end_to_end_on_gpu_logits(dev, ts, name, tmp_path):
     p = ts.params_to_device(params, dev)
     out = ts.sampler_sample(batch, p, 0, w.max_logprobs)
     out_sl = ts.sampler_sample_slices(slices, p, 0, w.max_logprobs)
+    fused_batch, out_f = ts.sampler_assemble_and_sample(slices, p, 0, w.max_logprobs)
     torch.cuda.synchronize()
     got = {k: getattr(out, k).cpu().numpy() for k in FIELDS}
     got_sl = {k: getattr(out_sl, k).cpu().numpy() for k in FIELDS}
+    got_f = {k: getattr(out_f, k).cpu().numpy() for k in FIELDS}
     logits = batch.cpu().numpy()
     assert np.array_equal(logits.view(np.uint32), local.cpu().numpy().view(np.uint32))
+    # The one-call step: its stitched buffer is the assembly's, bit for bit,
+    # and it samples exactly what the slice sampler samples.
+    assert np.array_equal(fused_batch.cpu().numpy().view(np.uint32), logits.view(np.uint32))
+    for k in FIELDS:
+        assert np.array_equal(got_f[k].view(np.uint8), got_sl[k].view(np.uint8)), k
     # The in-place slice sampler draws what the stitched call draws.  Its
     # chunks follow the slice boundaries, so sums (and the log-probabilities)
     # may differ in the last bits.
@@ -141,6 +150,8 @@ def test_step_end_to_end_on_gpu_logits(dev, ts, name, tmp_path):
         f"(top-p {int(res.flag_top_p.sum())}, ties {int(res.flag_tie.sum())})")
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
              res.row_status, flagged, lse, logits, label=f"e2e/{name}")
+    _compare(got_f, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, flagged, lse, logits, label=f"e2e/{name}/one-call")
     # fp32 keys of each row's two best kept keys against float64
     r, c, gk = _gpu_keys(ts, dev, logits, params, 0, top_ids)
     if r.size:

@@ -43,7 +43,10 @@ def _bits(t):
     return t.view(torch.int32) if t.dtype == torch.float32 else t
 
 
-def test_step_graph_replays(dev, ts):
+@pytest.mark.parametrize("one_call", [False, True])
+def test_step_graph_replays(dev, ts, one_call):
+    """one_call: assembly and sampler through sampler_assemble_and_sample (the
+    bench's step); else the assembly kernel, then the sampler on the buffer."""
     import torch
 
     rng = np.random.default_rng(31)
@@ -58,6 +61,9 @@ def test_step_graph_replays(dev, ts):
     slices = [torch.empty(rows, w, device=dev) for w in widths]
     batch = torch.empty(rows, V, device=dev)
     ws = ts.allocate_workspace(rows, V, max_lp, dev)
+    if one_call:
+        ws = torch.empty(max(256, ts.sampler_workspace_bytes_slices(rows, widths, max_lp)),
+                         dtype=torch.uint8, device=dev)
     out = ts.allocate_sample_output(rows, max_lp, dev)
 
     def step():
@@ -66,10 +72,15 @@ def test_step_graph_replays(dev, ts):
         for s, w in zip(slices, widths):  # the exchange's delivery, as device copies
             s.copy_(local[:, c0:c0 + w])
             c0 += w
-        ts.sampler_assemble_vocab_slices(slices, out=batch)
-        ts.sampler_sample(batch, params, row_offset=3, max_logprobs=max_lp, out=out, workspace=ws)
+        if one_call:
+            ts.sampler_assemble_and_sample(slices, params, 3, max_lp, assembled=batch, out=out,
+                                           workspace=ws)
+        else:
+            ts.sampler_assemble_vocab_slices(slices, out=batch)
+            ts.sampler_sample(batch, params, row_offset=3, max_logprobs=max_lp, out=out,
+                              workspace=ws)
 
-    say("graph: eager step", rows, H, V)
+    say("graph: eager step", rows, H, V, "one call" if one_call else "two calls")
     step()
     torch.cuda.synchronize()
     ref_logits = batch.clone()
