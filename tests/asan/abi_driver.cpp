@@ -91,6 +91,27 @@ int main() {
          TS_EINVAL, "assemble ld_out");
   expect(sampler_assemble_vocab_slices(ptrs, cols, lds, 0, 8, Ff, 100, nullptr), TS_EINVAL,
          "assemble 0 slices");
+  // the one-call assembly + sampler: both tables walked, nothing enqueued
+  float* wide = Ff + 1024 * 1024 * (TS_MAX_SLICES + 2);
+  expect(sampler_assemble_and_sample(ptrs, cols, lds, TS_MAX_SLICES, 8, wide,
+                                     TS_MAX_SLICES * 2374, Fp, 0, 5, 0, Fi, Ff, Fi, Ff, Fi,
+                                     nullptr, 0, nullptr), TS_EWORKSPACE, "one call 64");
+  expect(sampler_assemble_and_sample(ptrs, cols, lds, TS_MAX_SLICES + 1, 8, wide,
+                                     (TS_MAX_SLICES + 1) * 2374, Fp, 0, 5, 0, Fi, Ff, Fi, Ff, Fi,
+                                     nullptr, 0, nullptr), TS_EUNSUPPORTED, "one call 65");
+  expect(sampler_assemble_and_sample(ptrs, cols, lds, 4, 8, nullptr, 4 * 2374, Fp, 0, 5, 0, Fi,
+                                     Ff, Fi, Ff, Fi, nullptr, 0, nullptr), TS_EINVAL,
+         "one call null out");
+  expect(sampler_assemble_and_sample(ptrs, cols, lds, 4, 8, wide, 100, Fp, 0, 5, 0, Fi, Ff, Fi,
+                                     Ff, Fi, nullptr, 0, nullptr), TS_EINVAL, "one call ld_out");
+  expect(sampler_assemble_and_sample(ptrs, cols, lds, 4, 8, const_cast<float*>(ptrs[1]),
+                                     4 * 2374, Fp, 0, 5, 0, Fi, Ff, Fi, Ff, Fi, nullptr, 0,
+                                     nullptr), TS_EINVAL, "one call overlap");
+  expect(sampler_assemble_and_sample(ptrs, cols, lds, 4, 8, wide, 4 * 2374, Fp, 0, 5, 4, Fi, Ff,
+                                     Fi, Ff, Fi, nullptr, 0, nullptr), TS_EINVAL, "one call flags");
+  expect(sampler_assemble_and_sample(ptrs, cols, lds, 4, 0, nullptr, 4 * 2374, nullptr, 0, 5, 0,
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                                     nullptr), TS_OK, "one call empty");
 
   // workspace arithmetic over many shapes (host only)
   const int64_t rows_list[] = {0, 1, 3, 64, 640, 1024, 4096, 65536};
