@@ -149,7 +149,8 @@ struct ProbeRec {  // a top-p-only row whose boundary lies below the listed logi
 
 struct FastLayout {
   int S;  // chunks per row
-  int L;  // logits per chunk (multiple of 4; a slice's last chunk may be shorter)
+  int L;  // the longest chunk (logits, a multiple of 4)
+  int Ls[TS_MAX_SLICES];  // chunk length in slice s (a multiple of 4; its last chunk may be shorter)
   int cc;  // candidate slots per chunk (cand_slots)
   int nsl;                      // column slices
   int cbase[TS_MAX_SLICES + 1];  // first chunk of each slice (chunks never straddle slices)
@@ -207,14 +208,22 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n, int max_
   }
   L = (L + 3) / 4 * 4;
   if (L < 4) L = 4;
-  l.L = static_cast<int>(L);
   l.nsl = n;
-  int64_t total = 0;
+  // A slice takes as many chunks as the target length L needs, of equal
+  // length (a slice of 37,984 at L = 15,194: three of 12,664, not two full
+  // chunks and one half-empty one).
+  int64_t total = 0, longest = 4;
   l.cbase[0] = 0;
   for (int s = 0; s < n; ++s) {
-    total += (cols[s] + L - 1) / L;
+    const int64_t k = cols[s] > 0 ? (cols[s] + L - 1) / L : 0;
+    int64_t Ls = k > 0 ? ((cols[s] + k - 1) / k + 3) / 4 * 4 : 4;
+    if (Ls > L) Ls = L;
+    l.Ls[s] = static_cast<int>(Ls);
+    if (Ls > longest) longest = Ls;
+    total += (cols[s] + Ls - 1) / Ls;
     l.cbase[s + 1] = static_cast<int>(total < (1 << 30) ? total : (1 << 30));
   }
+  l.L = static_cast<int>(longest);
   l.S = (L > kChunkMax || total > kMaxChunks || n >= kMaxChunks || total < 1)
             ? 0
             : static_cast<int>(total);
@@ -285,10 +294,10 @@ __device__ __forceinline__ ChunkGeo chunk_geo(const LogitsView& lv, const FastLa
                                               int c) {
   int s = 0;
   while (s + 1 < lay.nsl && c >= lay.cbase[s + 1]) ++s;
-  const int c0 = (c - lay.cbase[s]) * lay.L;
+  const int c0 = (c - lay.cbase[s]) * lay.Ls[s];
   const int cols = static_cast<int>(lv.off[s + 1] - lv.off[s]);
   ChunkGeo g;
-  g.n = min(lay.L, cols - c0);
+  g.n = min(lay.Ls[s], cols - c0);
   g.gofs = static_cast<int>(lv.off[s]) + c0;
   g.src = lv.ptr[s] + static_cast<int64_t>(r) * lv.ld[s] + c0;
   return g;
