@@ -318,7 +318,12 @@ int sampler_assemble_vocab_slices(const float* const* slices, const int64_t* sli
  *                 the slices must not overlap it.
  *   Every other argument and output, and the workspace
  *   (sampler_workspace_bytes_slices), are as in sampler_sample_ex.
- * `out` and the sampling outputs are those of the two calls in sequence.
+ * `out` is exactly what sampler_assemble_vocab_slices writes.  The sampling
+ * outputs follow the same definitions as sampler_sample_ex; the call may cut
+ * the rows into narrower chunks (8 instead of 16 float4 per thread when
+ * that keeps at most 24 chunks per row, which overlaps the extra copy
+ * traffic better), so fp32 sums and the log-probabilities may differ from
+ * sampler_sample_ex's in the last bits.
  * Shapes whose rows all take the exact per-row kernel (slices that start at
  * a column not a multiple of 4) run the assembly kernel first instead.
  * Arguments of both calls are validated before anything is enqueued.

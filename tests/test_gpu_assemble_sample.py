@@ -1,7 +1,7 @@
 """GPU parity of sampler_assemble_and_sample: the stitched batch buffer is the
 received slices bit for bit (every row, whatever route the sampler takes for
-it), and the sampling outputs are the oracle's, exactly as for the separate
-assembly and slice-sampler calls (same bars as test_gpu_parity)."""
+it), and the sampling outputs are the oracle's to the bars of test_gpu_parity,
+with the same token ids, top-N ids and row status as the slice sampler."""
 import numpy as np
 import pytest
 
@@ -61,8 +61,17 @@ def _check_assembled(wide, logits_np, ld_out_extra):
 
 
 def _same_outputs(got, sep):
-    for k in FIELDS:
-        assert np.array_equal(got[k].view(np.uint8), sep[k].view(np.uint8)), k
+    """The one-call sampler draws what the slice sampler draws.  It may cut
+    the rows into narrower chunks, so its fp32 sums (and log-probabilities)
+    may round differently in the last bits."""
+    for k in ("token_ids", "topn_ids", "row_status"):
+        assert np.array_equal(got[k], sep[k]), k
+    for k in ("token_logprobs", "topn_logprobs"):
+        a, b = got[k], sep[k]
+        assert np.array_equal(np.isfinite(a), np.isfinite(b)), k
+        assert np.array_equal(np.isnan(a), np.isnan(b)), k
+        fin = np.isfinite(a)
+        assert np.abs(a[fin] - b[fin]).max(initial=0) <= 1e-5, k
 
 
 @pytest.mark.parametrize("name,n", [("spec_decode", 4), ("rank_share", 0), ("fp8", 0)])

@@ -121,10 +121,16 @@ def test_step_end_to_end_on_gpu_logits(dev, ts, name, tmp_path):
     logits = batch.cpu().numpy()
     assert np.array_equal(logits.view(np.uint32), local.cpu().numpy().view(np.uint32))
     # The one-call step: its stitched buffer is the assembly's, bit for bit,
-    # and it samples exactly what the slice sampler samples.
+    # and it draws what the slice sampler draws (its chunks may be narrower,
+    # so the log-probabilities may differ in the last bits).
     assert np.array_equal(fused_batch.cpu().numpy().view(np.uint32), logits.view(np.uint32))
-    for k in FIELDS:
-        assert np.array_equal(got_f[k].view(np.uint8), got_sl[k].view(np.uint8)), k
+    for k in ("token_ids", "topn_ids", "row_status"):
+        assert np.array_equal(got_f[k], got_sl[k]), k
+    for k in ("token_logprobs", "topn_logprobs"):
+        a, b = got_f[k], got_sl[k]
+        assert np.array_equal(np.isfinite(a), np.isfinite(b)), k
+        fin = np.isfinite(a)
+        assert np.abs(a[fin] - b[fin]).max(initial=0) <= 1e-5, k
     # The in-place slice sampler draws what the stitched call draws.  Its
     # chunks follow the slice boundaries, so sums (and the log-probabilities)
     # may differ in the last bits.

@@ -106,6 +106,7 @@ constexpr int kProbes = 8;        // probe points per top-p-only row
 constexpr int kMaxChunks = 128;   // chunks per row
 constexpr int kChunkThreads = 256;
 constexpr int kChunkVec = 16;     // float4 per thread
+constexpr int kChunkVecNarrow = 8;  // float4 per thread in a narrow chunk
 constexpr int kChunkMax = kChunkThreads * kChunkVec * 4;  // 16384 logits
 constexpr int kListMax = 4096;    // merged candidates a row may keep in LDS
 constexpr float kKeyMargin = 1e-4f;  // rounding margin between chunk-local and row keys
@@ -156,6 +157,7 @@ struct FastLayout {
   int cbase[TS_MAX_SLICES + 1];  // first chunk of each slice (chunks never straddle slices)
   size_t off_ctr, off_order, off_exact, off_probe, off_chunk, off_cand, off_key, off_prec, off_part,
       total;
+  int vec;      // float4 per thread of the chunk pass (kChunkVec or kChunkVecNarrow)
   int ordered;  // the chunk pass takes rows in the row-order pre-pass's order (else row order)
   int asm_vec4;  // the stitched copy takes 16-byte stores (aligned base, ld a multiple of 4)
 };
@@ -189,11 +191,14 @@ inline int cand_slots(int L, int S, int max_logprobs) {
   return static_cast<int>(cc < L ? cc : L);
 }
 
-inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n, int max_logprobs) {
+inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n, int max_logprobs,
+                              int vec = kChunkVec) {
   FastLayout l{};
+  l.vec = vec;
+  const int64_t chunk_max = static_cast<int64_t>(kChunkThreads) * vec * 4;
   int64_t vocab = 0;
   for (int s = 0; s < n; ++s) vocab += cols[s];
-  int64_t S = (vocab + kChunkMax - 1) / kChunkMax;
+  int64_t S = (vocab + chunk_max - 1) / chunk_max;
   int64_t want = rows > 0 ? (kWantChunks + rows - 1) / rows : 1;
   int64_t most = vocab / 1024 > 0 ? vocab / 1024 : 1;
   if (want > most) want = most;
@@ -224,7 +229,7 @@ inline FastLayout make_layout(int64_t rows, const int64_t* cols, int n, int max_
     l.cbase[s + 1] = static_cast<int>(total < (1 << 30) ? total : (1 << 30));
   }
   l.L = static_cast<int>(longest);
-  l.S = (L > kChunkMax || total > kMaxChunks || n >= kMaxChunks || total < 1)
+  l.S = (L > chunk_max || total > kMaxChunks || n >= kMaxChunks || total < 1)
             ? 0
             : static_cast<int>(total);
   l.cc = cand_slots(l.L, l.S > 0 ? l.S : 1, max_logprobs);

@@ -62,7 +62,6 @@ namespace {
 
 constexpr int AT = kChunkThreads;
 constexpr int AW = AT / kWave;
-constexpr int AV = kChunkVec;
 constexpr int RB = 2048;
 constexpr int BT = 256;
 constexpr int BW = BT / kWave;
@@ -156,13 +155,13 @@ __device__ __forceinline__ void set_lane(float4& f, int q, float x) {
 // unconditionally (out-of-range slots re-read the chunk's last element), so
 // all sixteen are in flight together, as non-temporal (streaming) loads.
 // VEC: 16-byte aligned rows and n % 4 == 0.
-template <bool VEC>
-__device__ __forceinline__ void load_chunk(float4 (&v)[AV], const float* __restrict__ src, int n,
+template <bool VEC, int AVW>
+__device__ __forceinline__ void load_chunk(float4 (&v)[AVW], const float* __restrict__ src, int n,
                                            int tid) {
   if (VEC) {
     const int n4 = n >> 2;
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
+    for (int j = 0; j < AVW; ++j) {
       const int i4 = j * AT + tid;
       const bool ok = i4 < n4;
       const float4 f = load_stream4(src + 4 * (ok ? i4 : n4 - 1));
@@ -173,7 +172,7 @@ __device__ __forceinline__ void load_chunk(float4 (&v)[AV], const float* __restr
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
+    for (int j = 0; j < AVW; ++j) {
       const int e = 4 * (j * AT + tid);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -189,18 +188,19 @@ __device__ __forceinline__ void load_chunk(float4 (&v)[AV], const float* __restr
 // the chunk's global column): slots past the chunk end are not written.
 // VEC4: dst 16-byte aligned and n % 4 == 0 (the chunk starts at a column that
 // is a multiple of 4).  Non-temporal stores: nothing reads them back here.
-__device__ __forceinline__ void store_chunk(const float4 (&v)[AV], float* __restrict__ dst, int n,
+template <int AVW>
+__device__ __forceinline__ void store_chunk(const float4 (&v)[AVW], float* __restrict__ dst, int n,
                                             int tid, bool vec4) {
   if (vec4) {
     const int n4 = n >> 2;
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
+    for (int j = 0; j < AVW; ++j) {
       const int i4 = j * AT + tid;
       if (i4 < n4) store_stream4(dst + 4 * i4, v[j]);
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
+    for (int j = 0; j < AVW; ++j) {
       const int e = 4 * (j * AT + tid);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
@@ -293,18 +293,23 @@ __device__ __forceinline__ float4 blend4(uint32_t m, const float4& a, const floa
 
 // Element b (= 4 j + q) of the thread's chunk registers, for a per-lane b: a
 // blend tree over j, then over q.
-__device__ __forceinline__ float pick_logit(const float4 (&v)[AV], int b) {
-  static_assert(AV == 16, "the blend tree is written for 16 float4 per thread");
+template <int AVW>
+__device__ __forceinline__ float pick_logit(const float4 (&v)[AVW], int b) {
+  static_assert(AVW == 16 || AVW == 8, "the blend tree is written for 8 or 16 float4 per thread");
   const uint32_t m0 = 0u - ((b >> 2) & 1u), m1 = 0u - ((b >> 3) & 1u),
                  m2 = 0u - ((b >> 4) & 1u), m3 = 0u - ((b >> 5) & 1u);
-  float4 l1[8], l2[4], l3[2];
+  float4 l1[AVW / 2], l2[AVW / 4], l3[AVW / 8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) l1[i] = blend4(m0, v[2 * i + 1], v[2 * i]);
+  for (int i = 0; i < AVW / 2; ++i) l1[i] = blend4(m0, v[2 * i + 1], v[2 * i]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) l2[i] = blend4(m1, l1[2 * i + 1], l1[2 * i]);
+  for (int i = 0; i < AVW / 4; ++i) l2[i] = blend4(m1, l1[2 * i + 1], l1[2 * i]);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) l3[i] = blend4(m2, l2[2 * i + 1], l2[2 * i]);
-  const float4 f = blend4(m3, l3[1], l3[0]);
+  for (int i = 0; i < AVW / 8; ++i) l3[i] = blend4(m2, l2[2 * i + 1], l2[2 * i]);
+  float4 f;
+  if constexpr (AVW == 16)
+    f = blend4(m3, l3[1], l3[0]);
+  else
+    f = l3[0];
   const uint32_t q0 = 0u - (b & 1u), q1 = 0u - ((b >> 1) & 1u);
   return bit_blend(q1, bit_blend(q0, f.w, f.z), bit_blend(q0, f.y, f.x));
 }
@@ -330,7 +335,8 @@ __device__ __forceinline__ uint32_t u_floor_bits(float xm, float bar) {
 // key is at least the smallest Gumbel value, the bar's start).  Every
 // thread of the workgroup calls it, with sh.nkey zero.  Returns the number
 // of keys listed (1, or 0 for an all-padding chunk); kfloor is the key.
-__device__ __forceinline__ int chunk_best_key(const float4 (&v)[AV], float cmax, float inv_t,
+template <int AVW>
+__device__ __forceinline__ int chunk_best_key(const float4 (&v)[AVW], float cmax, float inv_t,
                                               uint64_t seed, uint64_t grow, int c0,
                                               KeyRec* __restrict__ klist_out, ChunkSmem& sh,
                                               float& kfloor) {
@@ -340,7 +346,7 @@ __device__ __forceinline__ int chunk_best_key(const float4 (&v)[AV], float cmax,
   uint32_t kw = 0u;
   float wbar = kMinGumbel;
 #pragma unroll
-  for (int j = 0; j < AV; ++j) {
+  for (int j = 0; j < AVW; ++j) {
     const int e = 4 * (j * AT + tid);
     float x[4];
 #pragma unroll
@@ -364,7 +370,8 @@ __device__ __forceinline__ int chunk_best_key(const float4 (&v)[AV], float cmax,
       }
     }
     // Refreshed early and then less often: the bar rises fastest at first.
-    if (j == 0 || j == 1 || j == 3 || j == 7 || j == 11) wbar = fmaxf(wbar, wave_max_uniform(kb));
+    if (j == 0 || j == 1 || j == 3 || j == (AVW == 16 ? 7 : 5) || j == 11)
+      wbar = fmaxf(wbar, wave_max_uniform(kb));
   }
   const int mine = ib;
   block_best<AT>(kb, ib, sh.rf, sh.ri);
@@ -390,7 +397,8 @@ __device__ __forceinline__ int chunk_best_key(const float4 (&v)[AV], float cmax,
 // tokens rather than whenever one lane's token passes.  Every thread of the
 // workgroup calls it, with sh.nkey zero.  Returns the number of keys (above
 // kKeyCap: overflow, the list is not written); kfloor = B.
-__device__ __forceinline__ int chunk_keys_topp(const float4 (&v)[AV], float cmax, float inv_t,
+template <int AVW>
+__device__ __forceinline__ int chunk_keys_topp(const float4 (&v)[AVW], float cmax, float inv_t,
                                                float tmass, uint64_t seed, uint64_t grow, int c0,
                                                KeyRec* __restrict__ klist_out, ChunkSmem& sh,
                                                float& kfloor) {
@@ -421,7 +429,7 @@ __device__ __forceinline__ int chunk_keys_topp(const float4 (&v)[AV], float cmax
     qn = 0;
   };
 #pragma unroll
-  for (int j = 0; j < AV; ++j) {
+  for (int j = 0; j < AVW; ++j) {
     if (qn > kQueueCap - 4 * kWave) drain();
     const int e = 4 * (j * AT + tid);
     float x[4];
@@ -561,8 +569,8 @@ __global__ __launch_bounds__(OT) void order_rows_kernel(SamplerArgs a, FastLayou
   }
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLayout lay,
+template <bool VEC, int AVW>
+__global__ __launch_bounds__(AT, AVW == 16 ? 4 : 6) void chunk_pass_kernel(SamplerArgs a, FastLayout lay,
                                                         uint8_t* __restrict__ ws) {
   __shared__ ChunkSmem sh;
   const int S = lay.S;
@@ -583,8 +591,8 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   const ChunkGeo geo = chunk_geo(a.lv, lay, r, c);
   const int c0 = geo.gofs;  // global column of the chunk's first logit
   const int n = geo.n;
-  float4 v[AV];
-  load_chunk<VEC>(v, geo.src, n, tid);
+  float4 v[AVW];
+  load_chunk<VEC, AVW>(v, geo.src, n, tid);
   const ts_row_params p = a.params[r];
   const int V = a.vocab;
   // Row-uniform values in scalar registers, so the per-kind paths below are
@@ -618,7 +626,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   const float sc = inv_t * kLog2e;
   if (tk == 4) {
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
+    for (int j = 0; j < AVW; ++j) {
       const float4 f = v[j];
       lm = fmaxf(lm, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
 #pragma unroll
@@ -634,7 +642,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     }
   } else if (tk == 2) {
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
+    for (int j = 0; j < AVW; ++j) {
       const float4 f = v[j];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -646,7 +654,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     lm = t[0];
   } else {
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
+    for (int j = 0; j < AVW; ++j) {
       const float4 f = v[j];
       lm = fmaxf(lm, fmaxf(fmaxf(f.x, f.y), fmaxf(f.z, f.w)));
     }
@@ -659,14 +667,14 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
     // value but not the same instruction, so the compiler does not keep the
     // first loop's 64 differences alive for the second.
 #pragma unroll
-    for (int j = 0; j < AV; ++j) {
+    for (int j = 0; j < AVW; ++j) {
       const float4 f = v[j];
       ls += fast_exp(f.x - lm) + fast_exp(f.y - lm) + fast_exp(f.z - lm) + fast_exp(f.w - lm);
     }
     if (topp) {
       const float nsc = -sc;
 #pragma unroll
-      for (int j = 0; j < AV; ++j) {
+      for (int j = 0; j < AVW; ++j) {
         const float4 f = v[j];
         lt += __builtin_amdgcn_exp2f((lm - f.x) * nsc) + __builtin_amdgcn_exp2f((lm - f.y) * nsc) +
               __builtin_amdgcn_exp2f((lm - f.z) * nsc) + __builtin_amdgcn_exp2f((lm - f.w) * nsc);
@@ -677,7 +685,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   int flag = lm == INFINITY ? 1 : 0;
   if (lm == -INFINITY) {
 #pragma unroll
-    for (int j = 0; j < AV; ++j)
+    for (int j = 0; j < AVW; ++j)
       flag |= (isnan(v[j].x) || isnan(v[j].y) || isnan(v[j].z) || isnan(v[j].w)) ? 1 : 0;
   }
   // The wave's statistics: its maximum by DPP, each lane's sums rescaled to
@@ -750,7 +758,7 @@ __global__ __launch_bounds__(AT, 4) void chunk_pass_kernel(SamplerArgs a, FastLa
   // candidate costs no LDS round trip.
   unsigned long long cm = 0ull;  // bit 4j + q: lane q of v[j] is a candidate
 #pragma unroll
-  for (int j = 0; j < AV; ++j) {
+  for (int j = 0; j < AVW; ++j) {
     const int e = 4 * (j * AT + tid);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -2112,10 +2120,32 @@ bool sampler_takes_chunk_pass(int64_t rows, const int64_t* slice_cols, int n_sli
          fast_path_supported(rows, slice_cols, n_slices);
 }
 
+// The chunk width of a call: narrow chunks (twice the chunk workgroups, six
+// per CU instead of four) when the call also writes the stitched copy and
+// the narrow layout stays short.  The copy doubles the chunk pass's memory
+// traffic, and more resident workgroups overlap it with the arithmetic
+// better, but twice the chunks make the merge's union of chunk lists twice as
+// long.  Measured on MI355X (assembly + sampler): four 37,984-column slices,
+// 20 narrow chunks per row: 0.186 against 0.197 ms at 640 rows, 0.101 against
+// 0.108 ms at 256 rows; eight 31,040-column slices, 32 chunks: 0.329 against
+// 0.292 ms.
+constexpr int kNarrowMaxChunks = 24;
+
+FastLayout call_layout(int64_t rows, const int64_t* cols, int n, int max_logprobs, bool stitch) {
+  if (stitch) {
+    const FastLayout narrow = make_layout(rows, cols, n, max_logprobs, kChunkVecNarrow);
+    if (narrow.S > 0 && narrow.S <= kNarrowMaxChunks) return narrow;
+  }
+  return make_layout(rows, cols, n, max_logprobs, kChunkVec);
+}
+
 size_t sampler_workspace_size(int64_t rows, const int64_t* slice_cols, int n_slices,
                               int max_logprobs) {
   if (!fast_path_supported(rows, slice_cols, n_slices)) return 256;
-  return make_layout(rows, slice_cols, n_slices, max_logprobs).total;
+  // Either layout a call may take fits.
+  const size_t wide = call_layout(rows, slice_cols, n_slices, max_logprobs, false).total;
+  const size_t any = call_layout(rows, slice_cols, n_slices, max_logprobs, true).total;
+  return wide > any ? wide : any;
 }
 
 hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspace_bytes,
@@ -2127,7 +2157,7 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
   for (int s = 0; s < a.lv.n; ++s) cols[s] = a.lv.off[s + 1] - a.lv.off[s];
   if (env_flag("TS_SAMPLER_EXACT") || !fast_path_supported(a.rows, cols, a.lv.n))
     return launch_sampler_finish(a, nullptr, ws, stream);
-  FastLayout lay = make_layout(a.rows, cols, a.lv.n, a.max_logprobs);
+  FastLayout lay = call_layout(a.rows, cols, a.lv.n, a.max_logprobs, a.asm_out != nullptr);
   // float4 loads: every slice 16-byte aligned with rows and widths of whole float4s.
   int vec = 1;
   for (int s = 0; s < a.lv.n; ++s) {
@@ -2143,10 +2173,21 @@ hipError_t launch_sampler(const SamplerArgs& a, void* workspace, size_t workspac
   // and skips the pre-pass launch (about 4 us, a tenth of a 64-row call).
   lay.ordered = chunks > kOneRoundChunks ? 1 : 0;
   if (lay.ordered) hipLaunchKernelGGL(order_rows_kernel, dim3(1), dim3(OT), 0, stream, a, lay, ws);
-  if (vec)
-    hipLaunchKernelGGL(chunk_pass_kernel<true>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
-  else
-    hipLaunchKernelGGL(chunk_pass_kernel<false>, dim3(chunks), dim3(AT), 0, stream, a, lay, ws);
+  if (lay.vec == kChunkVecNarrow) {
+    if (vec)
+      hipLaunchKernelGGL((chunk_pass_kernel<true, kChunkVecNarrow>), dim3(chunks), dim3(AT), 0,
+                         stream, a, lay, ws);
+    else
+      hipLaunchKernelGGL((chunk_pass_kernel<false, kChunkVecNarrow>), dim3(chunks), dim3(AT), 0,
+                         stream, a, lay, ws);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((chunk_pass_kernel<true, kChunkVec>), dim3(chunks), dim3(AT), 0, stream,
+                         a, lay, ws);
+    else
+      hipLaunchKernelGGL((chunk_pass_kernel<false, kChunkVec>), dim3(chunks), dim3(AT), 0, stream,
+                         a, lay, ws);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int force = env_flag("TS_SAMPLER_FORCE_PROBE") ? 1 : 0;
