@@ -151,7 +151,7 @@ struct ProbeRec {  // a top-p-only row whose boundary lies below the listed logi
 struct FastLayout {
   int S;  // chunks per row
   int L;  // the longest chunk (logits, a multiple of 4)
-  int Ls[TS_MAX_SLICES];  // chunk length in slice s (a multiple of 4; its last chunk may be shorter)
+  int Ls[TS_MAX_SLICES];  // chunk length in slice s (multiple of 4; its last chunk may be shorter)
   int cc;  // candidate slots per chunk (cand_slots)
   int nsl;                      // column slices
   int cbase[TS_MAX_SLICES + 1];  // first chunk of each slice (chunks never straddle slices)
@@ -164,9 +164,9 @@ struct FastLayout {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Chunks per row: at most kChunkMax logits each, at least about one chunk
-// workgroup per compute unit (kWantChunks), chunks of at least 1024 logits, at
-// most kMaxChunks; every slice is cut into chunks of its own.  Few rows get no
+// Chunks per row: at most 4 * vec * kChunkThreads logits each (kChunkMax for
+// the wide chunks), at least about one chunk workgroup per compute unit
+// (kWantChunks), chunks of at least 1024 logits, at most kMaxChunks; every slice is cut into chunks of its own.  Few rows get no
 // more chunks than that: the merge of a row walks every chunk's candidates,
 // so for small batches it, not the read, sets the time.  S == 0 marks a shape
 // the chunked path does not take.

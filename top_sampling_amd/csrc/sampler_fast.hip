@@ -15,7 +15,9 @@
 //                 the end of the grid would leave a tail).
 // A  chunk pass   one 256-thread workgroup per (row, chunk of <= 16384
 //                 logits), the chunk held in registers (16 float4 per
-//                 thread).  Per chunk:
+//                 thread; 8 in the narrow chunks the one-call assembly +
+//                 sampler takes when they stay few, writing each chunk to
+//                 the stitched batch buffer as well).  Per chunk:
 //                   - max, then sum exp(l - max) and, for top-p-only rows,
 //                     sum exp((l - max) / T); lanes and waves are combined by
 //                     rescaling to the larger maximum (DPP reductions); a
@@ -153,7 +155,7 @@ __device__ __forceinline__ void set_lane(float4& f, int q, float x) {
 // The chunk into registers: logit e = 4 * (j * AT + tid) + q of the chunk in
 // lane q of v[j]; slots past the chunk end hold -inf.  Every load is issued
 // unconditionally (out-of-range slots re-read the chunk's last element), so
-// all sixteen are in flight together, as non-temporal (streaming) loads.
+// all AVW of them are in flight together, as non-temporal (streaming) loads.
 // VEC: 16-byte aligned rows and n % 4 == 0.
 template <bool VEC, int AVW>
 __device__ __forceinline__ void load_chunk(float4 (&v)[AVW], const float* __restrict__ src, int n,
@@ -573,8 +575,8 @@ __global__ __launch_bounds__(OT) void order_rows_kernel(SamplerArgs a, FastLayou
 }
 
 template <bool VEC, int AVW>
-__global__ __launch_bounds__(AT, AVW == 16 ? 4 : 6) void chunk_pass_kernel(SamplerArgs a, FastLayout lay,
-                                                        uint8_t* __restrict__ ws) {
+__global__ __launch_bounds__(AT, AVW == 16 ? 4 : 6) void chunk_pass_kernel(
+    SamplerArgs a, FastLayout lay, uint8_t* __restrict__ ws) {
   __shared__ ChunkSmem sh;
   const int S = lay.S;
   // Workgroup -> (row, chunk) through the row order; a chunk's records
