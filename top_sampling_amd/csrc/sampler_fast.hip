@@ -12,7 +12,9 @@
 // O  row order    one workgroup: the order the chunk pass takes the rows in,
 //                 rows that draw Gumbel keys over every token first, then
 //                 rows with long top-k lists, then the rest (a slow row near
-//                 the end of the grid would leave a tail).
+//                 the end of the grid would leave a tail).  Only wide-chunk
+//                 calls whose chunk grid takes more than one round of the
+//                 GPU launch it.
 // A  chunk pass   one 256-thread workgroup per (row, chunk of <= 16384
 //                 logits), the chunk held in registers (16 float4 per
 //                 thread; 8 in the narrow chunks the one-call assembly +
