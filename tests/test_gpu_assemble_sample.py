@@ -157,3 +157,31 @@ def test_assemble_and_sample_tiny(dev, ts, V, widths, route):
     res, lse = _oracle_ref(logits, params, 0, 3)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
              res.row_status, res.flagged, lse, logits, label="tiny/assemble")
+
+
+UNIFORM_KINDS = {
+    "greedy": (0.0, 0, 1.0),
+    "top_k_20": (0.7, 20, 1.0),
+    "top_k_1000_top_p_0.8": (0.7, 1000, 0.8),
+    "top_p_0.9": (0.9, 0, 0.9),
+    "full_vocabulary": (1.0, 0, 1.0),
+}
+
+
+@pytest.mark.parametrize("kind", list(UNIFORM_KINDS))
+def test_assemble_and_sample_uniform_kind(dev, ts, kind):
+    """160 spec_decode rows, four slices, every row given the same temperature,
+    top_k and top_p (the mix's n_logprobs): one route carries the whole grid.
+    With every row top-p-only each row is probed, 3,200 probe items for a
+    2,048-workgroup probe pass, so its workgroups take several items each."""
+    w = workloads.get("spec_decode")
+    params = workloads.make_params(w)[:160]
+    params["temperature"], params["top_k"], params["top_p"] = UNIFORM_KINDS[kind]
+    logits = workloads.make_logits(w, slice(0, 160))
+    say("assemble+sample uniform kind", kind)
+    wide, got, sep = _run(ts, dev, logits, _even_widths(w.vocab, 4), params, 0, w.max_logprobs)
+    _check_assembled(wide, logits, 0)
+    _same_outputs(got, sep)
+    res, lse = _oracle_ref(logits, params, 0, w.max_logprobs)
+    _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
+             res.row_status, res.flagged, lse, logits, label=f"{kind}/assemble")
