@@ -168,20 +168,25 @@ UNIFORM_KINDS = {
 }
 
 
+@pytest.mark.parametrize("n_slices", [4, 16])
 @pytest.mark.parametrize("kind", list(UNIFORM_KINDS))
-def test_assemble_and_sample_uniform_kind(dev, ts, kind):
-    """160 spec_decode rows, four slices, every row given the same temperature,
-    top_k and top_p (the mix's n_logprobs): one route carries the whole grid.
-    With every row top-p-only each row is probed, 3,200 probe items for a
-    2,048-workgroup probe pass, so its workgroups take several items each."""
+def test_assemble_and_sample_uniform_kind(dev, ts, kind, n_slices):
+    """160 spec_decode rows, every row given the same temperature, top_k and
+    top_p (the mix's n_logprobs): one route carries the whole grid.  Four
+    slices take narrow chunks (20 a row) in the rows' own order; sixteen
+    would make 32 narrow chunks a row, so they take wide ones (16 a row, 2,560
+    in all) behind the row-order pre-pass.  With every row top-p-only each
+    row is probed, 3,200 or 2,560 probe items for a 2,048-workgroup probe
+    pass, so some of its workgroups take more than one."""
     w = workloads.get("spec_decode")
     params = workloads.make_params(w)[:160]
     params["temperature"], params["top_k"], params["top_p"] = UNIFORM_KINDS[kind]
     logits = workloads.make_logits(w, slice(0, 160))
-    say("assemble+sample uniform kind", kind)
-    wide, got, sep = _run(ts, dev, logits, _even_widths(w.vocab, 4), params, 0, w.max_logprobs)
+    say("assemble+sample uniform kind", kind, n_slices)
+    wide, got, sep = _run(ts, dev, logits, _even_widths(w.vocab, n_slices), params, 0,
+                          w.max_logprobs)
     _check_assembled(wide, logits, 0)
     _same_outputs(got, sep)
     res, lse = _oracle_ref(logits, params, 0, w.max_logprobs)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
-             res.row_status, res.flagged, lse, logits, label=f"{kind}/assemble")
+             res.row_status, res.flagged, lse, logits, label=f"{kind}/{n_slices}/assemble")
