@@ -172,7 +172,8 @@ UNIFORM_KINDS = {
 @pytest.mark.parametrize("kind", list(UNIFORM_KINDS))
 def test_assemble_and_sample_uniform_kind(dev, ts, kind, n_slices):
     """160 spec_decode rows, every row given the same temperature, top_k and
-    top_p (the mix's n_logprobs): one route carries the whole grid.  Four
+    top_p (the mix's n_logprobs): one route carries the whole grid.  The
+    slice sampler and the buffer sampler draw the same as the one call.  Four
     slices take narrow chunks (20 a row) in the rows' own order; sixteen
     would make 32 narrow chunks a row, so they take wide ones (16 a row, 2,560
     in all) behind the row-order pre-pass.  With every row top-p-only each
@@ -187,6 +188,13 @@ def test_assemble_and_sample_uniform_kind(dev, ts, kind, n_slices):
                           w.max_logprobs)
     _check_assembled(wide, logits, 0)
     _same_outputs(got, sep)
+    # The buffer sampler on the stitched rows draws the same.
+    import torch
+
+    buf = ts.sampler_sample(torch.from_numpy(wide).to(dev), ts.params_to_device(params, dev), 0,
+                            w.max_logprobs)
+    torch.cuda.synchronize()
+    _same_outputs(got, {k: getattr(buf, k).cpu().numpy() for k in FIELDS})
     res, lse = _oracle_ref(logits, params, 0, w.max_logprobs)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
              res.row_status, res.flagged, lse, logits, label=f"{kind}/{n_slices}/assemble")
