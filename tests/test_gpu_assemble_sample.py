@@ -6,8 +6,8 @@ import numpy as np
 import pytest
 
 import workloads
-from test_gpu_parity import (SLICE_LAYOUTS, _compare, _edge_case, _even_widths,  # noqa: F401
-                             _load_expected, _oracle_ref, dev, route, say, ts)
+from test_gpu_parity import (SLICE_LAYOUTS, _compare, _compare_processed, _edge_case,  # noqa: F401
+                             _even_widths, _load_expected, _oracle_ref, dev, route, say, ts)
 
 pytestmark = pytest.mark.gpu
 
@@ -198,3 +198,23 @@ def test_assemble_and_sample_uniform_kind(dev, ts, kind, n_slices):
     res, lse = _oracle_ref(logits, params, 0, w.max_logprobs)
     _compare(got, res.token_ids, res.token_logprobs, res.topn_ids, res.topn_logprobs,
              res.row_status, res.flagged, lse, logits, label=f"{kind}/{n_slices}/assemble")
+
+
+@pytest.mark.parametrize("kind", list(UNIFORM_KINDS))
+def test_assemble_and_sample_uniform_kind_processed(dev, ts, kind):
+    """The processed-distribution log-probabilities of the one call on the
+    one-row-kind batches (four slices) are the oracle's."""
+    import oracle
+
+    w = workloads.get("spec_decode")
+    params = workloads.make_params(w)[:160]
+    params["temperature"], params["top_k"], params["top_p"] = UNIFORM_KINDS[kind]
+    logits = workloads.make_logits(w, slice(0, 160))
+    say("assemble+sample uniform kind processed", kind)
+    wide, got, sep = _run(ts, dev, logits, _even_widths(w.vocab, 4), params, 0, w.max_logprobs,
+                          processed=True)
+    _check_assembled(wide, logits, 0)
+    _same_outputs(got, sep)
+    res = oracle.sample(logits, params, 0, w.max_logprobs, processed=True)
+    assert res.flagged.sum() <= 1e-3 * 160
+    _compare_processed(got, res, label=f"{kind}/processed")
