@@ -42,6 +42,7 @@ struct FallbackSmem {
   unsigned long long sel_above_q;
   int list_n;
   double pabove[kProbes];  // probe rows: mass above each probe
+  double pstage[kMaxChunks * kProbes];  // probe rows: every chunk's partial masses
   LogitsView lv;  // the slice table, read with per-thread indices from here
 };
 
@@ -379,11 +380,19 @@ __device__ __forceinline__ void finish_probe_row(const SamplerArgs& a, const Fas
   const ts_row_params p = a.params[r];
   const double* part = reinterpret_cast<const double*>(ws + lay.off_part) +
                        static_cast<size_t>(li) * lay.S * kProbes;
-  // Thread i sums probe i's mass over the chunks (chunk order).
+  // Every chunk's partials are fetched at once (thread t takes chunk t / np,
+  // probe t % np), then thread i sums probe i's over the chunks in chunk
+  // order, the additions of a serial walk without its chain of loads.
   const int np = pr.npts;
+  const int nstage = lay.S * np;  // at most kMaxChunks * kProbes <= XT
+  for (int t = threadIdx.x; t < nstage; t += XT) {
+    const int c = t / np;
+    sh.pstage[t] = part[static_cast<size_t>(c) * kProbes + (t - c * np)];
+  }
+  __syncthreads();
   if (static_cast<int>(threadIdx.x) < np) {
     double above = 0.0;
-    for (int c = 0; c < lay.S; ++c) above += part[static_cast<size_t>(c) * kProbes + threadIdx.x];
+    for (int c = 0; c < lay.S; ++c) above += sh.pstage[c * np + threadIdx.x];
     sh.pabove[threadIdx.x] = above;
   }
   __syncthreads();
